@@ -1,0 +1,467 @@
+/*
+ * CPU oracle for the balanced expert-parallel MoE hot path.
+ *
+ * TEST INFRASTRUCTURE ONLY. This file is the plain, slow, single-threaded
+ * definition that the GPU library is checked against. Only the test suite,
+ * the smoke check and the benchmark's CPU-baseline leg may load it. It shares
+ * no code, header, table or helper with the GPU library.
+ *
+ * Sources (web pages on the method; cited by title and section):
+ *  [MoonEP-TD]  "MoonEP" technical overview (twodots.gr): the invariant that
+ *               every EP rank processes exactly S*K routed rows; redundant
+ *               expert instances planned online from the router output;
+ *               tokens written grouped by expert at the destination;
+ *               planner-produced cu_seqlens; expert rows 0..E-1, then
+ *               prefetch slots; static S*K buffers.
+ *  [UpdExp]     "aclnnMoeUpdateExpert" op doc, sections "功能说明"
+ *               (function description: load-balance remap and pruning
+ *               formulas), "参数说明" (parameter table) and "约束说明"
+ *               (constraints).
+ *  [MoonEP-API] "MoonEP API完全参考" (stapisi.com), sections 2.2 and 3.1:
+ *               planning, dispatch and combine entry points.
+ * The exact planning rule (native home rank floor(e*R/E), keep the first S*K
+ * routes of a rank in (expert, global token, k) order, spill the rest in that
+ * order to under-loaded ranks in ascending rank order) is the plainest rule
+ * that meets the [MoonEP-TD] invariant; the readings are listed with the
+ * design notes of this repository.
+ *
+ * Build: gcc -O2 -ffp-contract=off -fPIC -shared (no FMA contraction, so
+ * every fp32 multiply and add is rounded on its own).
+ */
+#include <stdint.h>
+#include <stdlib.h>
+#include <string.h>
+
+enum { OR_OK = 0, OR_ERR_ARG = 1, OR_ERR_ALLOC = 2, OR_ERR_INTERNAL = 3 };
+
+/* ---------------------------------------------------------------- helpers */
+
+/* Native home rank of expert e: floor(e*R/E), in 64-bit integers. */
+static int home_rank(int e, int R, int E) {
+    return (int)(((int64_t)e * (int64_t)R) / (int64_t)E);
+}
+
+/* bf16 bit pattern -> float (exact widening: bf16 is the top half of fp32). */
+static float bf16_to_float(uint16_t b) {
+    uint32_t u = (uint32_t)b << 16;
+    float f;
+    memcpy(&f, &u, 4);
+    return f;
+}
+
+/* float -> bf16, round to nearest, ties to even, from the bit layout.
+ * NaN maps to a quiet NaN with the same sign. */
+static uint16_t float_to_bf16_rne(float f) {
+    uint32_t u;
+    memcpy(&u, &f, 4);
+    if ((u & 0x7fffffffu) > 0x7f800000u) return (uint16_t)((u >> 16) | 0x0040u);
+    uint32_t lsb = (u >> 16) & 1u;
+    u += 0x7fffu + lsb;
+    return (uint16_t)(u >> 16);
+}
+
+/* IEEE binary16 bit pattern -> float, decoded field by field (exact). */
+static float fp16_to_float(uint16_t h) {
+    uint32_t sign = (uint32_t)(h >> 15) << 31;
+    uint32_t ex = (h >> 10) & 0x1fu;
+    uint32_t man = h & 0x3ffu;
+    uint32_t u;
+    if (ex == 0) {
+        if (man == 0) {
+            u = sign;
+        } else { /* subnormal: value = man * 2^-24 */
+            int shift = 0;
+            while ((man & 0x400u) == 0) { man <<= 1; shift++; }
+            man &= 0x3ffu;
+            u = sign | ((uint32_t)(127 - 15 - shift + 1) << 23) | (man << 13);
+        }
+    } else if (ex == 31) {
+        u = sign | 0x7f800000u | (man << 13);
+    } else {
+        u = sign | ((ex - 15 + 127) << 23) | (man << 13);
+    }
+    float f;
+    memcpy(&f, &u, 4);
+    return f;
+}
+
+/* qsort keys: (primary, secondary) pairs compared lexicographically. */
+typedef struct { int64_t a; int64_t b; int32_t idx; } key2;
+
+static int cmp_key2(const void* x, const void* y) {
+    const key2* p = (const key2*)x;
+    const key2* q = (const key2*)y;
+    if (p->a != q->a) return p->a < q->a ? -1 : 1;
+    if (p->b != q->b) return p->b < q->b ? -1 : 1;
+    return 0;
+}
+
+/* ------------------------------------------------------------------- plan */
+
+/*
+ * oracle_plan: global plan over the R x S x K routing table, plus the send
+ * and receive maps of rank m.
+ *
+ * [MoonEP-TD] invariant: every rank ends with exactly C = S*K routed rows.
+ * Steps:
+ *  1. cnt[e] and native loads L[r] = sum of cnt[e] over home(e) = r.
+ *  2. Order all routes f = g*K + k (g = src*S + s) by (expert, f): a stable
+ *     sort by expert, which is the (expert, global token, k) order.
+ *  3. Each rank's routes form one block of that order (home is monotone in
+ *     e). The first C of a block stay on the home rank at slots 0..C-1; the
+ *     rest are that rank's excess.
+ *  4. The excess of all over-loaded ranks, concatenated in ascending rank
+ *     (= the same global order), is handed out in order to the under-loaded
+ *     ranks in ascending rank; rank u takes C - L[u] routes at slots
+ *     L[u], L[u]+1, ...
+ *  5. Local instance layout of rank u ([MoonEP-TD]: rows grouped by expert,
+ *     expert rows first, prefetch slots after): native experts of u in
+ *     ascending e (zero-row natives keep their place), then redundant
+ *     instances (experts with home != u that received rows on u) in
+ *     ascending e. inst_cu holds the row offsets (the cu_seqlens).
+ *  6. send_pos: rank m's routes ordered by (dest, dest slot).
+ *     recv_pos: rank m's slots ordered by (source rank, slot); recv_pos[t]
+ *     is the row of the source-major arrival buffer that feeds slot t.
+ *
+ * Outputs beyond inst_count[u]: inst_expert = -1, inst_cu = C.
+ * Returns OR_ERR_INTERNAL if the slot assignment does not match the layout
+ * of step 5 (a self-check; never expected).
+ */
+int oracle_plan(int R, int E, int S, int K, int m, const int32_t* ids,
+                int32_t* expert_count, int32_t* rank_load,
+                int32_t* route_dest, int32_t* route_slot,
+                int32_t* inst_count, int32_t* inst_expert, int32_t* inst_cu,
+                int32_t* inst_gid_base,
+                int32_t* send_pos, int32_t* send_count,
+                int32_t* recv_pos, int32_t* recv_count) {
+    if (R < 1 || E < 1 || S < 1 || K < 1 || K > E || m < 0 || m >= R)
+        return OR_ERR_ARG;
+    const int64_t C = (int64_t)S * K;
+    const int64_t N = (int64_t)R * C;
+    int rc = OR_OK;
+
+    /* step 1 */
+    int64_t* cnt = calloc((size_t)E, sizeof(int64_t));
+    int64_t* L = calloc((size_t)R, sizeof(int64_t));
+    key2* order = malloc((size_t)N * sizeof(key2));
+    int32_t* slot_route = malloc((size_t)N * sizeof(int32_t));
+    int64_t* rcount = calloc((size_t)R * E, sizeof(int64_t));
+    key2* tmp = malloc((size_t)C * sizeof(key2));
+    if (!cnt || !L || !order || !slot_route || !rcount || !tmp) {
+        rc = OR_ERR_ALLOC;
+        goto done;
+    }
+    for (int64_t f = 0; f < N; f++) {
+        int e = ids[f];
+        if (e < 0 || e >= E) { rc = OR_ERR_ARG; goto done; }
+        cnt[e]++;
+    }
+    for (int e = 0; e < E; e++) L[home_rank(e, R, E)] += cnt[e];
+    for (int e = 0; e < E; e++) expert_count[e] = (int32_t)cnt[e];
+    for (int r = 0; r < R; r++) rank_load[r] = (int32_t)L[r];
+
+    /* step 2 */
+    for (int64_t f = 0; f < N; f++) {
+        order[f].a = ids[f];
+        order[f].b = f;
+        order[f].idx = (int32_t)f;
+    }
+    qsort(order, (size_t)N, sizeof(key2), cmp_key2);
+
+    /* step 3: walk each rank's block, keep the first C, list the rest */
+    int32_t* excess = malloc((size_t)N * sizeof(int32_t));
+    if (!excess) { rc = OR_ERR_ALLOC; goto done; }
+    int64_t n_excess = 0;
+    {
+        int64_t p = 0;
+        for (int r = 0; r < R; r++) {
+            for (int64_t q = 0; q < L[r]; q++, p++) {
+                int32_t f = order[p].idx;
+                if (home_rank(ids[f], R, E) != r) { rc = OR_ERR_INTERNAL; free(excess); goto done; }
+                if (q < C) {
+                    route_dest[f] = r;
+                    route_slot[f] = (int32_t)q;
+                } else {
+                    excess[n_excess++] = f;
+                }
+            }
+        }
+    }
+    /* step 4: hand the excess out to under-loaded ranks in ascending order */
+    {
+        int64_t j = 0;
+        for (int u = 0; u < R; u++) {
+            for (int64_t slot = L[u]; slot < C; slot++) {
+                if (j >= n_excess) { rc = OR_ERR_INTERNAL; free(excess); goto done; }
+                int32_t f = excess[j++];
+                route_dest[f] = u;
+                route_slot[f] = (int32_t)slot;
+            }
+        }
+        if (j != n_excess) { rc = OR_ERR_INTERNAL; free(excess); goto done; }
+    }
+    free(excess);
+
+    /* inverse map: which route sits in (dest, slot) */
+    for (int64_t i = 0; i < N; i++) slot_route[i] = -1;
+    for (int64_t f = 0; f < N; f++) {
+        int64_t at = (int64_t)route_dest[f] * C + route_slot[f];
+        if (slot_route[at] != -1) { rc = OR_ERR_INTERNAL; goto done; }
+        slot_route[at] = (int32_t)f;
+    }
+
+    /* step 5: instance tables */
+    for (int64_t f = 0; f < N; f++) rcount[(int64_t)route_dest[f] * E + ids[f]]++;
+    {
+        int64_t gid = 0;
+        for (int u = 0; u < R; u++) {
+            int32_t* ie = inst_expert + (int64_t)u * E;
+            int32_t* cu = inst_cu + (int64_t)u * (E + 1);
+            int n = 0;
+            int64_t row = 0;
+            for (int e = 0; e < E; e++) {           /* natives */
+                if (home_rank(e, R, E) != u) continue;
+                ie[n] = e;
+                cu[n] = (int32_t)row;
+                row += rcount[(int64_t)u * E + e];
+                n++;
+            }
+            for (int e = 0; e < E; e++) {           /* redundant instances */
+                if (home_rank(e, R, E) == u || rcount[(int64_t)u * E + e] == 0) continue;
+                ie[n] = e;
+                cu[n] = (int32_t)row;
+                row += rcount[(int64_t)u * E + e];
+                n++;
+            }
+            if (row != C || n > E) { rc = OR_ERR_INTERNAL; goto done; }
+            cu[n] = (int32_t)C;
+            for (int i = n; i < E; i++) ie[i] = -1;
+            for (int i = n + 1; i <= E; i++) cu[i] = (int32_t)C;
+            inst_count[u] = n;
+            inst_gid_base[u] = (int32_t)gid;
+            gid += n;
+            /* self-check: the slots of instance i hold exactly its expert */
+            for (int i = 0; i < n; i++)
+                for (int64_t t = cu[i]; t < cu[i + 1]; t++)
+                    if (ids[slot_route[(int64_t)u * C + t]] != ie[i]) {
+                        rc = OR_ERR_INTERNAL;
+                        goto done;
+                    }
+        }
+        inst_gid_base[R] = (int32_t)gid;
+    }
+
+    /* step 6a: send map of rank m, ordered by (dest, dest slot) */
+    for (int r = 0; r < R; r++) send_count[r] = 0;
+    for (int64_t i = 0; i < C; i++) {
+        int64_t f = (int64_t)m * C + i;
+        tmp[i].a = route_dest[f];
+        tmp[i].b = route_slot[f];
+        tmp[i].idx = (int32_t)i;
+        send_count[route_dest[f]]++;
+    }
+    qsort(tmp, (size_t)C, sizeof(key2), cmp_key2);
+    for (int64_t i = 0; i < C; i++) send_pos[tmp[i].idx] = (int32_t)i;
+
+    /* step 6b: arrival order on rank m, ordered by (source rank, slot) */
+    for (int r = 0; r < R; r++) recv_count[r] = 0;
+    for (int64_t t = 0; t < C; t++) {
+        int64_t f = slot_route[(int64_t)m * C + t];
+        int64_t src = f / C;
+        tmp[t].a = src;
+        tmp[t].b = t;
+        tmp[t].idx = (int32_t)t;
+        recv_count[src]++;
+    }
+    qsort(tmp, (size_t)C, sizeof(key2), cmp_key2);
+    for (int64_t i = 0; i < C; i++) recv_pos[tmp[i].idx] = (int32_t)i;
+
+done:
+    free(cnt);
+    free(L);
+    free(order);
+    free(slot_route);
+    free(rcount);
+    free(tmp);
+    return rc;
+}
+
+/* --------------------------------------------------------- remap / prune */
+
+/*
+ * oracle_remap_prune: [UpdExp] "功能说明" load-balance remap and pruning.
+ *
+ * Remap, per (t, k) with e = expert_ids[t,k] and count = table[e*F]:
+ *   count == 1        -> column 1
+ *   balance_mode == 0 -> column local_rank_id / ceil(world_size / count) + 1
+ *   balance_mode == 1 -> column (t mod count) + 1  (t = token index)
+ *   balanced_ids[t,k] = table[e*F + column]
+ * Pruning, with scales widened exactly to fp32:
+ *   thr_sum[t] = sum over k = 0..K-1 of fl(scale[t,k] * threshold[k]),
+ *               added in k order from +0.0f, each step rounded to fp32
+ *   mask[t,k]  = active[t] and not (scale[t,k] < thr_sum[t])
+ *   (a route whose scale falls below the sum is pruned; a tie is kept)
+ *   Without scales and threshold every mask entry is 1.
+ * Send map (dispatch after remap): kept routes ordered by (destination card,
+ * instance id, t, k), the card of an instance being id / place_per_rank;
+ * send_pos[t*K+k] = row, -1 when pruned; send_count[card] = kept routes.
+ *
+ * scale_dtype: 0 = fp32, 1 = bf16, 2 = fp16. scales/thr/active may be NULL
+ * (scales and thr together; active only with them). send_pos and
+ * send_count may be NULL (together).
+ */
+int oracle_remap_prune(int BS, int K, int E, int F, int world_size,
+                       int place_per_rank, int local_rank_id, int balance_mode,
+                       const int32_t* expert_ids, const int32_t* eplb_table,
+                       const void* scales, int scale_dtype, const float* thr,
+                       const uint8_t* active,
+                       int32_t* balanced_ids, uint8_t* balanced_mask,
+                       int32_t* send_pos, int32_t* send_count) {
+    if (BS < 1 || K < 1 || E < 1 || F < 2 || world_size < 1 || place_per_rank < 1)
+        return OR_ERR_ARG;
+    if (balance_mode != 0 && balance_mode != 1) return OR_ERR_ARG;
+    if ((scales == NULL) != (thr == NULL)) return OR_ERR_ARG;
+    if (active != NULL && scales == NULL) return OR_ERR_ARG;
+    const int n_inst = world_size * place_per_rank;
+
+    for (int t = 0; t < BS; t++) {
+        for (int k = 0; k < K; k++) {
+            int e = expert_ids[t * K + k];
+            if (e < 0 || e >= E) return OR_ERR_ARG;
+            int count = eplb_table[(int64_t)e * F];
+            int col;
+            if (count == 1) {
+                col = 1;
+            } else if (balance_mode == 0) {
+                int mode_value = (world_size + count - 1) / count;
+                col = local_rank_id / mode_value + 1;
+            } else {
+                col = t % count + 1;
+            }
+            if (col < 1 || col >= F) return OR_ERR_ARG;
+            balanced_ids[t * K + k] = eplb_table[(int64_t)e * F + col];
+        }
+    }
+
+    for (int t = 0; t < BS; t++) {
+        if (scales == NULL) {
+            for (int k = 0; k < K; k++) balanced_mask[t * K + k] = 1;
+            continue;
+        }
+        float s[64];
+        if (K > 64) return OR_ERR_ARG;
+        for (int k = 0; k < K; k++) {
+            int64_t i = (int64_t)t * K + k;
+            if (scale_dtype == 0) s[k] = ((const float*)scales)[i];
+            else if (scale_dtype == 1) s[k] = bf16_to_float(((const uint16_t*)scales)[i]);
+            else if (scale_dtype == 2) s[k] = fp16_to_float(((const uint16_t*)scales)[i]);
+            else return OR_ERR_ARG;
+        }
+        float thr_sum = 0.0f;
+        for (int k = 0; k < K; k++) {
+            float prod = s[k] * thr[k];
+            thr_sum = thr_sum + prod;
+        }
+        int act = active == NULL ? 1 : (active[t] != 0);
+        for (int k = 0; k < K; k++)
+            balanced_mask[t * K + k] = (uint8_t)(act && !(s[k] < thr_sum));
+    }
+
+    if (send_pos != NULL || send_count != NULL) {
+        if (send_pos == NULL || send_count == NULL) return OR_ERR_ARG;
+        key2* tmp = malloc((size_t)BS * K * sizeof(key2));
+        if (!tmp) return OR_ERR_ALLOC;
+        int64_t n = 0;
+        for (int c = 0; c < world_size; c++) send_count[c] = 0;
+        for (int64_t i = 0; i < (int64_t)BS * K; i++) {
+            send_pos[i] = -1;
+            if (!balanced_mask[i]) continue;
+            int inst = balanced_ids[i];
+            if (inst < 0 || inst >= n_inst) { free(tmp); return OR_ERR_ARG; }
+            int card = inst / place_per_rank;
+            tmp[n].a = (int64_t)card * n_inst + inst;
+            tmp[n].b = i;
+            tmp[n].idx = (int32_t)i;
+            n++;
+            send_count[card]++;
+        }
+        qsort(tmp, (size_t)n, sizeof(key2), cmp_key2);
+        for (int64_t r = 0; r < n; r++) send_pos[tmp[r].idx] = (int32_t)r;
+        free(tmp);
+    }
+    return OR_OK;
+}
+
+/* --------------------------------------------------------------- dispatch */
+
+/*
+ * oracle_pack: send_buf[send_pos[t*K+k], :] = x[t, :] for every route whose
+ * send_pos is >= 0 (per-destination send segments; [MoonEP-API] 3.1).
+ */
+int oracle_pack(int T, int K, int H, const uint16_t* x, const int32_t* send_pos,
+                uint16_t* send_buf) {
+    if (T < 0 || K < 1 || H < 1) return OR_ERR_ARG;
+    for (int64_t t = 0; t < T; t++)
+        for (int k = 0; k < K; k++) {
+            int32_t row = send_pos[t * K + k];
+            if (row < 0) continue;
+            for (int64_t h = 0; h < H; h++)
+                send_buf[(int64_t)row * H + h] = x[t * H + h];
+        }
+    return OR_OK;
+}
+
+/*
+ * oracle_group: recv_grouped[t, :] = recv_raw[recv_pos[t], :], turning the
+ * source-major arrival buffer into rows grouped by expert instance
+ * ([MoonEP-TD]: tokens land grouped by expert at the destination).
+ */
+int oracle_group(int n_recv, int H, const int32_t* recv_pos,
+                 const uint16_t* recv_raw, uint16_t* recv_grouped) {
+    if (n_recv < 0 || H < 1) return OR_ERR_ARG;
+    for (int64_t t = 0; t < n_recv; t++) {
+        int64_t src = recv_pos[t];
+        for (int64_t h = 0; h < H; h++)
+            recv_grouped[t * H + h] = recv_raw[src * H + h];
+    }
+    return OR_OK;
+}
+
+/* ---------------------------------------------------------------- combine */
+
+/*
+ * oracle_combine: score-weighted K-way reduction in fixed k order.
+ *   acc = +0.0f
+ *   for k = 0..K-1 with send_pos[t*K+k] >= 0:
+ *       acc = fl(acc + fl(score[t,k] * float(y_ret[send_pos[t*K+k], h])))
+ *   out_f32[t,h] = acc, out_bf16[t,h] = round-to-nearest-even(acc)
+ * Either output may be NULL.
+ */
+int oracle_combine(int T, int K, int H, const uint16_t* y_ret,
+                   const int32_t* send_pos, const float* scores,
+                   uint16_t* out_bf16, float* out_f32) {
+    if (T < 0 || K < 1 || H < 1) return OR_ERR_ARG;
+    for (int64_t t = 0; t < T; t++)
+        for (int64_t h = 0; h < H; h++) {
+            float acc = 0.0f;
+            for (int k = 0; k < K; k++) {
+                int32_t row = send_pos[t * K + k];
+                if (row < 0) continue;
+                float y = bf16_to_float(y_ret[(int64_t)row * H + h]);
+                float prod = scores[t * K + k] * y;
+                acc = acc + prod;
+            }
+            if (out_f32) out_f32[t * H + h] = acc;
+            if (out_bf16) out_bf16[t * H + h] = float_to_bf16_rne(acc);
+        }
+    return OR_OK;
+}
+
+/* Exposed for pinning the conversions in tests. */
+void oracle_bf16_from_float(const float* in, uint16_t* out, int64_t n) {
+    for (int64_t i = 0; i < n; i++) out[i] = float_to_bf16_rne(in[i]);
+}
+
+void oracle_float_from_fp16(const uint16_t* in, float* out, int64_t n) {
+    for (int64_t i = 0; i < n; i++) out[i] = fp16_to_float(in[i]);
+}

@@ -1,0 +1,46 @@
+"""The seeded generator: deterministic, right shapes, valid top-K."""
+import numpy as np
+import pytest
+
+import synth
+
+
+@pytest.mark.parametrize("name", ["tiny", "small", "dsv3"])
+def test_routing_is_seeded_and_valid(name):
+    a = synth.make_routing(name)
+    b = synth.make_routing(name)
+    assert np.array_equal(a["topk_ids"], b["topk_ids"])
+    assert np.array_equal(a["scores"], b["scores"])
+    R, E, S, K = a["R"], a["E"], a["S"], a["K"]
+    ids = a["topk_ids"].reshape(-1, K)
+    assert a["topk_ids"].shape == (R, S, K) and ids.dtype == np.int32
+    assert ids.min() >= 0 and ids.max() < E
+    srt = np.sort(ids, axis=1)
+    assert np.all(srt[:, 1:] != srt[:, :-1])          # distinct per token
+    sc = a["scores"].reshape(-1, K)
+    assert np.all(sc[:, 1:] <= sc[:, :-1])             # descending
+    assert np.allclose(sc.sum(axis=1), 1.0, atol=1e-5)
+
+
+def test_topk_ties_go_to_lower_id():
+    lg = np.array([[1.0, 3.0, 3.0, 0.5, 3.0]], np.float32)
+    assert synth._topk_desc(lg, 2).tolist() == [[1, 2]]
+    assert synth._topk_desc(lg, 4).tolist() == [[1, 2, 4, 0]]
+
+
+def test_eplb_inputs():
+    d = synth.make_eplb_inputs(with_x=False)
+    t = d["eplb_table"]
+    assert t.shape == (512, 9)
+    assert t[:, 0].min() >= 1 and t[:, 0].max() <= 8
+    for row in t:
+        assert len(set(row[1:].tolist())) == 8
+        assert row[1:].min() >= 0 and row[1:].max() < 768
+    assert d["active_mask"].sum() == 448 and d["active_mask"][:448].all()
+    s = (d["expert_scales"].astype(np.uint32) << 16).view(np.float32)
+    assert np.all(s[:, 1:] <= s[:, :-1])
+
+
+def test_bf16_truncation():
+    v = np.array([1.0, -2.5, 1.00390625 + 2 ** -10], np.float32)
+    assert synth.bf16_from_f32_trunc(v).tolist() == [0x3F80, 0xC020, 0x3F80]
