@@ -1,0 +1,11 @@
+"""Balanced expert-parallel MoE hot path on MI355X (gfx950).
+
+The work is done by libmep.so (C ABI in include/mep.h, HIP kernels under
+csrc/). This package is its binding: ``_binding`` holds the raw entry points
+under their C names, ``api`` the tensor-level calls. Importing the package
+does not load the library; the first call does, and raises if it has not
+been built (``python -m combine_balancing_amd.build``).
+"""
+from .api import (combine, dispatch, plan, plan_outputs, plan_workspace,  # noqa: F401
+                  remap_prune)
+from ._binding import MepError, lib  # noqa: F401

@@ -1,0 +1,206 @@
+"""Tensor-level calls onto the mep C ABI.
+
+Each function checks dtypes, devices and sizes of torch tensors, allocates
+outputs when none are given, and calls the matching C entry point on the
+current stream (or the stream passed). No arithmetic of the method happens
+here. bf16 rows may be passed as torch.bfloat16 or as int16/uint16 bit
+patterns.
+"""
+from __future__ import annotations
+
+import torch
+
+from . import _binding as B
+
+_BF16_LIKE = (torch.bfloat16, torch.int16, torch.uint16)
+
+
+def _stream_handle(stream):
+    s = torch.cuda.current_stream() if stream is None else stream
+    return s.cuda_stream
+
+
+def _need(t, name, dtypes, numel=None):
+    if t is None:
+        raise ValueError(f"{name} is required")
+    if not t.is_cuda:
+        raise ValueError(f"{name} must be a device tensor")
+    if not t.is_contiguous():
+        raise ValueError(f"{name} must be contiguous")
+    if t.dtype not in (dtypes if isinstance(dtypes, tuple) else (dtypes,)):
+        raise ValueError(f"{name} has dtype {t.dtype}, expected {dtypes}")
+    if numel is not None and t.numel() != numel:
+        raise ValueError(f"{name} has {t.numel()} elements, expected {numel}")
+    return t.data_ptr()
+
+
+def _opt(t, name, dtypes, numel=None):
+    return None if t is None else _need(t, name, dtypes, numel)
+
+
+def plan_workspace(R, E, S, K, device=None):
+    n = B.mep_plan_workspace_size(R, E, S, K)
+    if n == 0:
+        raise ValueError(f"unsupported plan sizes R={R} E={E} S={S} K={K}")
+    return torch.empty(n, dtype=torch.uint8, device=device or "cuda")
+
+
+def plan_outputs(R, E, S, K, device=None, with_routes=True):
+    dev = device or "cuda"
+    C = S * K
+    i32 = dict(dtype=torch.int32, device=dev)
+    out = dict(
+        expert_count=torch.empty(E, **i32), rank_load=torch.empty(R, **i32),
+        inst_count=torch.empty(R, **i32), inst_expert=torch.empty(R, E, **i32),
+        inst_cu=torch.empty(R, E + 1, **i32), inst_gid_base=torch.empty(R + 1, **i32),
+        send_pos=torch.empty(C, **i32), send_count=torch.empty(R, **i32),
+        recv_pos=torch.empty(C, **i32), recv_count=torch.empty(R, **i32))
+    if with_routes:
+        out["route_dest"] = torch.empty(R * C, **i32)
+        out["route_slot"] = torch.empty(R * C, **i32)
+    else:
+        out["route_dest"] = out["route_slot"] = None
+    return out
+
+
+def plan(topk_ids, R, E, S, K, my_rank=0, workspace=None, out=None, stream=None,
+         with_routes=True):
+    """mep_plan on device int32 topk_ids [R*S*K]. Returns the output dict."""
+    N = R * S * K
+    ids = _need(topk_ids, "topk_ids", torch.int32, N)
+    if workspace is None:
+        workspace = plan_workspace(R, E, S, K, topk_ids.device)
+    if out is None:
+        out = plan_outputs(R, E, S, K, topk_ids.device, with_routes)
+    C = S * K
+    o = out
+    rc = B.mep_plan(
+        R, E, S, K, my_rank, ids, _need(workspace, "workspace", torch.uint8),
+        workspace.numel(),
+        _need(o["expert_count"], "expert_count", torch.int32, E),
+        _need(o["rank_load"], "rank_load", torch.int32, R),
+        _opt(o["route_dest"], "route_dest", torch.int32, N),
+        _opt(o["route_slot"], "route_slot", torch.int32, N),
+        _need(o["inst_count"], "inst_count", torch.int32, R),
+        _need(o["inst_expert"], "inst_expert", torch.int32, R * E),
+        _need(o["inst_cu"], "inst_cu", torch.int32, R * (E + 1)),
+        _need(o["inst_gid_base"], "inst_gid_base", torch.int32, R + 1),
+        _need(o["send_pos"], "send_pos", torch.int32, C),
+        _need(o["send_count"], "send_count", torch.int32, R),
+        _need(o["recv_pos"], "recv_pos", torch.int32, C),
+        _need(o["recv_count"], "recv_count", torch.int32, R),
+        _stream_handle(stream))
+    B.check("mep_plan", rc)
+    return out
+
+
+_SCALE_CODES = {torch.float32: B.MEP_SCALE_F32, torch.bfloat16: B.MEP_SCALE_BF16,
+                torch.float16: B.MEP_SCALE_F16}
+
+
+def remap_prune(expert_ids, eplb_table, world_size, place_per_rank, local_rank_id,
+                balance_mode, expert_scales=None, pruning_threshold=None,
+                active_mask=None, scale_dtype=None, want_send=True, out=None,
+                stream=None):
+    """mep_remap_prune. expert_ids [BS,K] int32, eplb_table [E,F] int32.
+
+    expert_scales: float32 / bfloat16 / float16 tensor [BS,K], or raw 16-bit
+    patterns with scale_dtype given ("bf16" or "fp16").
+    """
+    BS, K = expert_ids.shape
+    E, F = eplb_table.shape
+    dev = expert_ids.device
+    if expert_scales is not None:
+        if scale_dtype is None:
+            code = _SCALE_CODES[expert_scales.dtype]
+        else:
+            code = {"fp32": B.MEP_SCALE_F32, "bf16": B.MEP_SCALE_BF16,
+                    "fp16": B.MEP_SCALE_F16}[scale_dtype]
+        sc = _need(expert_scales, "expert_scales",
+                   (torch.float32, torch.bfloat16, torch.float16, torch.int16, torch.uint16),
+                   BS * K)
+    else:
+        code, sc = B.MEP_SCALE_BF16, None
+    if out is None:
+        out = dict(balanced_ids=torch.empty(BS, K, dtype=torch.int32, device=dev),
+                   balanced_mask=torch.empty(BS, K, dtype=torch.uint8, device=dev))
+        if want_send:
+            out["send_pos"] = torch.empty(BS * K, dtype=torch.int32, device=dev)
+            out["send_count"] = torch.empty(world_size, dtype=torch.int32, device=dev)
+    rc = B.mep_remap_prune(
+        BS, K, E, F, world_size, place_per_rank, local_rank_id, balance_mode,
+        _need(expert_ids, "expert_ids", torch.int32), _need(eplb_table, "eplb_table", torch.int32),
+        sc, code, _opt(pruning_threshold, "pruning_threshold", torch.float32, K),
+        _opt(active_mask, "active_mask", (torch.uint8, torch.bool), BS),
+        _need(out["balanced_ids"], "balanced_ids", torch.int32, BS * K),
+        _need(out["balanced_mask"], "balanced_mask", (torch.uint8, torch.bool), BS * K),
+        _opt(out.get("send_pos"), "send_pos", torch.int32, BS * K),
+        _opt(out.get("send_count"), "send_count", torch.int32, world_size),
+        _stream_handle(stream))
+    B.check("mep_remap_prune", rc)
+    return out
+
+
+def dispatch(K, x=None, send_pos=None, send_buf=None, recv_raw=None, recv_pos=None,
+             recv_grouped=None, stream=None):
+    """mep_dispatch: pack (x -> send_buf) and/or group (recv_raw -> recv_grouped).
+
+    Allocates send_buf [T*K,H] / recv_grouped [n,H] when not given (pack leaves
+    rows not named by send_pos untouched, so a fresh buffer is zero-filled).
+    Returns (send_buf, recv_grouped).
+    """
+    if x is None and recv_raw is None:
+        raise ValueError("nothing to do: give x and/or recv_raw")
+    T = H = 0
+    if x is not None:
+        T, H = x.shape
+        if send_buf is None:
+            send_buf = torch.zeros(T * K, H, dtype=x.dtype, device=x.device)
+        if send_buf.dim() != 2 or send_buf.shape[1] != H or send_buf.shape[0] < T * K:
+            raise ValueError("send_buf must be [>= T*K, H]")
+    n = 0
+    if recv_raw is not None:
+        n, H2 = recv_raw.shape
+        if x is not None and H2 != H:
+            raise ValueError("x and recv_raw disagree on H")
+        H = H2
+        if recv_grouped is None:
+            recv_grouped = torch.empty_like(recv_raw)
+    rc = B.mep_dispatch(
+        T, K, H, _opt(x, "x", _BF16_LIKE),
+        _opt(send_pos, "send_pos", torch.int32, T * K if x is not None else None),
+        _opt(send_buf, "send_buf", _BF16_LIKE),
+        n, _opt(recv_pos, "recv_pos", torch.int32, n if recv_raw is not None else None),
+        _opt(recv_raw, "recv_raw", _BF16_LIKE),
+        _opt(recv_grouped, "recv_grouped", _BF16_LIKE, n * H if recv_raw is not None else None),
+        _stream_handle(stream))
+    B.check("mep_dispatch", rc)
+    return send_buf, recv_grouped
+
+
+def combine(y_ret, send_pos, scores, out_bf16=True, out_f32=False, stream=None):
+    """mep_combine. y_ret [n_y,H] bf16 rows, send_pos [T*K], scores [T,K] fp32.
+
+    out_bf16/out_f32: True to allocate, a tensor to write into, or False/None.
+    Returns (out_bf16, out_f32).
+    """
+    T, K = scores.shape
+    n_y, H = y_ret.shape
+    dev = y_ret.device
+    if out_bf16 is True:
+        out_bf16 = torch.empty(T, H, dtype=torch.bfloat16, device=dev)
+    elif out_bf16 is False:
+        out_bf16 = None
+    if out_f32 is True:
+        out_f32 = torch.empty(T, H, dtype=torch.float32, device=dev)
+    elif out_f32 is False:
+        out_f32 = None
+    rc = B.mep_combine(
+        T, K, H, _need(y_ret, "y_ret", _BF16_LIKE), n_y,
+        _need(send_pos, "send_pos", torch.int32, T * K),
+        _need(scores, "scores", torch.float32, T * K),
+        _opt(out_bf16, "out_bf16", _BF16_LIKE, T * H),
+        _opt(out_f32, "out_f32", torch.float32, T * H),
+        _stream_handle(stream))
+    B.check("mep_combine", rc)
+    return out_bf16, out_f32

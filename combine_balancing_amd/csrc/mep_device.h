@@ -1,0 +1,121 @@
+// Device helpers shared by the mep kernels (gfx950, wave64).
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+#include "mep.h"
+
+namespace mep {
+
+constexpr int kWave = 64;
+
+// Lane index within the wave.
+__device__ __forceinline__ int lane_id() {
+    return (int)__builtin_amdgcn_mbcnt_hi(~0u, __builtin_amdgcn_mbcnt_lo(~0u, 0u));
+}
+
+// Number of set bits of `mask` at lanes below this one.
+__device__ __forceinline__ int count_below(uint64_t mask) {
+    return (int)__builtin_amdgcn_mbcnt_hi((uint32_t)(mask >> 32),
+                                          __builtin_amdgcn_mbcnt_lo((uint32_t)mask, 0u));
+}
+
+// Lanes (among `valid` ones) whose key equals this lane's key, found with one
+// ballot per key bit: a wave-wide multi-split, so equal keys are ranked by
+// lane order without atomics (deterministic). Must be called by the whole
+// wave with a wave-uniform `nbits`.
+__device__ __forceinline__ uint64_t match_peers(int key, bool valid, int nbits) {
+    uint64_t peers = __ballot(valid);
+    for (int b = 0; b < nbits; ++b) {
+        const bool bit = (key >> b) & 1;
+        const uint64_t m = __ballot(valid && bit);
+        peers &= bit ? m : ~m;
+    }
+    return peers;
+}
+
+// True on the highest lane of its peer group.
+__device__ __forceinline__ bool is_group_leader(uint64_t peers) {
+    const int lane = lane_id();
+    const uint64_t above = lane == 63 ? 0ull : (~0ull << (lane + 1));
+    return (peers & above) == 0;
+}
+
+// Inclusive sum over the wave (lanes 0..lane).
+__device__ __forceinline__ int wave_inclusive_sum(int x) {
+    const int lane = lane_id();
+#pragma unroll
+    for (int d = 1; d < kWave; d <<= 1) {
+        const int y = __shfl_up(x, d, kWave);
+        if (lane >= d) x += y;
+    }
+    return x;
+}
+
+// Exclusive block-wide sum. `scratch` holds at least blockDim/64 + 1 ints of
+// LDS. Every thread of the block must call it. Returns the exclusive prefix;
+// *total receives the block sum.
+__device__ __forceinline__ int block_exclusive_sum(int v, int* scratch, int* total) {
+    const int lane = threadIdx.x & (kWave - 1);
+    const int wave = threadIdx.x / kWave;
+    const int nw = (blockDim.x + kWave - 1) / kWave;
+    const int inc = wave_inclusive_sum(v);
+    if (lane == kWave - 1 || (int)threadIdx.x == (int)blockDim.x - 1) scratch[wave] = inc;
+    __syncthreads();
+    if (wave == 0) {
+        const int w = lane < nw ? scratch[lane] : 0;
+        const int s = wave_inclusive_sum(w);
+        if (lane < nw) scratch[lane] = s - w;
+        if (lane == nw - 1) scratch[nw] = s;
+    }
+    __syncthreads();
+    const int res = inc - v + scratch[wave];
+    *total = scratch[nw];
+    __syncthreads();
+    return res;
+}
+
+// Smallest index i in [0, n) with a[i] >= x (n if none).
+__device__ __forceinline__ int lower_bound(const int* a, int n, int x) {
+    int lo = 0, hi = n;
+    while (lo < hi) {
+        const int mid = (lo + hi) >> 1;
+        if (a[mid] < x) lo = mid + 1; else hi = mid;
+    }
+    return lo;
+}
+
+// Smallest index i in [0, n) with a[i] > x (n if none).
+__device__ __forceinline__ int upper_bound(const int* a, int n, int x) {
+    int lo = 0, hi = n;
+    while (lo < hi) {
+        const int mid = (lo + hi) >> 1;
+        if (a[mid] <= x) lo = mid + 1; else hi = mid;
+    }
+    return lo;
+}
+
+__device__ __forceinline__ int clampi(int v, int lo, int hi) {
+    return v < lo ? lo : (v > hi ? hi : v);
+}
+
+// bf16 bit pattern -> fp32 (exact).
+__device__ __forceinline__ float bf16_bits_to_float(uint32_t b) {
+    return __uint_as_float(b << 16);
+}
+
+// fp32 -> bf16 bits, round to nearest, ties to even; NaN stays a quiet NaN.
+__device__ __forceinline__ uint32_t float_to_bf16_bits(float f) {
+    const uint32_t u = __float_as_uint(f);
+    if ((u & 0x7fffffffu) > 0x7f800000u) return (u >> 16) | 0x0040u;
+    return (u + 0x7fffu + ((u >> 16) & 1u)) >> 16;
+}
+
+}  // namespace mep
+
+// Host-side launch check shared by the entry points.
+#define MEP_LAUNCH_CHECK()                                   \
+    do {                                                     \
+        if (hipGetLastError() != hipSuccess) return MEP_ERR_HIP; \
+    } while (0)

@@ -1,0 +1,257 @@
+/*
+ * mep.h - C ABI of the balanced expert-parallel MoE hot path (MI355X, gfx950).
+ *
+ * One GPU computes, for a logical expert-parallel world of R ranks:
+ *   - the global plan that every rank would compute identically
+ *     (mep_plan), and this rank's send and receive maps;
+ *   - the EPLB logical-to-physical expert remap with score pruning
+ *     (mep_remap_prune);
+ *   - this rank's pack into per-destination send segments and the grouping
+ *     of received rows by expert instance (mep_dispatch);
+ *   - the score-weighted K-way reduction of returned expert outputs
+ *     (mep_combine).
+ *
+ * Sources, cited by page title and section:
+ *   [MoonEP-TD]  "MoonEP" technical overview (twodots.gr), architecture and
+ *                memory-contract sections: every EP rank processes exactly
+ *                S*K routed rows; temporary redundant expert copies planned
+ *                online on the GPU from the router output; tokens land at
+ *                their final position grouped by expert; planner-made
+ *                cu_seqlens; static S*K buffers so no per-layer host sync.
+ *   [MoonEP-API] "MoonEP API完全参考" (stapisi.com), sections 2.2 (planning)
+ *                and 3.1 (dispatch and combine).
+ *   [UpdExp]     "aclnnMoeUpdateExpert" op doc: "功能说明" (remap and pruning
+ *                formulas), "函数原型"/"参数说明" (two-phase API, parameters),
+ *                "返回值" (status codes), "约束说明" (constraints).
+ *
+ * Conventions for every call:
+ *   - Pointers are DEVICE pointers unless marked (host). The caller owns
+ *     every buffer; the library keeps no state between calls and never
+ *     allocates device memory.
+ *   - bf16 data is passed as raw 16-bit patterns (uint16_t); ids, tables
+ *     and maps are int32_t; masks are uint8_t holding 0 or 1.
+ *   - `stream` is a hipStream_t (NULL = the legacy default stream). Calls
+ *     only enqueue work: no host synchronisation, no host read of device
+ *     data. Outputs are complete when the stream reaches that point.
+ *   - Arguments are validated on the host before anything is enqueued; on
+ *     an error status nothing has been enqueued. Device-side VALUES (ids in
+ *     range, table entries valid, maps forming the stated permutations) are
+ *     the caller's responsibility, as in [UpdExp] "参数说明" (the table's
+ *     values must be correct); kernels clamp their own reads so that bad
+ *     values give wrong results, not out-of-bounds accesses (an
+ *     out-of-range row index skips that row).
+ *   - Row pointers (x, send_buf, recv_raw, recv_grouped, y_ret, out_bf16,
+ *     out_f32) must be 16-byte aligned and H a multiple of 8.
+ *   - Every output is a pure function of the inputs (no order-dependent
+ *     atomics), as [UpdExp] "约束说明" asks (deterministic by default).
+ *   - Calls are reentrant; concurrent calls must not share output buffers.
+ */
+#ifndef MEP_H
+#define MEP_H
+
+#include <stddef.h>
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+/* Status codes. The three argument errors mirror the op doc's
+ * ACLNN_ERR_PARAM_NULLPTR, ACLNN_ERR_PARAM_INVALID and
+ * ACLNN_ERR_INNER_TILING_ERROR ([UpdExp] "返回值"). */
+typedef enum {
+    MEP_OK = 0,
+    MEP_ERR_NULLPTR = 1, /* a required pointer is NULL */
+    MEP_ERR_PARAM = 2,   /* bad mode, unpaired optional arguments, rank out
+                            of range, workspace too small, K > E */
+    MEP_ERR_SHAPE = 3,   /* a size out of the supported range, H % 8 != 0,
+                            a row pointer not 16-byte aligned */
+    MEP_ERR_HIP = 4      /* the HIP runtime reported an error at launch */
+} mep_status;
+
+/* Human-readable name of a status (static string, never NULL). */
+const char* mep_status_str(int status);
+
+/* Library version as major*10000 + minor*100 + patch. */
+int mep_version(void);
+
+/* ------------------------------------------------------------------ plan */
+
+/* Supported plan sizes: 1 <= R <= 1024, 1 <= E <= 1024, 1 <= K <= E,
+ * S >= 1, R*S*K <= 2^30. */
+
+/*
+ * Bytes of device workspace mep_plan needs for these sizes (host-only, pure
+ * function; [UpdExp] "函数原型": size query before execution). Returns 0 if
+ * the sizes are unsupported.
+ */
+size_t mep_plan_workspace_size(int R, int E, int S, int K);
+
+/*
+ * mep_plan - global balanced plan and rank `my_rank`'s maps.
+ *
+ * [MoonEP-TD] invariant: each of the R ranks receives exactly C = S*K
+ * routed rows. With home(e) = floor(e*R/E), native loads
+ * L[r] = sum of cnt[e] over home(e) = r, and routes f = g*K + k
+ * (g = src*S + s) taken in (expert, g, k) order:
+ *   - each rank keeps the first C of its routes at slots 0..C-1 in order;
+ *   - the remaining routes of over-loaded ranks, in the same global order,
+ *     fill the under-loaded ranks in ascending rank order, rank u taking
+ *     C - L[u] routes at slots L[u], L[u]+1, ...; each (expert, rank != home)
+ *     pair so created is a redundant instance.
+ * Rank u's local layout (its grouped receive buffer; the row offsets are the
+ * cu_seqlens of [MoonEP-TD]): native experts in ascending e (zero-row
+ * natives keep their place), then redundant instances in ascending e. A
+ * global instance id (gid) numbers instances in (rank, local index) order.
+ *
+ * Inputs:
+ *   topk_ids   [R*S*K] int32, row-major [R][S][K]: the whole routing table;
+ *              values in [0, E).
+ *   workspace  device buffer of at least mep_plan_workspace_size() bytes,
+ *              256-byte aligned; contents on entry do not matter; clobbered.
+ * Outputs (all int32, all overwritten):
+ *   expert_count  [E]      routes per expert.
+ *   rank_load     [R]      native loads L[r] (before balancing).
+ *   route_dest    [R*S*K]  destination rank of each route   (may be NULL).
+ *   route_slot    [R*S*K]  slot on that rank, in [0, C)      (may be NULL;
+ *                          NULL together with route_dest).
+ *   inst_count    [R]      instances per rank (natives + redundant).
+ *   inst_expert   [R][E]   expert of local instance i; -1 past inst_count.
+ *   inst_cu       [R][E+1] row offset of local instance i; entries past
+ *                          inst_count hold C.
+ *   inst_gid_base [R+1]    exclusive prefix of inst_count.
+ *   send_pos      [S*K]    row of route (my_rank, s, k) in the send buffer,
+ *                          ordered by (destination, destination slot).
+ *   send_count    [R]      rows sent to each destination.
+ *   recv_pos      [C]      for grouped slot t of my_rank, the row of the
+ *                          source-major arrival buffer (sources ascending,
+ *                          each source's rows in slot order) holding it.
+ *   recv_count    [R]      rows received from each source.
+ * Errors: MEP_ERR_NULLPTR (required pointer NULL), MEP_ERR_SHAPE (sizes),
+ *   MEP_ERR_PARAM (my_rank out of range, K > E, workspace too small or
+ *   misaligned, only one of route_dest/route_slot given), MEP_ERR_HIP.
+ */
+int mep_plan(int R, int E, int S, int K, int my_rank,
+             const int32_t* topk_ids, void* workspace, size_t workspace_bytes,
+             int32_t* expert_count, int32_t* rank_load,
+             int32_t* route_dest, int32_t* route_slot,
+             int32_t* inst_count, int32_t* inst_expert, int32_t* inst_cu,
+             int32_t* inst_gid_base,
+             int32_t* send_pos, int32_t* send_count,
+             int32_t* recv_pos, int32_t* recv_count,
+             void* stream);
+
+/* ---------------------------------------------------------- remap / prune */
+
+/* Scale element types accepted by mep_remap_prune ([UpdExp] "参数说明":
+ * FLOAT, BFLOAT16, FLOAT16). */
+enum { MEP_SCALE_F32 = 0, MEP_SCALE_BF16 = 1, MEP_SCALE_F16 = 2 };
+
+/*
+ * mep_remap_prune - EPLB logical -> physical instance remap and pruning
+ * ([UpdExp] "功能说明").
+ *
+ * Remap, for token t and slot k, e = expert_ids[t*K+k],
+ * count = eplb_table[e*F] (instances of e, in [1, F-1]):
+ *   count == 1        -> column 1
+ *   balance_mode == 0 -> column local_rank_id / ceil(world_size/count) + 1
+ *   balance_mode == 1 -> column (t mod count) + 1
+ *   balanced_ids[t*K+k] = eplb_table[e*F + column]
+ * Pruning (only with expert_scales and pruning_threshold), scales widened
+ * exactly to fp32:
+ *   thr_sum[t] = sum over k = 0..K-1 of fl(scale[t,k] * threshold[k]),
+ *                accumulated in k order from +0.0f, each step rounded to fp32
+ *   balanced_mask[t*K+k] = active[t] && !(scale[t,k] < thr_sum[t])
+ * (a route below the token's sum is pruned; a tie is kept; every route of
+ * an inactive token is pruned). Without scales and threshold the mask is
+ * all ones. Pruned routes still receive a remapped id.
+ * Send map (when send_pos is given): kept routes ordered by (card, instance,
+ * t, k), where card = instance / place_per_rank;
+ *   send_pos[t*K+k] = row in that order, or -1 if pruned;
+ *   send_count[card] = kept routes per card ([world_size] entries).
+ *
+ * Inputs:
+ *   expert_ids        [BS*K] int32 in [0, E).
+ *   eplb_table        [E*F]  int32; column 0 the count, columns 1..count
+ *                     instance ids in [0, world_size*place_per_rank).
+ *   expert_scales     [BS*K] of scale_dtype (MEP_SCALE_*), sorted
+ *                     descending per token; may be NULL.
+ *   pruning_threshold [K] fp32 ((K,) and (1,K) alike); NULL iff scales NULL.
+ *   active_mask       [BS] uint8, ones before zeros; may be NULL (= all
+ *                     active); needs scales and threshold.
+ * Outputs: balanced_ids [BS*K] int32, balanced_mask [BS*K] uint8,
+ *   send_pos [BS*K] int32 and send_count [world_size] int32 (both NULL or
+ *   both given).
+ * Limits ([UpdExp] "约束说明"): 1 <= BS <= 65536, 1 <= K <= 16, K <= E,
+ *   1 <= E <= 1024, 2 <= F <= world_size+1, 1 <= world_size <= 1024,
+ *   world_size*place_per_rank <= 1024, balance_mode in {0,1};
+ *   mode 0 needs 0 <= local_rank_id < world_size.
+ * Errors: MEP_ERR_NULLPTR, MEP_ERR_PARAM (mode, unpaired optionals, rank,
+ *   dtype), MEP_ERR_SHAPE (limits), MEP_ERR_HIP.
+ */
+int mep_remap_prune(int BS, int K, int E, int F, int world_size,
+                    int place_per_rank, int local_rank_id, int balance_mode,
+                    const int32_t* expert_ids, const int32_t* eplb_table,
+                    const void* expert_scales, int scale_dtype,
+                    const float* pruning_threshold, const uint8_t* active_mask,
+                    int32_t* balanced_ids, uint8_t* balanced_mask,
+                    int32_t* send_pos, int32_t* send_count,
+                    void* stream);
+
+/* ---------------------------------------------------------------- dispatch */
+
+/*
+ * mep_dispatch - pack this rank's token rows into per-destination send
+ * segments, and/or group received rows by expert instance ([MoonEP-API]
+ * 3.1; [MoonEP-TD]: rows land grouped by expert at the destination).
+ *
+ * Pack (runs when x != NULL):
+ *   send_buf[send_pos[t*K+k], :] = x[t, :] for every send_pos >= 0.
+ *   x [T,H] bf16; send_pos [T*K] int32 (a row index < T*K, or negative to
+ *   skip the route); send_buf [T*K, H] bf16 (rows not named by send_pos
+ *   are left untouched).
+ * Group (runs when recv_raw != NULL):
+ *   recv_grouped[t, :] = recv_raw[recv_pos[t], :] for t in [0, n_recv).
+ *   recv_raw [n_recv,H] bf16 in arrival (source-major) order; recv_pos
+ *   [n_recv] int32 in [0, n_recv); recv_grouped [n_recv,H] bf16.
+ * At least one of the two must run, unless T == 0 and n_recv == 0 (then
+ * the call does nothing and may pass NULL buffers). Sizes: T >= 0, n_recv >= 0,
+ * 1 <= K <= 64, 8 <= H <= 65536 with H % 8 == 0.
+ * Errors: MEP_ERR_NULLPTR, MEP_ERR_PARAM (neither phase requested),
+ *   MEP_ERR_SHAPE, MEP_ERR_HIP.
+ */
+int mep_dispatch(int T, int K, int H,
+                 const uint16_t* x, const int32_t* send_pos, uint16_t* send_buf,
+                 int n_recv, const int32_t* recv_pos, const uint16_t* recv_raw,
+                 uint16_t* recv_grouped,
+                 void* stream);
+
+/* ----------------------------------------------------------------- combine */
+
+/*
+ * mep_combine - score-weighted K-way reduction of the returned expert
+ * outputs in fixed k order ([MoonEP-API] 3.1 combine; the op doc's combine
+ * takes the same per-route expert scales).
+ *   acc = +0.0f
+ *   for k = 0..K-1 with send_pos[t*K+k] >= 0:
+ *       acc = fl(acc + fl(scores[t*K+k] * float(y_ret[send_pos[t*K+k], h])))
+ *   out_f32[t,h] = acc; out_bf16[t,h] = acc rounded to nearest even.
+ * Scores are used as given (no renormalisation).
+ *   y_ret [n_y,H] bf16 in this rank's send order; send_pos [T*K] int32
+ *   (a row < n_y; a negative or out-of-range entry skips the route);
+ *   scores [T*K] fp32; out_bf16 [T,H] bf16
+ *   and out_f32 [T,H] fp32, either may be NULL but not both.
+ * Sizes: T >= 0, 1 <= K <= 64, 8 <= H <= 65536, H % 8 == 0. With T == 0
+ * the call does nothing (buffers may be NULL).
+ * Errors: MEP_ERR_NULLPTR, MEP_ERR_SHAPE, MEP_ERR_HIP.
+ */
+int mep_combine(int T, int K, int H, const uint16_t* y_ret, int n_y,
+                const int32_t* send_pos, const float* scores,
+                uint16_t* out_bf16, float* out_f32,
+                void* stream);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* MEP_H */

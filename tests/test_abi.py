@@ -1,0 +1,142 @@
+"""The C-ABI library: it loads, exports every function include/mep.h
+declares, and rejects bad arguments on the host before touching the GPU.
+
+No compute call is made here (no GPU is needed).
+"""
+import ctypes
+import os
+import re
+import subprocess
+
+import pytest
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+HEADER = os.path.join(ROOT, "include", "mep.h")
+
+
+def _declared():
+    src = open(HEADER).read()
+    src = re.sub(r"/\*.*?\*/", "", src, flags=re.S)
+    return sorted(set(re.findall(r"\b(mep_[a-z_]+)\s*\(", src)))
+
+
+@pytest.fixture(scope="module")
+def B():
+    from combine_balancing_amd import _binding
+    if not os.path.exists(_binding.LIB_PATH):
+        from combine_balancing_amd import build
+        build.build()
+    _binding.lib()
+    return _binding
+
+
+def test_header_declares_the_four_entry_points():
+    names = _declared()
+    for n in ("mep_plan", "mep_remap_prune", "mep_dispatch", "mep_combine",
+              "mep_plan_workspace_size", "mep_status_str", "mep_version"):
+        assert n in names
+
+
+def test_every_declared_symbol_is_exported(B):
+    lib = ctypes.CDLL(B.LIB_PATH)
+    for n in _declared():
+        assert hasattr(lib, n), n
+    out = subprocess.run(["nm", "-D", "--defined-only", B.LIB_PATH], capture_output=True,
+                         text=True, check=True).stdout
+    exported = set(re.findall(r"\bT (mep_[a-z_]+)\b", out))
+    assert set(_declared()) <= exported
+
+
+def test_library_has_gfx950_code(B):
+    # the offload bundle embedded in the library names its one target
+    data = open(B.LIB_PATH, "rb").read()
+    assert b"__CLANG_OFFLOAD_BUNDLE__" in data
+    assert b"amdgcn-amd-amdhsa--gfx950" in data
+    assert b"gfx942" not in data and b"sm_" + b"90" not in data
+
+
+def test_status_strings(B):
+    assert B.status_str(0) == "MEP_OK"
+    for c in range(1, 5):
+        assert B.status_str(c).startswith("MEP_ERR")
+    assert B.lib().mep_version() >= 100
+
+
+def test_workspace_size(B):
+    assert B.mep_plan_workspace_size(8, 256, 4096, 8) > 8 * 256 * 4
+    assert B.mep_plan_workspace_size(0, 256, 4096, 8) == 0
+    assert B.mep_plan_workspace_size(8, 2000, 4096, 8) == 0   # E > 1024
+    assert B.mep_plan_workspace_size(8, 4, 16, 8) == 0       # K > E
+    assert B.mep_plan_workspace_size(2048, 256, 16, 8) == 0  # R > 1024
+    assert B.mep_plan_workspace_size(1024, 1024, 1 << 17, 16) == 0  # N > 2^30
+
+
+def _plan(B, R=8, E=256, S=16, K=8, m=0, ids=1, ws=256, wsb=1 << 30, outs=1, rd=1, rs=1):
+    o = [outs] * 12
+    o[2], o[3] = rd, rs
+    return B.mep_plan(R, E, S, K, m, ids, ws, wsb, *o, None)
+
+
+def test_plan_validation(B):
+    assert _plan(B, ids=None) == B.MEP_ERR_NULLPTR
+    assert _plan(B, outs=None, rd=1, rs=1) == B.MEP_ERR_NULLPTR
+    assert _plan(B, R=0) == B.MEP_ERR_SHAPE
+    assert _plan(B, E=1025) == B.MEP_ERR_SHAPE
+    assert _plan(B, K=300) == B.MEP_ERR_PARAM
+    assert _plan(B, m=8) == B.MEP_ERR_PARAM
+    assert _plan(B, m=-1) == B.MEP_ERR_PARAM
+    assert _plan(B, wsb=16) == B.MEP_ERR_PARAM
+    assert _plan(B, ws=258) == B.MEP_ERR_PARAM      # misaligned workspace
+    assert _plan(B, rd=None) == B.MEP_ERR_PARAM     # route maps come in pairs
+
+
+def _remap(B, BS=4, K=2, E=8, F=3, ws=4, ppr=2, rank=0, mode=0, ids=1, table=1, sc=None,
+           sdt=1, thr=None, act=None, bal=1, mask=1, sp=None, scnt=None):
+    return B.mep_remap_prune(BS, K, E, F, ws, ppr, rank, mode, ids, table, sc, sdt, thr, act,
+                             bal, mask, sp, scnt, None)
+
+
+def test_remap_validation(B):
+    assert _remap(B, ids=None) == B.MEP_ERR_NULLPTR
+    assert _remap(B, mask=None) == B.MEP_ERR_NULLPTR
+    assert _remap(B, mode=2) == B.MEP_ERR_PARAM
+    assert _remap(B, sc=16) == B.MEP_ERR_PARAM              # scales without threshold
+    assert _remap(B, thr=16) == B.MEP_ERR_PARAM             # threshold without scales
+    assert _remap(B, act=16) == B.MEP_ERR_PARAM             # mask without scales
+    assert _remap(B, sp=16) == B.MEP_ERR_PARAM              # send map needs both
+    assert _remap(B, sc=16, thr=16, sdt=7) == B.MEP_ERR_PARAM
+    assert _remap(B, rank=4) == B.MEP_ERR_PARAM             # mode 0 rank out of range
+    assert _remap(B, K=17) == B.MEP_ERR_SHAPE
+    assert _remap(B, K=9, E=8) == B.MEP_ERR_PARAM
+    assert _remap(B, F=6, ws=4) == B.MEP_ERR_SHAPE          # F > world_size + 1
+    assert _remap(B, F=1) == B.MEP_ERR_SHAPE
+    assert _remap(B, ws=600, ppr=2) == B.MEP_ERR_SHAPE      # > 1024 instances
+    assert _remap(B, BS=0) == B.MEP_ERR_SHAPE
+    assert _remap(B, E=1025) == B.MEP_ERR_SHAPE
+
+
+def test_dispatch_combine_validation(B):
+    D = B.mep_dispatch
+    assert D(4, 2, 64, None, None, None, 0, None, None, None, None) == B.MEP_ERR_PARAM
+    assert D(0, 2, 64, None, None, None, 0, None, None, None, None) == B.MEP_OK
+    assert D(4, 2, 64, 16, None, 16, 0, None, None, None, None) == B.MEP_ERR_NULLPTR
+    assert D(4, 2, 60, 16, 16, 16, 0, None, None, None, None) == B.MEP_ERR_SHAPE   # H % 8
+    assert D(4, 2, 64, 8, 16, 16, 0, None, None, None, None) == B.MEP_ERR_SHAPE    # unaligned
+    assert D(4, 65, 64, 16, 16, 16, 0, None, None, None, None) == B.MEP_ERR_SHAPE  # K > 64
+    assert D(0, 2, 64, None, None, None, 4, 16, 16, None, None) == B.MEP_ERR_NULLPTR
+    assert D(0, 2, 64, None, None, None, -1, 16, 16, 16, None) == B.MEP_ERR_SHAPE
+    Cb = B.mep_combine
+    assert Cb(0, 2, 64, None, 0, None, None, None, None, None) == B.MEP_OK
+    assert Cb(4, 2, 64, None, 8, 16, 16, 16, None, None) == B.MEP_ERR_NULLPTR
+    assert Cb(4, 2, 64, 16, 8, 16, 16, None, None, None) == B.MEP_ERR_NULLPTR
+    assert Cb(4, 2, 64, 24, 8, 16, 16, 16, None, None) == B.MEP_ERR_SHAPE          # unaligned
+    assert Cb(4, 0, 64, 16, 8, 16, 16, 16, None, None) == B.MEP_ERR_SHAPE
+    assert Cb(4, 2, 12, 16, 8, 16, 16, 16, None, None) == B.MEP_ERR_SHAPE
+
+
+def test_package_has_no_fallback(monkeypatch, tmp_path):
+    from combine_balancing_amd import _binding
+    monkeypatch.setattr(_binding, "LIB_PATH", str(tmp_path / "missing.so"))
+    monkeypatch.setattr(_binding, "_lib", None)
+    with pytest.raises(RuntimeError, match="missing"):
+        _binding.lib()
