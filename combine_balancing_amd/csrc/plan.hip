@@ -185,10 +185,10 @@ __global__ __launch_bounds__(kGlobalThreads) void plan_global(PlanDims d, PlanWs
     __syncthreads();
 
     // 2. rank blocks, native loads, surplus and deficit prefixes
-    if (tid <= R) {
-        const int rb = s_eex[efirst_of(tid, R, E)];
-        s_rb[tid] = rb;
-        w.rb[tid] = rb;
+    for (int r = tid; r <= R; r += NT) {  // R may equal the block size
+        const int rb = s_eex[efirst_of(r, R, E)];
+        s_rb[r] = rb;
+        w.rb[r] = rb;
     }
     __syncthreads();
     int L = 0, U = 0, D = 0;
