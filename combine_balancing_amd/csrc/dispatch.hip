@@ -9,13 +9,15 @@
 // in fixed k order in fp32.
 //
 // All three kernels move whole bf16 rows and are HBM-bound (no
-// contraction, no MFMA). One wave owns one row: each lane moves 16-byte
-// vectors at stride 64, so every wave-wide access is a contiguous 1 KiB
-// segment; a lane keeps up to 16 vectors (a 16 KiB row per wave) in flight
-// before its stores. Per-row indices and scores are wave-uniform and come
-// through scalar loads. Outputs are written once and not re-read by these
-// kernels, so stores are non-temporal. There is no reuse between blocks,
-// so the block -> XCD assignment does not matter for these kernels.
+// contraction, no MFMA). Every access is a 16-byte vector and consecutive
+// threads touch consecutive vectors of a row, so each wave-wide access is a
+// contiguous 1 KiB segment. Per-row indices and scores are uniform across
+// the threads that use them and come through scalar loads. Outputs are
+// written once and not re-read by these kernels, and inputs are read once,
+// so loads and stores are non-temporal. There is no reuse between
+// work-groups, so the work-group -> XCD assignment does not matter here.
+#include <algorithm>
+
 #include "mep_device.h"
 
 namespace mep {
@@ -24,25 +26,34 @@ namespace {
 typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
 typedef float f32x4 __attribute__((ext_vector_type(4)));
 
-constexpr int kRowThreads = 256;
-constexpr int kRowsPerBlock = kRowThreads / kWave;
+// Launch shapes (chosen by measurement on MI355X at H=7168):
+//  - pack: one wave per token; the row (up to 16 vectors per lane) is loaded
+//    once and each vector is stored to the K destinations back to back.
+//  - group and combine: one work-group per row (per token for combine),
+//    each thread owning VPT vectors of it, so a whole 14 KiB row is in flight
+//    at once; small rows share a work-group (RPB rows per group).
+constexpr int kPackThreads = 256;
+constexpr int kPackRows = kPackThreads / kWave;
 constexpr int kMaxVpl = 16;
+constexpr int kMaxTpr = 1024;
+constexpr int kCombineThreads = 256;  // K*VPT row loads in flight need the VGPRs
 
 __device__ __forceinline__ int wave_row() {
-    return __builtin_amdgcn_readfirstlane((int)(blockIdx.x * kRowsPerBlock + threadIdx.x / kWave));
+    return __builtin_amdgcn_readfirstlane((int)(blockIdx.x * kPackRows + threadIdx.x / kWave));
 }
 
 // ------------------------------------------------------------------- pack
 // send_buf[send_pos[t*K+k]] = x[t] for each k with 0 <= send_pos < nrows.
 template <int VPL>
-__global__ __launch_bounds__(kRowThreads) void pack_rows(const u32x4* __restrict__ x,
-                                                         const int* __restrict__ send_pos,
-                                                         u32x4* __restrict__ send_buf, int T, int K,
-                                                         int nvec, int nrows) {
+__global__ __launch_bounds__(kPackThreads) void pack_rows(const u32x4* __restrict__ x,
+                                                          const int* __restrict__ send_pos,
+                                                          u32x4* __restrict__ send_buf, int T, int K,
+                                                          int nvec, int nrows) {
     const int t = wave_row();
     if (t >= T) return;
     const int lane = lane_id();
-    const int my_pos = lane < K ? send_pos[(size_t)t * K + lane] : -1;
+    int my_pos = lane < K ? send_pos[(size_t)t * K + lane] : -1;
+    if ((unsigned)my_pos >= (unsigned)nrows) my_pos = -1;
     const u32x4* src = x + (size_t)t * nvec;
     for (int v0 = 0; v0 < nvec; v0 += kWave * VPL) {
         u32x4 r[VPL];
@@ -51,14 +62,13 @@ __global__ __launch_bounds__(kRowThreads) void pack_rows(const u32x4* __restrict
             const int v = v0 + i * kWave + lane;
             if (v < nvec) r[i] = __builtin_nontemporal_load(src + v);
         }
-        for (int k = 0; k < K; ++k) {
-            const int pos = __builtin_amdgcn_readlane(my_pos, k);
-            if ((unsigned)pos >= (unsigned)nrows) continue;
-            u32x4* dst = send_buf + (size_t)pos * nvec;
 #pragma unroll
-            for (int i = 0; i < VPL; ++i) {
-                const int v = v0 + i * kWave + lane;
-                if (v < nvec) __builtin_nontemporal_store(r[i], dst + v);
+        for (int i = 0; i < VPL; ++i) {
+            const int v = v0 + i * kWave + lane;
+            if (v >= nvec) continue;
+            for (int k = 0; k < K; ++k) {
+                const int pos = __builtin_amdgcn_readlane(my_pos, k);
+                if (pos >= 0) __builtin_nontemporal_store(r[i], send_buf + (size_t)pos * nvec + v);
             }
         }
     }
@@ -66,153 +76,158 @@ __global__ __launch_bounds__(kRowThreads) void pack_rows(const u32x4* __restrict
 
 // ------------------------------------------------------------------ group
 // recv_grouped[t] = recv_raw[recv_pos[t]] for 0 <= recv_pos[t] < n.
-template <int VPL>
-__global__ __launch_bounds__(kRowThreads) void group_rows(const u32x4* __restrict__ raw,
-                                                          const int* __restrict__ recv_pos,
-                                                          u32x4* __restrict__ out, int n,
-                                                          int nvec) {
-    const int t = wave_row();
+// blockDim = tpr * rpb; row t = blockIdx * rpb + threadIdx / tpr.
+template <int VPT>
+__global__ __launch_bounds__(kMaxTpr) void group_rows(const u32x4* __restrict__ raw,
+                                                      const int* __restrict__ recv_pos,
+                                                      u32x4* __restrict__ out, int n, int nvec,
+                                                      int tpr, int rpb) {
+    const int r = threadIdx.x / tpr;
+    const int tid = threadIdx.x - r * tpr;
+    const int t = blockIdx.x * rpb + r;
     if (t >= n) return;
     const int from = recv_pos[t];
     if ((unsigned)from >= (unsigned)n) return;
-    const int lane = lane_id();
     const u32x4* src = raw + (size_t)from * nvec;
     u32x4* dst = out + (size_t)t * nvec;
-    for (int v0 = 0; v0 < nvec; v0 += kWave * VPL) {
-        u32x4 r[VPL];
+    for (int v0 = 0; v0 < nvec; v0 += tpr * VPT) {
+        u32x4 q[VPT];
 #pragma unroll
-        for (int i = 0; i < VPL; ++i) {
-            const int v = v0 + i * kWave + lane;
-            if (v < nvec) r[i] = __builtin_nontemporal_load(src + v);
+        for (int i = 0; i < VPT; ++i) {
+            const int v = v0 + i * tpr + tid;
+            if (v < nvec) q[i] = __builtin_nontemporal_load(src + v);
         }
 #pragma unroll
-        for (int i = 0; i < VPL; ++i) {
-            const int v = v0 + i * kWave + lane;
-            if (v < nvec) __builtin_nontemporal_store(r[i], dst + v);
+        for (int i = 0; i < VPT; ++i) {
+            const int v = v0 + i * tpr + tid;
+            if (v < nvec) __builtin_nontemporal_store(q[i], dst + v);
         }
     }
 }
 
 // ---------------------------------------------------------------- combine
 // acc = +0; for k in order: acc = acc + score_k * y[pos_k] (each op rounded
-// to fp32: built without FMA contraction).
-template <int KT>
-__device__ __forceinline__ void combine_vec(const u32x4* __restrict__ y, const int* pos,
-                                            const float* sc, int nvec, int v,
-                                            u32x4* __restrict__ out_bf16,
-                                            f32x4* __restrict__ out_f32, size_t t) {
-    u32x4 yk[KT];
+// to fp32: built without FMA contraction). One work-group per token (rpb
+// tokens per group for small rows); each thread owns VPT vectors and keeps
+// their K loads in flight together.
+__device__ __forceinline__ void accumulate(float* acc, u32x4 w, float s) {
 #pragma unroll
-    for (int k = 0; k < KT; ++k)
-        if (pos[k] >= 0) yk[k] = __builtin_nontemporal_load(y + (size_t)pos[k] * nvec + v);
-    float acc[8];
-#pragma unroll
-    for (int j = 0; j < 8; ++j) acc[j] = 0.0f;
-#pragma unroll
-    for (int k = 0; k < KT; ++k) {
-        if (pos[k] < 0) continue;
-#pragma unroll
-        for (int j = 0; j < 4; ++j) {
-            const uint32_t w = yk[k][j];
-            acc[2 * j] = acc[2 * j] + sc[k] * __uint_as_float(w << 16);
-            acc[2 * j + 1] = acc[2 * j + 1] + sc[k] * __uint_as_float(w & 0xffff0000u);
-        }
+    for (int j = 0; j < 4; ++j) {
+        acc[2 * j] = acc[2 * j] + s * __uint_as_float(w[j] << 16);
+        acc[2 * j + 1] = acc[2 * j + 1] + s * __uint_as_float(w[j] & 0xffff0000u);
     }
+}
+
+__device__ __forceinline__ void store_out(const float* acc, u32x4* __restrict__ out_bf16,
+                                          f32x4* __restrict__ out_f32, size_t at) {
     if (out_bf16) {
         u32x4 o;
 #pragma unroll
         for (int j = 0; j < 4; ++j)
             o[j] = float_to_bf16_bits(acc[2 * j]) | (float_to_bf16_bits(acc[2 * j + 1]) << 16);
-        __builtin_nontemporal_store(o, out_bf16 + t * nvec + v);
+        __builtin_nontemporal_store(o, out_bf16 + at);
     }
     if (out_f32) {
         const f32x4 a = {acc[0], acc[1], acc[2], acc[3]};
         const f32x4 b = {acc[4], acc[5], acc[6], acc[7]};
-        __builtin_nontemporal_store(a, out_f32 + (t * nvec + v) * 2);
-        __builtin_nontemporal_store(b, out_f32 + (t * nvec + v) * 2 + 1);
+        __builtin_nontemporal_store(a, out_f32 + at * 2);
+        __builtin_nontemporal_store(b, out_f32 + at * 2 + 1);
     }
 }
 
-template <int KT>
-__global__ __launch_bounds__(kRowThreads) void combine_rows(const u32x4* __restrict__ y, int n_y,
-                                                            const int* __restrict__ send_pos,
-                                                            const float* __restrict__ scores,
-                                                            u32x4* __restrict__ out_bf16,
-                                                            f32x4* __restrict__ out_f32, int T,
-                                                            int nvec) {
-    const int t = wave_row();
+template <int KT, int VPT>
+__global__ __launch_bounds__(kCombineThreads) void combine_rows(const u32x4* __restrict__ y, int n_y,
+                                                                const int* __restrict__ send_pos,
+                                                                const float* __restrict__ scores,
+                                                                u32x4* __restrict__ out_bf16,
+                                                                f32x4* __restrict__ out_f32, int T,
+                                                                int nvec, int tpr, int rpb) {
+    const int r = threadIdx.x / tpr;
+    const int tid = threadIdx.x - r * tpr;
+    const int t = blockIdx.x * rpb + r;
     if (t >= T) return;
+    // Skipped routes (negative or out-of-range rows) still load row 0 so that
+    // all K loads issue together; their terms are then left out exactly.
     int pos[KT];
     float sc[KT];
+    uint32_t use = 0;
 #pragma unroll
     for (int k = 0; k < KT; ++k) {
         const int p = send_pos[(size_t)t * KT + k];
-        pos[k] = (unsigned)p < (unsigned)n_y ? p : -1;
+        const bool ok = (unsigned)p < (unsigned)n_y;
+        use |= (uint32_t)ok << k;
+        pos[k] = ok ? p : 0;
         sc[k] = scores[(size_t)t * KT + k];
     }
-    const int lane = lane_id();
-#pragma unroll 2
-    for (int v = lane; v < nvec; v += kWave)
-        combine_vec<KT>(y, pos, sc, nvec, v, out_bf16, out_f32, (size_t)t);
+    for (int v0 = 0; v0 < nvec; v0 += tpr * VPT) {
+        u32x4 yk[VPT][KT];
+#pragma unroll
+        for (int i = 0; i < VPT; ++i) {
+            const int v = min(v0 + i * tpr + tid, nvec - 1);
+#pragma unroll
+            for (int k = 0; k < KT; ++k)
+                yk[i][k] = __builtin_nontemporal_load(y + (size_t)pos[k] * nvec + v);
+        }
+#pragma unroll
+        for (int i = 0; i < VPT; ++i) {
+            const int v = v0 + i * tpr + tid;
+            float acc[8];
+#pragma unroll
+            for (int j = 0; j < 8; ++j) acc[j] = 0.0f;
+#pragma unroll
+            for (int k = 0; k < KT; ++k)
+                if ((use >> k) & 1u) accumulate(acc, yk[i][k], sc[k]);
+            if (v < nvec) store_out(acc, out_bf16, out_f32, (size_t)t * nvec + v);
+        }
+    }
 }
 
 // Any K up to 64: one route at a time, in k order.
-__global__ __launch_bounds__(kRowThreads) void combine_rows_any(
+__global__ __launch_bounds__(kCombineThreads) void combine_rows_any(
     const u32x4* __restrict__ y, int n_y, const int* __restrict__ send_pos,
     const float* __restrict__ scores, u32x4* __restrict__ out_bf16, f32x4* __restrict__ out_f32,
-    int T, int K, int nvec) {
-    const int t = wave_row();
+    int T, int K, int nvec, int tpr, int rpb) {
+    const int r = threadIdx.x / tpr;
+    const int tid = threadIdx.x - r * tpr;
+    const int t = blockIdx.x * rpb + r;
     if (t >= T) return;
-    const int lane = lane_id();
-    for (int v = lane; v < nvec; v += kWave) {
+    for (int v = tid; v < nvec; v += tpr) {
         float acc[8];
 #pragma unroll
         for (int j = 0; j < 8; ++j) acc[j] = 0.0f;
         for (int k = 0; k < K; ++k) {
             const int p = send_pos[(size_t)t * K + k];
             if ((unsigned)p >= (unsigned)n_y) continue;
-            const float s = scores[(size_t)t * K + k];
-            const u32x4 w4 = y[(size_t)p * nvec + v];
-#pragma unroll
-            for (int j = 0; j < 4; ++j) {
-                acc[2 * j] = acc[2 * j] + s * __uint_as_float(w4[j] << 16);
-                acc[2 * j + 1] = acc[2 * j + 1] + s * __uint_as_float(w4[j] & 0xffff0000u);
-            }
+            accumulate(acc, y[(size_t)p * nvec + v], scores[(size_t)t * K + k]);
         }
-        if (out_bf16) {
-            u32x4 o;
-#pragma unroll
-            for (int j = 0; j < 4; ++j)
-                o[j] = float_to_bf16_bits(acc[2 * j]) | (float_to_bf16_bits(acc[2 * j + 1]) << 16);
-            out_bf16[(size_t)t * nvec + v] = o;
-        }
-        if (out_f32) {
-            const f32x4 a = {acc[0], acc[1], acc[2], acc[3]};
-            const f32x4 b = {acc[4], acc[5], acc[6], acc[7]};
-            out_f32[((size_t)t * nvec + v) * 2] = a;
-            out_f32[((size_t)t * nvec + v) * 2 + 1] = b;
-        }
+        store_out(acc, out_bf16, out_f32, (size_t)t * nvec + v);
     }
 }
 
 // ------------------------------------------------------------------- host
-int vpl_for(int nvec) {
-    const int v = (nvec + kWave - 1) / kWave;
-    return v < 1 ? 1 : (v > kMaxVpl ? kMaxVpl : v);
-}
-
 bool aligned16(const void* p) { return ((uintptr_t)p & 15u) == 0; }
 
-template <int VPL>
-void launch_pack(dim3 g, hipStream_t s, const u32x4* x, const int* sp, u32x4* buf, int T, int K,
-                 int nvec, int nrows) {
-    hipLaunchKernelGGL(pack_rows<VPL>, g, dim3(kRowThreads), 0, s, x, sp, buf, T, K, nvec, nrows);
+// Threads per row for `vpt` vectors per thread: a multiple of the wave size,
+// at most 1024; rows per work-group so that small rows still fill 256 threads.
+struct RowShape {
+    int tpr, rpb;
+};
+
+RowShape row_shape(int nvec, int vpt, int max_tpr) {
+    int tpr = (nvec + vpt - 1) / vpt;
+    tpr = (tpr + kWave - 1) / kWave * kWave;
+    if (tpr > max_tpr) tpr = max_tpr;
+    int rpb = 256 / tpr;
+    if (rpb < 1) rpb = 1;
+    return {tpr, rpb};
 }
 
 template <int VPL>
-void launch_group(dim3 g, hipStream_t s, const u32x4* raw, const int* rp, u32x4* out, int n,
-                  int nvec) {
-    hipLaunchKernelGGL(group_rows<VPL>, g, dim3(kRowThreads), 0, s, raw, rp, out, n, nvec);
+void launch_pack(hipStream_t s, const u32x4* x, const int* sp, u32x4* buf, int T, int K,
+                 int nvec, int nrows) {
+    const dim3 g((T + kPackRows - 1) / kPackRows);
+    hipLaunchKernelGGL(pack_rows<VPL>, g, dim3(kPackThreads), 0, s, x, sp, buf, T, K, nvec,
+                       nrows);
 }
 
 #define MEP_VPL_SWITCH(vpl, FN, ...)         \
@@ -235,11 +250,34 @@ void launch_group(dim3 g, hipStream_t s, const u32x4* raw, const int* rp, u32x4*
         default: FN<16>(__VA_ARGS__); break; \
     }
 
+void launch_group(hipStream_t s, const u32x4* raw, const int* rp, u32x4* out, int n, int nvec) {
+    // one vector per thread up to 1024 vectors (16 KiB rows), then 2, 4, 8
+    int vpt = 1;
+    while (vpt < 8 && nvec > kMaxTpr * vpt) vpt *= 2;
+    const RowShape rs = row_shape(nvec, vpt, kMaxTpr);
+    const dim3 g((n + rs.rpb - 1) / rs.rpb), b(rs.tpr * rs.rpb);
+    switch (vpt) {
+        case 1: hipLaunchKernelGGL(group_rows<1>, g, b, 0, s, raw, rp, out, n, nvec, rs.tpr, rs.rpb); break;
+        case 2: hipLaunchKernelGGL(group_rows<2>, g, b, 0, s, raw, rp, out, n, nvec, rs.tpr, rs.rpb); break;
+        case 4: hipLaunchKernelGGL(group_rows<4>, g, b, 0, s, raw, rp, out, n, nvec, rs.tpr, rs.rpb); break;
+        default: hipLaunchKernelGGL(group_rows<8>, g, b, 0, s, raw, rp, out, n, nvec, rs.tpr, rs.rpb); break;
+    }
+}
+
+// Vectors per thread in combine: about 32 row loads in flight per thread.
 template <int KT>
-void launch_combine(dim3 g, hipStream_t s, const u32x4* y, int n_y, const int* sp,
-                    const float* sc, u32x4* ob, f32x4* of, int T, int nvec) {
-    hipLaunchKernelGGL(combine_rows<KT>, g, dim3(kRowThreads), 0, s, y, n_y, sp, sc, ob, of, T,
-                       nvec);
+constexpr int combine_vpt() {
+    return KT > 8 ? 2 : 4;
+}
+
+template <int KT>
+void launch_combine(hipStream_t s, const u32x4* y, int n_y, const int* sp, const float* sc,
+                    u32x4* ob, f32x4* of, int T, int nvec) {
+    constexpr int VPT = combine_vpt<KT>();
+    const RowShape rs = row_shape(nvec, VPT, kCombineThreads);
+    const dim3 g((T + rs.rpb - 1) / rs.rpb), b(rs.tpr * rs.rpb);
+    hipLaunchKernelGGL((combine_rows<KT, VPT>), g, b, 0, s, y, n_y, sp, sc, ob, of, T, nvec,
+                       rs.tpr, rs.rpb);
 }
 
 }  // namespace
@@ -263,17 +301,15 @@ extern "C" int mep_dispatch(int T, int K, int H, const uint16_t* x, const int32_
     if (do_group && (!aligned16(recv_raw) || !aligned16(recv_grouped))) return MEP_ERR_SHAPE;
     hipStream_t s = (hipStream_t)stream;
     const int nvec = H / 8;
-    const int vpl = vpl_for(nvec);
     if (do_pack && T > 0) {
-        const dim3 g((T + kRowsPerBlock - 1) / kRowsPerBlock);
-        MEP_VPL_SWITCH(vpl, launch_pack, g, s, (const u32x4*)x, (const int*)send_pos,
+        const int vpl = std::min(kMaxVpl, std::max(1, (nvec + kWave - 1) / kWave));
+        MEP_VPL_SWITCH(vpl, launch_pack, s, (const u32x4*)x, (const int*)send_pos,
                        (u32x4*)send_buf, T, K, nvec, T * K);
         MEP_LAUNCH_CHECK();
     }
     if (do_group && n_recv > 0) {
-        const dim3 g((n_recv + kRowsPerBlock - 1) / kRowsPerBlock);
-        MEP_VPL_SWITCH(vpl, launch_group, g, s, (const u32x4*)recv_raw, (const int*)recv_pos,
-                       (u32x4*)recv_grouped, n_recv, nvec);
+        launch_group(s, (const u32x4*)recv_raw, (const int*)recv_pos, (u32x4*)recv_grouped,
+                     n_recv, nvec);
         MEP_LAUNCH_CHECK();
     }
     return MEP_OK;
@@ -292,32 +328,34 @@ extern "C" int mep_combine(int T, int K, int H, const uint16_t* y_ret, int n_y,
         return MEP_ERR_SHAPE;
     hipStream_t s = (hipStream_t)stream;
     const int nvec = H / 8;
-    const dim3 g((T + kRowsPerBlock - 1) / kRowsPerBlock);
     const u32x4* y = (const u32x4*)y_ret;
     const int* sp = (const int*)send_pos;
     u32x4* ob = (u32x4*)out_bf16;
     f32x4* of = (f32x4*)out_f32;
-    switch (K) {
-        case 1: launch_combine<1>(g, s, y, n_y, sp, scores, ob, of, T, nvec); break;
-        case 2: launch_combine<2>(g, s, y, n_y, sp, scores, ob, of, T, nvec); break;
-        case 3: launch_combine<3>(g, s, y, n_y, sp, scores, ob, of, T, nvec); break;
-        case 4: launch_combine<4>(g, s, y, n_y, sp, scores, ob, of, T, nvec); break;
-        case 5: launch_combine<5>(g, s, y, n_y, sp, scores, ob, of, T, nvec); break;
-        case 6: launch_combine<6>(g, s, y, n_y, sp, scores, ob, of, T, nvec); break;
-        case 7: launch_combine<7>(g, s, y, n_y, sp, scores, ob, of, T, nvec); break;
-        case 8: launch_combine<8>(g, s, y, n_y, sp, scores, ob, of, T, nvec); break;
-        case 9: launch_combine<9>(g, s, y, n_y, sp, scores, ob, of, T, nvec); break;
-        case 10: launch_combine<10>(g, s, y, n_y, sp, scores, ob, of, T, nvec); break;
-        case 11: launch_combine<11>(g, s, y, n_y, sp, scores, ob, of, T, nvec); break;
-        case 12: launch_combine<12>(g, s, y, n_y, sp, scores, ob, of, T, nvec); break;
-        case 13: launch_combine<13>(g, s, y, n_y, sp, scores, ob, of, T, nvec); break;
-        case 14: launch_combine<14>(g, s, y, n_y, sp, scores, ob, of, T, nvec); break;
-        case 15: launch_combine<15>(g, s, y, n_y, sp, scores, ob, of, T, nvec); break;
-        case 16: launch_combine<16>(g, s, y, n_y, sp, scores, ob, of, T, nvec); break;
-        default:
-            hipLaunchKernelGGL(combine_rows_any, g, dim3(kRowThreads), 0, s, y, n_y, sp, scores,
-                               ob, of, T, K, nvec);
+    switch (n_y > 0 ? K : 0) {
+        case 1: launch_combine<1>(s, y, n_y, sp, scores, ob, of, T, nvec); break;
+        case 2: launch_combine<2>(s, y, n_y, sp, scores, ob, of, T, nvec); break;
+        case 3: launch_combine<3>(s, y, n_y, sp, scores, ob, of, T, nvec); break;
+        case 4: launch_combine<4>(s, y, n_y, sp, scores, ob, of, T, nvec); break;
+        case 5: launch_combine<5>(s, y, n_y, sp, scores, ob, of, T, nvec); break;
+        case 6: launch_combine<6>(s, y, n_y, sp, scores, ob, of, T, nvec); break;
+        case 7: launch_combine<7>(s, y, n_y, sp, scores, ob, of, T, nvec); break;
+        case 8: launch_combine<8>(s, y, n_y, sp, scores, ob, of, T, nvec); break;
+        case 9: launch_combine<9>(s, y, n_y, sp, scores, ob, of, T, nvec); break;
+        case 10: launch_combine<10>(s, y, n_y, sp, scores, ob, of, T, nvec); break;
+        case 11: launch_combine<11>(s, y, n_y, sp, scores, ob, of, T, nvec); break;
+        case 12: launch_combine<12>(s, y, n_y, sp, scores, ob, of, T, nvec); break;
+        case 13: launch_combine<13>(s, y, n_y, sp, scores, ob, of, T, nvec); break;
+        case 14: launch_combine<14>(s, y, n_y, sp, scores, ob, of, T, nvec); break;
+        case 15: launch_combine<15>(s, y, n_y, sp, scores, ob, of, T, nvec); break;
+        case 16: launch_combine<16>(s, y, n_y, sp, scores, ob, of, T, nvec); break;
+        default: {
+            const RowShape rs = row_shape(nvec, 1, kCombineThreads);
+            hipLaunchKernelGGL(combine_rows_any, dim3((T + rs.rpb - 1) / rs.rpb),
+                               dim3(rs.tpr * rs.rpb), 0, s, y, n_y, sp, scores, ob, of, T, K,
+                               nvec, rs.tpr, rs.rpb);
             break;
+        }
     }
     MEP_LAUNCH_CHECK();
     return MEP_OK;
