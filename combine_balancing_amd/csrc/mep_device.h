@@ -76,6 +76,44 @@ __device__ __forceinline__ int block_exclusive_sum(int v, int* scratch, int* tot
     return res;
 }
 
+// Two exclusive block-wide sums with one pair of barriers. `scratch` holds
+// at least 2*(blockDim/64 + 1) ints of LDS.
+__device__ __forceinline__ void block_exclusive_sum2(int a, int b, int* scratch, int* ea, int* eb,
+                                                     int* ta, int* tb) {
+    const int lane = threadIdx.x & (kWave - 1);
+    const int wave = threadIdx.x / kWave;
+    const int nw = (blockDim.x + kWave - 1) / kWave;
+    int* sa = scratch;
+    int* sb = scratch + nw + 1;
+    const int ia = wave_inclusive_sum(a);
+    const int ib = wave_inclusive_sum(b);
+    if (lane == kWave - 1 || (int)threadIdx.x == (int)blockDim.x - 1) {
+        sa[wave] = ia;
+        sb[wave] = ib;
+    }
+    __syncthreads();
+    if (wave == 0) {
+        const int wa = lane < nw ? sa[lane] : 0;
+        const int wb = lane < nw ? sb[lane] : 0;
+        const int xa = wave_inclusive_sum(wa);
+        const int xb = wave_inclusive_sum(wb);
+        if (lane < nw) {
+            sa[lane] = xa - wa;
+            sb[lane] = xb - wb;
+        }
+        if (lane == nw - 1) {
+            sa[nw] = xa;
+            sb[nw] = xb;
+        }
+    }
+    __syncthreads();
+    *ea = ia - a + sa[wave];
+    *eb = ib - b + sb[wave];
+    *ta = sa[nw];
+    *tb = sb[nw];
+    __syncthreads();
+}
+
 // Smallest index i in [0, n) with a[i] >= x (n if none).
 __device__ __forceinline__ int lower_bound(const int* a, int n, int x) {
     int lo = 0, hi = n;

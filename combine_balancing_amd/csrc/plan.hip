@@ -39,17 +39,25 @@
 namespace mep {
 namespace {
 
+#ifndef MEP_PLAN_ROUTE_THREADS
+#define MEP_PLAN_ROUTE_THREADS 256
+#endif
+#ifndef MEP_PLAN_CHUNK
+#define MEP_PLAN_CHUNK 1024
+#endif
 constexpr int kHistThreads = 256;
 constexpr int kScanThreads = 1024;
 constexpr int kScanItems = 4;
 constexpr int kMaxChunks = kScanThreads * kScanItems;
 constexpr int kGlobalThreads = 1024;
-constexpr int kRouteThreads = 256;
+constexpr int kRouteThreads = MEP_PLAN_ROUTE_THREADS;  // work-group of plan_routes
+constexpr int kMinChunk = MEP_PLAN_CHUNK;              // routes per chunk (at least)
 constexpr int kRouteWaves = kRouteThreads / kWave;
 constexpr int kMaxR = 1024;
 constexpr int kMaxE = 1024;
+constexpr int kStageIds = 4096;  // chunk sizes up to this keep their ids in LDS
 
-enum { SC_NP = 0, SC_EFIRST_M = 1, SC_NAT_M = 2, SC_FP_M = 3, SC_COUNT = 16 };
+enum { SC_NP = 0, SC_EFIRST_M = 1, SC_NAT_M = 2, SC_FP_M = 3, SC_NIM = 4, SC_COUNT = 16 };
 
 struct PlanDims {
     int R, E, S, K, m;
@@ -69,17 +77,11 @@ struct PlanWs {
     int* load;      // [R]   native loads
     int* uex;       // [R+1] exclusive prefix of surplus
     int* dex;       // [R+1] exclusive prefix of deficit
-    int* kept;      // [E]   routes of e kept on its home rank
-    int* js;        // [E]   excess-list index of e's first spilled route
     int* pstart;    // [E+R+1] excess index where each piece starts (sorted)
-    int* phost;     // [E+R]
-    int* pexpert;   // [E+R]
-    int* ppos;      // [E+R] position of the piece's first route
-    int* pn;        // [E+R] rows in the piece
-    int* psend;     // [E+R] send base of each piece (this rank)
-    int* nsend;     // [E]   send base of each native instance (this rank)
-    int* sendscan;  // [2E+R+1]
-    int* recvbase;  // [E][R] receive base per (local instance, source)
+    int* phost;     // [E+R+1] host rank of each piece
+    int* psend;     // [E+R+1] send base of each piece (this rank)
+    int* nsend;     // [E]     send base of each native instance (this rank)
+    int* recvbase;  // [R][E]  receive base per (source, local instance)
     int* scal;      // [SC_COUNT]
 };
 
@@ -141,317 +143,385 @@ __global__ __launch_bounds__(kScanThreads) void plan_scan(PlanDims d, int* __res
 }
 
 // -------------------------------------------------------------- plan_global
-// Routes of source rank `src` of expert e that precede the source's first
-// chunk (src == R gives the expert's total).
-__device__ __forceinline__ int pre_of(const PlanDims& d, const int* chunk, const int* s_cnt, int src,
+// Everything this single work-group touches more than once lives in LDS
+// (gfx950 gives a work-group up to 160 KiB); global memory is read in one
+// round trip at the start and written at the end.
+struct GlobalLds {
+    int *cnt, *eex, *kept, *js, *prem, *prem1, *cjs, *cje;
+    int *rb, *L, *uex, *dex, *cdl, *cdu, *coin, *fp, *np, *gid, *sbase, *roff;
+    int *pst, *phost, *pexp, *ppos, *pn;
+    int* scratch;
+};
+
+__host__ __device__ inline size_t global_lds_ints(int E, int R) {
+    return (size_t)8 * E + 1 + (size_t)12 * R + 9 + (size_t)5 * (E + R) + 1 +
+           2 * (kGlobalThreads / kWave + 1);
+}
+
+__device__ inline GlobalLds carve_global(int* p, int E, int R) {
+    GlobalLds g;
+    g.cnt = p; p += E;
+    g.eex = p; p += E + 1;
+    g.kept = p; p += E;
+    g.js = p; p += E;
+    g.prem = p; p += E;
+    g.prem1 = p; p += E;
+    g.cjs = p; p += E;
+    g.cje = p; p += E;
+    g.rb = p; p += R + 1;
+    g.L = p; p += R;
+    g.uex = p; p += R + 1;
+    g.dex = p; p += R + 1;
+    g.cdl = p; p += R;
+    g.cdu = p; p += R;
+    g.coin = p; p += R + 1;
+    g.fp = p; p += R + 1;
+    g.np = p; p += R;
+    g.gid = p; p += R + 1;
+    g.sbase = p; p += R + 1;
+    g.roff = p; p += R + 1;
+    g.pst = p; p += E + R + 1;
+    g.phost = p; p += E + R;
+    g.pexp = p; p += E + R;
+    g.ppos = p; p += E + R;
+    g.pn = p; p += E + R;
+    g.scratch = p;
+    return g;
+}
+
+// Local instance i of rank u: its expert, first position in (expert, f)
+// order and row count.
+__device__ __forceinline__ void inst_of(const GlobalLds& g, int E, int R, int u, int i, int* e,
+                                        int* P, int* n, int* pi) {
+    const int ef = efirst_of(u, R, E);
+    const int nat = efirst_of(u + 1, R, E) - ef;
+    if (i < nat) {
+        *e = ef + i;
+        *P = g.eex[*e];
+        *n = g.kept[*e];
+        *pi = -1;
+    } else {
+        *pi = g.fp[u] + i - nat;
+        *e = g.pexp[*pi];
+        *P = g.ppos[*pi];
+        *n = g.pn[*pi];
+    }
+}
+
+// Routes of expert e from source ranks below `src` (src == R: all of them).
+__device__ __forceinline__ int pre_of(const PlanDims& d, const int* chunk, const int* cnt, int src,
                                       int e) {
-    return src >= d.R ? s_cnt[e] : chunk[(src * d.cps) * d.E + e];
+    return src >= d.R ? cnt[e] : chunk[(src * d.cps) * d.E + e];
 }
 
 __global__ __launch_bounds__(kGlobalThreads) void plan_global(PlanDims d, PlanWs w, PlanOut o) {
     extern __shared__ int lds[];
-    const int E = d.E, R = d.R, C = d.C;
+    const int E = d.E, R = d.R, C = d.C, m = d.m;
     const int tid = threadIdx.x, NT = blockDim.x;
-    int* s_eex = lds;               // E+1
-    int* s_cnt = s_eex + E + 1;     // E
-    int* s_cjs = s_cnt + E;         // E  excess starts of spilling experts
-    int* s_cje = s_cjs + E;         // E  their experts
-    int* s_rb = s_cje + E;          // R+1
-    int* s_L = s_rb + R + 1;        // R
-    int* s_uex = s_L + R;           // R+1
-    int* s_dex = s_uex + R + 1;     // R+1
-    int* s_cdl = s_dex + R + 1;     // R  deficit starts of under-loaded ranks
-    int* s_cdu = s_cdl + R;         // R  their ranks
-    int* s_coin = s_cdu + R;        // R+1 prefix count of shared starts
-    int* s_fp = s_coin + R + 1;     // R+1 first piece of each under-loaded rank
-    int* s_np = s_fp + R + 1;       // R  pieces per rank
-    int* s_gid = s_np + R;          // R+1 instance gid base per rank
-    int* scratch = s_gid + R + 1;   // NT/64+1
+    const GlobalLds g = carve_global(lds, E, R);
+    int* scratch = g.scratch;
 
-    // 1. expert offsets in (expert, f) order
-    int c = tid < E ? w.cnt[tid] : 0;
-    int total;
-    int ex = block_exclusive_sum(c, scratch, &total);
+    // A. one round trip: expert totals and this rank's per-expert offsets
+    int c = 0, pm = 0, pm1 = 0;
     if (tid < E) {
-        s_cnt[tid] = c;
-        s_eex[tid] = ex;
+        c = w.cnt[tid];
+        pm = w.chunk[(m * d.cps) * E + tid];
+        pm1 = m + 1 < R ? w.chunk[((m + 1) * d.cps) * E + tid] : -1;
+    }
+    int total;
+    const int ex = block_exclusive_sum(c, scratch, &total);
+    if (tid < E) {
+        g.cnt[tid] = c;
+        g.eex[tid] = ex;
+        g.prem[tid] = pm;
+        g.prem1[tid] = pm1 < 0 ? c : pm1;
         w.eex[tid] = ex;
         o.expert_count[tid] = c;
     }
     if (tid == 0) {
-        s_eex[E] = total;
+        g.eex[E] = total;
         w.eex[E] = total;
     }
     __syncthreads();
 
-    // 2. rank blocks, native loads, surplus and deficit prefixes
+    // B. rank blocks, native loads, surplus and deficit prefixes
     for (int r = tid; r <= R; r += NT) {  // R may equal the block size
-        const int rb = s_eex[efirst_of(r, R, E)];
-        s_rb[r] = rb;
+        const int rb = g.eex[efirst_of(r, R, E)];
+        g.rb[r] = rb;
         w.rb[r] = rb;
     }
     __syncthreads();
-    int L = 0, U = 0, D = 0;
+    int U = 0, D = 0;
     if (tid < R) {
-        L = s_rb[tid + 1] - s_rb[tid];
-        U = max(L - C, 0);
-        D = max(C - L, 0);
-        s_L[tid] = L;
-        w.load[tid] = L;
-        o.rank_load[tid] = L;
+        const int Lr = g.rb[tid + 1] - g.rb[tid];
+        U = max(Lr - C, 0);
+        D = max(C - Lr, 0);
+        g.L[tid] = Lr;
+        w.load[tid] = Lr;
+        o.rank_load[tid] = Lr;
     }
-    int totU, totD;
-    const int uex = block_exclusive_sum(U, scratch, &totU);
-    const int dex = block_exclusive_sum(D, scratch, &totD);
+    int uex, dex, totU, totD;
+    block_exclusive_sum2(U, D, scratch, &uex, &dex, &totU, &totD);
     if (tid < R) {
-        s_uex[tid] = uex;
-        s_dex[tid] = dex;
+        g.uex[tid] = uex;
+        g.dex[tid] = dex;
         w.uex[tid] = uex;
         w.dex[tid] = dex;
     }
     if (tid == 0) {
-        s_uex[R] = totU;
-        s_dex[R] = totD;
+        g.uex[R] = totU;
+        g.dex[R] = totD;
         w.uex[R] = totU;
         w.dex[R] = totD;
     }
     __syncthreads();
 
-    // 3. per expert: rows kept at home and the start of its excess
-    int spill = 0, kept = 0, js = 0;
+    // C. rows of each expert kept at home, start of its excess; compacted
+    //    lists of spilling experts and under-loaded ranks
+    int spill = 0, under = 0, js = 0;
     if (tid < E) {
         const int h = home_of(tid, R, E);
-        const int rb = s_rb[h];
-        kept = clampi(rb + C - s_eex[tid], 0, s_cnt[tid]);
-        js = s_uex[h] + max(0, s_eex[tid] + kept - rb - C);
-        spill = kept < s_cnt[tid];
-        w.kept[tid] = kept;
-        w.js[tid] = js;
+        const long long rb = g.rb[h];
+        const int kept = (int)std::min<long long>(std::max<long long>(rb + C - g.eex[tid], 0), c);
+        js = g.uex[h] + (int)std::max<long long>(0, g.eex[tid] + kept - rb - C);
+        g.kept[tid] = kept;
+        g.js[tid] = js;
+        spill = kept < c;
     }
-    int NS;
-    const int si = block_exclusive_sum(spill, scratch, &NS);
+    if (tid < R) under = g.L[tid] < C;
+    int si, ui, NS, NU;
+    block_exclusive_sum2(spill, under, scratch, &si, &ui, &NS, &NU);
     if (spill) {
-        s_cjs[si] = js;
-        s_cje[si] = tid;
+        g.cjs[si] = js;
+        g.cje[si] = tid;
     }
-    const int under = tid < R && s_L[tid] < C;
-    int NU;
-    const int ui = block_exclusive_sum(under, scratch, &NU);
     if (under) {
-        s_cdl[ui] = s_dex[tid];
-        s_cdu[ui] = tid;
+        g.cdl[ui] = g.dex[tid];
+        g.cdu[ui] = tid;
     }
+    if (tid < R) g.np[tid] = 0;
     __syncthreads();
+
+    // D. deficit starts that coincide with an expert's excess start
     int coin = 0;
     if (tid < NU) {
-        const int s = s_cdl[tid];
-        const int lb = lower_bound(s_cjs, NS, s);
-        coin = lb < NS && s_cjs[lb] == s;
+        const int s = g.cdl[tid];
+        const int lb = lower_bound(g.cjs, NS, s);
+        coin = lb < NS && g.cjs[lb] == s;
     }
     int NC;
     const int ci = block_exclusive_sum(coin, scratch, &NC);
-    if (tid < NU) s_coin[tid] = ci;
-    if (tid == 0) s_coin[NU] = NC;
+    if (tid < NU) g.coin[tid] = ci;
+    if (tid == 0) g.coin[NU] = NC;
     __syncthreads();
     const int NP = NS + NU - NC;
 
-    // 4. pieces (redundant instances): the excess list [0, totU) cut at every
-    //    expert boundary and every under-loaded rank boundary, in order.
+    // E. pieces (redundant instances): the excess list [0, totU) cut at every
+    //    expert boundary and every under-loaded rank boundary, in order; a
+    //    piece's index is its start's rank in the merged list of starts.
     if (tid < NS) {
-        const int s = s_cjs[tid];
-        const int e = s_cje[tid];
-        const int lb = lower_bound(s_cdl, NU, s);
-        const int pi = tid + lb - s_coin[lb];
-        const int k = upper_bound(s_cdl, NU, s) - 1;
-        const int u = s_cdu[k];
-        const int kp = w.kept[e];
-        const int end = min(s + s_cnt[e] - kp, s_dex[u] + (C - s_L[u]));
-        w.pstart[pi] = s;
-        w.phost[pi] = u;
-        w.pexpert[pi] = e;
-        w.pn[pi] = end - s;
-        w.ppos[pi] = s_eex[e] + kp;
+        const int s = g.cjs[tid];
+        const int e = g.cje[tid];
+        const int lb = lower_bound(g.cdl, NU, s);
+        const int pi = tid + lb - g.coin[lb];
+        const int u = g.cdu[upper_bound(g.cdl, NU, s) - 1];
+        const int kp = g.kept[e];
+        const int end = min(s + g.cnt[e] - kp, g.dex[u] + (C - g.L[u]));
+        g.pst[pi] = s;
+        g.phost[pi] = u;
+        g.pexp[pi] = e;
+        g.pn[pi] = end - s;
+        g.ppos[pi] = g.eex[e] + kp;
     }
     if (tid < NU && !coin) {
-        const int s = s_cdl[tid];
-        const int u = s_cdu[tid];
-        const int lb = lower_bound(s_cjs, NS, s);
-        const int pi = tid + lb - s_coin[tid];
-        const int e = s_cje[lb - 1];
-        const int jse = w.js[e];
-        const int kp = w.kept[e];
-        const int end = min(jse + s_cnt[e] - kp, s + (C - s_L[u]));
-        w.pstart[pi] = s;
-        w.phost[pi] = u;
-        w.pexpert[pi] = e;
-        w.pn[pi] = end - s;
-        w.ppos[pi] = s_eex[e] + kp + (s - jse);
+        const int s = g.cdl[tid];
+        const int u = g.cdu[tid];
+        const int lb = lower_bound(g.cjs, NS, s);
+        const int pi = tid + lb - g.coin[tid];
+        const int e = g.cje[lb - 1];
+        const int jse = g.js[e];
+        const int kp = g.kept[e];
+        const int end = min(jse + g.cnt[e] - kp, s + (C - g.L[u]));
+        g.pst[pi] = s;
+        g.phost[pi] = u;
+        g.pexp[pi] = e;
+        g.pn[pi] = end - s;
+        g.ppos[pi] = g.eex[e] + kp + (s - jse);
     }
-    if (tid < NU) {
-        const int s = s_cdl[tid];
-        s_fp[s_cdu[tid]] = tid + lower_bound(s_cjs, NS, s) - s_coin[tid];
-    }
-    if (tid < R) s_np[tid] = 0;
-    if (tid == 0) w.pstart[NP] = totU;
+    if (tid < NU) g.fp[g.cdu[tid]] = tid + lower_bound(g.cjs, NS, g.cdl[tid]) - g.coin[tid];
+    if (tid == 0) g.pst[NP] = totU;
     __syncthreads();
     if (tid < NU) {
-        const int u = s_cdu[tid];
-        const int nxt = tid + 1 < NU ? s_fp[s_cdu[tid + 1]] : NP;
-        s_np[u] = nxt - s_fp[u];
+        const int u = g.cdu[tid];
+        const int nxt = tid + 1 < NU ? g.fp[g.cdu[tid + 1]] : NP;
+        g.np[u] = nxt - g.fp[u];
     }
     __syncthreads();
 
-    // 5. instance counts and gid bases
+    // F. instance counts and gid bases
     int ic = 0;
     if (tid < R) {
-        ic = efirst_of(tid + 1, R, E) - efirst_of(tid, R, E) + s_np[tid];
+        ic = efirst_of(tid + 1, R, E) - efirst_of(tid, R, E) + g.np[tid];
         o.inst_count[tid] = ic;
     }
     int NI;
     const int gb = block_exclusive_sum(ic, scratch, &NI);
     if (tid < R) {
-        s_gid[tid] = gb;
+        g.gid[tid] = gb;
         o.inst_gid_base[tid] = gb;
     }
     if (tid == 0) {
-        s_gid[R] = NI;
+        g.gid[R] = NI;
         o.inst_gid_base[R] = NI;
     }
     __syncthreads();
 
-    // 6. instance tables
+    // G. instance tables
     const int E1 = E + 1;
     for (int idx = tid; idx < R * E1; idx += NT) {
         const int u = idx / E1;
         const int i = idx - u * E1;
         const int ef = efirst_of(u, R, E);
         const int nat = efirst_of(u + 1, R, E) - ef;
-        const int n = nat + s_np[u];
-        int cu;
-        if (i < nat) {
-            cu = min(s_eex[ef + i] - s_rb[u], C);
-        } else if (i < n) {
-            cu = s_L[u] + w.pstart[s_fp[u] + i - nat] - s_dex[u];
-        } else {
-            cu = C;
-        }
+        const int n = nat + g.np[u];
+        int cu = C;
+        if (i < nat) cu = min(g.eex[ef + i] - g.rb[u], C);
+        else if (i < n) cu = g.L[u] + g.pst[g.fp[u] + i - nat] - g.dex[u];
         o.inst_cu[idx] = cu;
-        if (i < E) {
-            const int ie = i < nat ? ef + i : (i < n ? w.pexpert[s_fp[u] + i - nat] : -1);
-            o.inst_expert[u * E + i] = ie;
-        }
+        if (i < E) o.inst_expert[u * E + i] = i < nat ? ef + i : (i < n ? g.pexp[g.fp[u] + i - nat] : -1);
     }
 
-    // 7. send bases of this rank: instances in gid order = (dest, slot) order
-    const int m = d.m;
-    int carry = 0;
-    for (int base = 0; base < NI; base += NT) {
-        const int gid = base + tid;
-        int cm = 0, qP = 0, e = 0, pi = -1;
-        if (gid < NI) {
-            const int u = upper_bound(s_gid, R + 1, gid) - 1;
-            const int i = gid - s_gid[u];
-            const int ef = efirst_of(u, R, E);
-            const int nat = efirst_of(u + 1, R, E) - ef;
-            int P, n;
-            if (i < nat) {
-                e = ef + i;
-                P = s_eex[e];
-                n = w.kept[e];
-            } else {
-                pi = s_fp[u] + i - nat;
-                e = w.pexpert[pi];
-                P = w.ppos[pi];
-                n = w.pn[pi];
-            }
-            const int pre = pre_of(d, w.chunk, s_cnt, m, e);
-            const int Hm = pre_of(d, w.chunk, s_cnt, m + 1, e) - pre;
-            qP = clampi(P - s_eex[e] - pre, 0, Hm);
-            cm = clampi(P + n - s_eex[e] - pre, 0, Hm) - qP;
+    // H. send bases of this rank: instances in gid order = (dest, slot)
+    //    order; c_m(I) = this rank's routes inside instance I.
+    {
+        const int ipt = (NI + NT - 1) / NT;
+        const int g0 = min(tid * ipt, NI), g1 = min(g0 + ipt, NI);
+        int sum = 0;
+        for (int gi = g0; gi < g1; ++gi) {
+            const int u = upper_bound(g.gid, R + 1, gi) - 1;
+            int e, P, n, pi;
+            inst_of(g, E, R, u, gi - g.gid[u], &e, &P, &n, &pi);
+            const int Hm = g.prem1[e] - g.prem[e];
+            sum += clampi(P + n - g.eex[e] - g.prem[e], 0, Hm) - clampi(P - g.eex[e] - g.prem[e], 0, Hm);
         }
         int tot;
-        const int sx = block_exclusive_sum(cm, scratch, &tot) + carry;
-        if (gid < NI) {
-            w.sendscan[gid] = sx;
-            if (pi < 0) w.nsend[e] = sx - qP;
-            else w.psend[pi] = sx - qP;
+        int run = block_exclusive_sum(sum, scratch, &tot);
+        for (int gi = g0; gi < g1; ++gi) {
+            const int u = upper_bound(g.gid, R + 1, gi) - 1;
+            int e, P, n, pi;
+            inst_of(g, E, R, u, gi - g.gid[u], &e, &P, &n, &pi);
+            const int Hm = g.prem1[e] - g.prem[e];
+            const int q0 = clampi(P - g.eex[e] - g.prem[e], 0, Hm);
+            const int cm = clampi(P + n - g.eex[e] - g.prem[e], 0, Hm) - q0;
+            if (pi < 0) w.nsend[e] = run - q0;
+            else w.psend[pi] = run - q0;
+            if (gi == g.gid[u]) g.sbase[u] = run;
+            run += cm;
         }
-        carry += tot;
+        if (tid == 0) g.sbase[R] = tot;
     }
-    if (tid == 0) w.sendscan[NI] = carry;
-    __syncthreads();
-    for (int dd = tid; dd < R; dd += NT) o.send_count[dd] = w.sendscan[s_gid[dd + 1]] - w.sendscan[s_gid[dd]];
 
-    // 8. receive bases of this rank: per (local instance i, source), the
-    //    source's rows in earlier instances minus the instance's start rank
+    // I. receive bases of this rank: items (source, local instance i) in
+    //    arrival order; recvbase = sources' rows before the item minus the
+    //    item's start rank within its expert.
     const int ef_m = efirst_of(m, R, E);
     const int nat_m = efirst_of(m + 1, R, E) - ef_m;
-    const int nim = nat_m + s_np[m];
-    const int fp_m = s_fp[m];
-    int acc = 0;
-    const int src = tid;
-    if (src < R) {
-        for (int i = 0; i < nim; ++i) {
-            int e, P, n;
-            if (i < nat_m) {
-                e = ef_m + i;
-                P = s_eex[e];
-                n = w.kept[e];
-            } else {
-                const int pi = fp_m + i - nat_m;
-                e = w.pexpert[pi];
-                P = w.ppos[pi];
-                n = w.pn[pi];
-            }
-            const int pre = pre_of(d, w.chunk, s_cnt, src, e);
-            const int Hs = pre_of(d, w.chunk, s_cnt, src + 1, e) - pre;
-            const int q0 = clampi(P - s_eex[e] - pre, 0, Hs);
-            const int q1 = clampi(P + n - s_eex[e] - pre, 0, Hs);
-            w.recvbase[i * R + src] = acc - q0;
-            acc += q1 - q0;
+    const int nim = nat_m + g.np[m];
+    {
+        const int items = R * nim;
+        const int ipt = (items + NT - 1) / NT;
+        const int q0i = min(tid * ipt, items), q1i = min(q0i + ipt, items);
+        int sum = 0;
+        for (int q = q0i; q < q1i; ++q) {
+            const int src = q / nim, i = q - src * nim;
+            int e, P, n, pi;
+            inst_of(g, E, R, m, i, &e, &P, &n, &pi);
+            const int pre = pre_of(d, w.chunk, g.cnt, src, e);
+            const int Hs = pre_of(d, w.chunk, g.cnt, src + 1, e) - pre;
+            sum += clampi(P + n - g.eex[e] - pre, 0, Hs) - clampi(P - g.eex[e] - pre, 0, Hs);
         }
-        o.recv_count[src] = acc;
+        int tot;
+        int run = block_exclusive_sum(sum, scratch, &tot);
+        for (int q = q0i; q < q1i; ++q) {
+            const int src = q / nim, i = q - src * nim;
+            int e, P, n, pi;
+            inst_of(g, E, R, m, i, &e, &P, &n, &pi);
+            const int pre = pre_of(d, w.chunk, g.cnt, src, e);
+            const int Hs = pre_of(d, w.chunk, g.cnt, src + 1, e) - pre;
+            const int q0 = clampi(P - g.eex[e] - pre, 0, Hs);
+            const int cs = clampi(P + n - g.eex[e] - pre, 0, Hs) - q0;
+            w.recvbase[src * E + i] = run - q0;
+            if (i == 0) g.roff[src] = run;
+            run += cs;
+        }
+        if (tid == 0) g.roff[R] = tot;
     }
-    int totr;
-    const int roff = block_exclusive_sum(src < R ? acc : 0, scratch, &totr);
-    if (src < R) {
-        for (int i = 0; i < nim; ++i) w.recvbase[i * R + src] += roff;
+    __syncthreads();
+    for (int r = tid; r < R; r += NT) {
+        o.send_count[r] = g.sbase[r + 1] - g.sbase[r];
+        o.recv_count[r] = g.roff[r + 1] - g.roff[r];
+    }
+
+    // J. tables the per-route kernel stages
+    for (int i = tid; i <= NP; i += NT) {
+        w.pstart[i] = g.pst[i];
+        if (i < NP) w.phost[i] = g.phost[i];
     }
     if (tid == 0) {
         w.scal[SC_NP] = NP;
         w.scal[SC_EFIRST_M] = ef_m;
         w.scal[SC_NAT_M] = nat_m;
-        w.scal[SC_FP_M] = fp_m;
+        w.scal[SC_FP_M] = g.fp[m];
+        w.scal[SC_NIM] = nim;
     }
 }
 
 // -------------------------------------------------------------- plan_routes
+__host__ __device__ inline size_t routes_lds_ints(int E, int R, int T) {
+    return (size_t)(kRouteWaves + 3) * E + (size_t)4 * R + 1 + (size_t)3 * (E + R + 1) + E +
+           (T <= kStageIds ? T : 0);
+}
+
 __global__ __launch_bounds__(kRouteThreads) void plan_routes(PlanDims d, PlanWs w,
                                                              const int* __restrict__ ids,
                                                              PlanOut o) {
     extern __shared__ int lds[];
-    const int E = d.E, R = d.R, C = d.C;
+    const int E = d.E, R = d.R, C = d.C, m = d.m;
     const int tid = threadIdx.x;
-    int* s_cnt = lds;                      // [waves][E]
-    int* s_off = s_cnt + kRouteWaves * E;  // [E]
-    int* s_pre = s_off + E;                // [E]
-    int* s_eex = s_pre + E;                // [E]
-    int* s_rb = s_eex + E;                 // [R+1]
+    const int PM = E + R + 1;  // room for every piece start
+    int* s_cnt = lds;                      // [waves][E] per-wave running counts
+    int* s_base = s_cnt + kRouteWaves * E; // [E] position of the chunk's first route of e
+    int* s_q0 = s_base + E;                // [E] routes of e from this source before the chunk
+    int* s_nsend = s_q0 + E;               // [E]
+    int* s_rb = s_nsend + E;               // [R+1]
     int* s_uex = s_rb + R + 1;             // [R]
     int* s_L = s_uex + R;                  // [R]
     int* s_dex = s_L + R;                  // [R]
-    int* s_ps = s_dex + R;                 // [NP+1]
+    int* s_ps = s_dex + R;                 // [PM]
+    int* s_phost = s_ps + PM;              // [PM]
+    int* s_psend = s_phost + PM;           // [PM]
+    int* s_rcv = s_psend + PM;             // [E] receive bases of this source
+    int* s_ids = s_rcv + E;                // [T] when T <= kStageIds
 
     const int c = blockIdx.x;
     const int src = c / d.cps, sub = c - src * d.cps;
     const int f0 = src * C + sub * d.T;
     const int f1 = min(f0 + d.T, (src + 1) * C);
-    const int NP = w.scal[SC_NP];
+    const int len = f1 - f0;
+    const bool staged = d.T <= kStageIds;
 
+    // one round trip: every table this block reads, and its routes
+    const int NP = w.scal[SC_NP];
+    const int ef_m = w.scal[SC_EFIRST_M];
+    const int nat_m = w.scal[SC_NAT_M];
+    const int fp_m = w.scal[SC_FP_M];
     for (int e = tid; e < E; e += kRouteThreads) {
-        s_off[e] = w.chunk[c * E + e];
-        s_pre[e] = w.chunk[(src * d.cps) * E + e];
-        s_eex[e] = w.eex[e];
+        const int off = w.chunk[c * E + e];
+        const int pre = w.chunk[(src * d.cps) * E + e];
+        s_base[e] = w.eex[e] + off;
+        s_q0[e] = off - pre;
+        s_nsend[e] = w.nsend[e];
+        s_rcv[e] = w.recvbase[src * E + e];
     }
     for (int i = tid; i < kRouteWaves * E; i += kRouteThreads) s_cnt[i] = 0;
     for (int r = tid; r <= R; r += kRouteThreads) s_rb[r] = w.rb[r];
@@ -460,20 +530,25 @@ __global__ __launch_bounds__(kRouteThreads) void plan_routes(PlanDims d, PlanWs 
         s_L[r] = w.load[r];
         s_dex[r] = w.dex[r];
     }
-    for (int i = tid; i <= NP; i += kRouteThreads) s_ps[i] = w.pstart[i];
+    for (int i = tid; i < PM; i += kRouteThreads) {
+        s_ps[i] = w.pstart[i];
+        s_phost[i] = w.phost[i];
+        s_psend[i] = w.psend[i];
+    }
+    if (staged)
+        for (int j = tid; j < len; j += kRouteThreads) s_ids[j] = ids[f0 + j];
     __syncthreads();
 
     const int wave = tid / kWave;
     const int lane = tid & (kWave - 1);
-    const int len = f1 - f0;
     const int seg = (((len + kRouteWaves - 1) / kRouteWaves) + kWave - 1) & ~(kWave - 1);
-    const int a = min(f0 + wave * seg, f1);
-    const int b = min(a + seg, f1);
+    const int a = min(wave * seg, len);
+    const int b = min(a + seg, len);
     int* my_cnt = s_cnt + wave * E;
 
     // pass 1: per-wave expert counts
-    for (int f = a + lane; f < b; f += kWave) {
-        const int e = ids[f];
+    for (int j = a + lane; j < b; j += kWave) {
+        const int e = staged ? s_ids[j] : ids[f0 + j];
         if ((unsigned)e < (unsigned)E) atomicAdd(&my_cnt[e], 1);
     }
     __syncthreads();
@@ -488,28 +563,25 @@ __global__ __launch_bounds__(kRouteThreads) void plan_routes(PlanDims d, PlanWs 
     __syncthreads();
 
     // pass 2: stable rank within the chunk, then placement
-    const int m = d.m;
-    const int ef_m = w.scal[SC_EFIRST_M];
-    const int nat_m = w.scal[SC_NAT_M];
-    const int fp_m = w.scal[SC_FP_M];
     for (int base = a; base < b; base += kWave) {
-        const int f = base + lane;
-        bool valid = f < b;
-        int e = valid ? ids[f] : 0;
+        const int j = base + lane;
+        const int f = f0 + j;
+        bool valid = j < b;
+        int e = valid ? (staged ? s_ids[j] : ids[f]) : 0;
         valid = valid && (unsigned)e < (unsigned)E;
         if (!valid) e = 0;
         const uint64_t peers = match_peers(e, valid, d.nbits);
         const int rin = my_cnt[e] + count_below(peers);
         if (valid && is_group_leader(peers)) my_cnt[e] += __popcll(peers);
         if (!valid) {
-            if (f < b && o.route_dest) {
+            if (j < b && o.route_dest) {
                 o.route_dest[f] = -1;
                 o.route_slot[f] = -1;
             }
             continue;
         }
-        const int qs = s_off[e] - s_pre[e] + rin;  // rank among src's routes of e
-        const int p = s_eex[e] + s_off[e] + rin;   // position in (expert, f) order
+        const int qs = s_q0[e] + rin;    // rank among this source's routes of e
+        const int p = s_base[e] + rin;   // position in (expert, f) order
         const int h = home_of(e, R, E);
         const int q = p - s_rb[h];
         int dest, slot, pi = -1;
@@ -517,9 +589,9 @@ __global__ __launch_bounds__(kRouteThreads) void plan_routes(PlanDims d, PlanWs 
             dest = h;
             slot = q;
         } else {
-            const int j = s_uex[h] + q - C;
-            pi = upper_bound(s_ps, NP, j) - 1;
-            dest = pi >= 0 ? w.phost[pi] : -1;
+            const int jx = s_uex[h] + q - C;
+            pi = upper_bound(s_ps, NP, jx) - 1;
+            dest = pi >= 0 ? s_phost[pi] : -1;
             if ((unsigned)dest >= (unsigned)R) {  // only for inconsistent inputs
                 if (o.route_dest) {
                     o.route_dest[f] = -1;
@@ -527,16 +599,16 @@ __global__ __launch_bounds__(kRouteThreads) void plan_routes(PlanDims d, PlanWs 
                 }
                 continue;
             }
-            slot = s_L[dest] + j - s_dex[dest];
+            slot = s_L[dest] + jx - s_dex[dest];
         }
         if (o.route_dest) {
             o.route_dest[f] = dest;
             o.route_slot[f] = slot;
         }
-        if (src == m) o.send_pos[f - m * C] = (pi < 0 ? w.nsend[e] : w.psend[pi]) + qs;
+        if (src == m) o.send_pos[f - m * C] = (pi < 0 ? s_nsend[e] : s_psend[pi]) + qs;
         if (dest == m && (unsigned)slot < (unsigned)C) {
             const int i = pi < 0 ? e - ef_m : nat_m + pi - fp_m;
-            o.recv_pos[slot] = w.recvbase[i * R + src] + qs;
+            if ((unsigned)i < (unsigned)E) o.recv_pos[slot] = s_rcv[i] + qs;
         }
     }
 }
@@ -554,7 +626,7 @@ bool plan_dims(int R, int E, int S, int K, int m, PlanDims* d) {
     d->m = m;
     d->C = (int)C;
     d->N = (int)N;
-    long long T = 1024;
+    long long T = kMinChunk;
     while ((long long)R * ((C + T - 1) / T) > kMaxChunks) T *= 2;
     d->T = (int)std::min<long long>(T, C);
     d->cps = (int)((C + d->T - 1) / d->T);
@@ -566,8 +638,7 @@ bool plan_dims(int R, int E, int S, int K, int m, PlanDims* d) {
 }
 
 struct WsOffsets {
-    size_t chunk, cnt, eex, rb, load, uex, dex, kept, js, pstart, phost, pexpert, ppos, pn, psend,
-        nsend, sendscan, recvbase, scal, total;
+    size_t chunk, cnt, eex, rb, load, uex, dex, pstart, phost, psend, nsend, recvbase, scal, total;
 };
 
 WsOffsets ws_offsets(const PlanDims& d) {
@@ -586,31 +657,19 @@ WsOffsets ws_offsets(const PlanDims& d) {
     o.load = take(R);
     o.uex = take(R + 1);
     o.dex = take(R + 1);
-    o.kept = take(E);
-    o.js = take(E);
     o.pstart = take(E + R + 1);
-    o.phost = take(E + R);
-    o.pexpert = take(E + R);
-    o.ppos = take(E + R);
-    o.pn = take(E + R);
-    o.psend = take(E + R);
+    o.phost = take(E + R + 1);
+    o.psend = take(E + R + 1);
     o.nsend = take(E);
-    o.sendscan = take(2 * E + R + 1);
-    o.recvbase = take(E * R);
+    o.recvbase = take(R * E);
     o.scal = take(SC_COUNT);
     o.total = at;
     return o;
 }
 
-size_t global_lds_bytes(const PlanDims& d) {
-    const size_t ints = (size_t)4 * d.E + 1 + (size_t)10 * d.R + 6 + kGlobalThreads / kWave + 1;
-    return ints * sizeof(int);
-}
+size_t global_lds_bytes(const PlanDims& d) { return global_lds_ints(d.E, d.R) * sizeof(int); }
 
-size_t routes_lds_bytes(const PlanDims& d) {
-    const size_t ints = (size_t)(kRouteWaves + 3) * d.E + (size_t)4 * d.R + 1 + (size_t)d.E + d.R + 1;
-    return ints * sizeof(int);
-}
+size_t routes_lds_bytes(const PlanDims& d) { return routes_lds_ints(d.E, d.R, d.T) * sizeof(int); }
 
 bool lds_ready() {
     // Allow the two single-pass kernels to use more than 64 KiB of LDS when
@@ -667,16 +726,10 @@ extern "C" int mep_plan(int R, int E, int S, int K, int my_rank, const int32_t* 
     w.load = (int*)(ws + off.load);
     w.uex = (int*)(ws + off.uex);
     w.dex = (int*)(ws + off.dex);
-    w.kept = (int*)(ws + off.kept);
-    w.js = (int*)(ws + off.js);
     w.pstart = (int*)(ws + off.pstart);
     w.phost = (int*)(ws + off.phost);
-    w.pexpert = (int*)(ws + off.pexpert);
-    w.ppos = (int*)(ws + off.ppos);
-    w.pn = (int*)(ws + off.pn);
     w.psend = (int*)(ws + off.psend);
     w.nsend = (int*)(ws + off.nsend);
-    w.sendscan = (int*)(ws + off.sendscan);
     w.recvbase = (int*)(ws + off.recvbase);
     w.scal = (int*)(ws + off.scal);
     PlanOut o{expert_count, rank_load, route_dest, route_slot, inst_count, inst_expert,

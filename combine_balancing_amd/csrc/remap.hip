@@ -19,21 +19,25 @@
 namespace mep {
 namespace {
 
-constexpr int kRemapThreads = 512;
+constexpr int kRemapThreads = 1024;
 constexpr int kRemapWaves = kRemapThreads / kWave;
 constexpr int kMaxInst = 1024;
+constexpr int kMaxBS = 512;
+constexpr int kMaxK = 16;
+constexpr int kMaxEntries = kMaxBS * kMaxK;
+constexpr int kPerThread = kMaxEntries / kRemapThreads;
 
 struct RemapArgs {
     int BS, K, E, F, ws, ppr, rank, mode, scale_dtype;
-    const int* ids;
-    const int* table;
-    const void* scales;
-    const float* thr;
-    const uint8_t* active;
-    int* out_ids;
-    uint8_t* out_mask;
-    int* send_pos;
-    int* send_count;
+    const int* __restrict__ ids;
+    const int* __restrict__ table;
+    const void* __restrict__ scales;
+    const float* __restrict__ thr;
+    const uint8_t* __restrict__ active;
+    int* __restrict__ out_ids;
+    uint8_t* __restrict__ out_mask;
+    int* __restrict__ send_pos;
+    int* __restrict__ send_count;
 };
 
 __device__ __forceinline__ float load_scale(const void* p, int dtype, int i) {
@@ -43,53 +47,79 @@ __device__ __forceinline__ float load_scale(const void* p, int dtype, int i) {
     return (float)__builtin_bit_cast(_Float16, h);
 }
 
+// Entry i = t*K + k of the thread's r-th slot: i = tid + r * kRemapThreads.
 __global__ __launch_bounds__(kRemapThreads) void remap_prune_kernel(RemapArgs a) {
-    __shared__ int s_cnt[kRemapWaves * kMaxInst];
+    __shared__ float s_sc[kMaxEntries];               // scales widened to fp32
+    __shared__ int s_bal[kMaxEntries];                // remapped ids
+    __shared__ uint8_t s_keep[kMaxEntries];           // prune mask
+    __shared__ float s_sum[kMaxBS];                   // per-token threshold sums
+    __shared__ int s_cnt[kRemapWaves * kMaxInst];     // send-map counts
     __shared__ int s_tot[kMaxInst];
     __shared__ int scratch[kRemapThreads / kWave + 1];
     const int n = a.BS * a.K;
     const int tid = threadIdx.x;
     const int n_inst = a.ws * a.ppr;
+    const bool pruning = a.scales != nullptr;
 
-    // 1. remap and mask
-    for (int i = tid; i < n; i += kRemapThreads) {
+    // 1. ids, their table rows' counts and (for pruning) the scales: the
+    //    loads of all of a thread's entries are issued together.
+    int e[kPerThread], cnt[kPerThread];
+#pragma unroll
+    for (int r = 0; r < kPerThread; ++r) {
+        const int i = tid + r * kRemapThreads;
+        e[r] = i < n ? a.ids[i] : -1;
+        if (pruning && i < n) s_sc[i] = load_scale(a.scales, a.scale_dtype, i);
+    }
+#pragma unroll
+    for (int r = 0; r < kPerThread; ++r)
+        cnt[r] = (unsigned)e[r] < (unsigned)a.E ? a.table[(size_t)e[r] * a.F] : 1;
+    int bal[kPerThread];
+#pragma unroll
+    for (int r = 0; r < kPerThread; ++r) {
+        const int i = tid + r * kRemapThreads;
         const int t = i / a.K;
-        const int e = a.ids[i];
-        int out = -1;
-        if ((unsigned)e < (unsigned)a.E) {
-            const int* row = a.table + (size_t)e * a.F;
-            const int count = row[0];
-            int col = 1;
-            if (count > 1) {
-                if (a.mode == 0) {
-                    const int mode_value = (a.ws + count - 1) / count;
-                    col = a.rank / mode_value + 1;
-                } else {
-                    col = t % count + 1;
-                }
-            }
-            col = clampi(col, 1, a.F - 1);
-            out = row[col];
+        int col = 1;
+        if (cnt[r] > 1) {
+            if (a.mode == 0) col = a.rank / ((a.ws + cnt[r] - 1) / cnt[r]) + 1;
+            else col = t % cnt[r] + 1;
         }
-        a.out_ids[i] = out;
+        col = clampi(col, 1, a.F - 1);
+        bal[r] = (unsigned)e[r] < (unsigned)a.E ? a.table[(size_t)e[r] * a.F + col] : -1;
+    }
+    __syncthreads();
+
+    // 2. per-token sum of scale x threshold, in k order from +0 (fp32, no FMA)
+    if (pruning && tid < a.BS) {
+        float sum = 0.0f;
+        for (int k = 0; k < a.K; ++k) {
+            const float prod = s_sc[tid * a.K + k] * a.thr[k];
+            sum = sum + prod;
+        }
+        s_sum[tid] = sum;
+    }
+    __syncthreads();
+
+    // 3. masks; outputs
+#pragma unroll
+    for (int r = 0; r < kPerThread; ++r) {
+        const int i = tid + r * kRemapThreads;
+        if (i >= n) continue;
+        const int t = i / a.K;
         uint8_t keep = 1;
-        if (a.scales) {
-            float sum = 0.0f;
-            for (int k = 0; k < a.K; ++k) {
-                const float prod = load_scale(a.scales, a.scale_dtype, t * a.K + k) * a.thr[k];
-                sum = sum + prod;
-            }
-            const float s = load_scale(a.scales, a.scale_dtype, i);
+        if (pruning) {
             const bool act = a.active ? a.active[t] != 0 : true;
-            keep = (uint8_t)(act && !(s < sum));
+            keep = (uint8_t)(act && !(s_sc[i] < s_sum[t]));
         }
+        a.out_ids[i] = bal[r];
         a.out_mask[i] = keep;
+        s_bal[i] = bal[r];
+        s_keep[i] = keep;
     }
     if (!a.send_pos) return;
 
-    // 2. send map: stable counting sort of kept routes by instance
+    // 4. send map: stable counting sort of kept routes by instance
     for (int i = tid; i < kRemapWaves * n_inst; i += kRemapThreads) s_cnt[i] = 0;
-    __syncthreads();  // also publishes step 1's global writes to the block
+    __syncthreads();
     const int wave = tid / kWave;
     const int lane = tid & (kWave - 1);
     const int seg = (((n + kRemapWaves - 1) / kRemapWaves) + kWave - 1) & ~(kWave - 1);
@@ -97,35 +127,22 @@ __global__ __launch_bounds__(kRemapThreads) void remap_prune_kernel(RemapArgs a)
     const int hi = min(lo + seg, n);
     int* my_cnt = s_cnt + wave * n_inst;
     for (int i = lo + lane; i < hi; i += kWave) {
-        const int inst = a.out_ids[i];
-        if (a.out_mask[i] && (unsigned)inst < (unsigned)n_inst) atomicAdd(&my_cnt[inst], 1);
+        const int inst = s_bal[i];
+        if (s_keep[i] && (unsigned)inst < (unsigned)n_inst) atomicAdd(&my_cnt[inst], 1);
     }
     __syncthreads();
-    // Per-instance totals, then exclusive offsets in (instance, wave) order.
-    // n_inst <= kMaxInst = 2 * kRemapThreads: two instances per thread.
-    const int i0 = 2 * tid, i1 = 2 * tid + 1;
-    int t0 = 0, t1 = 0;
-    if (i0 < n_inst)
-        for (int v = 0; v < kRemapWaves; ++v) t0 += s_cnt[v * n_inst + i0];
-    if (i1 < n_inst)
-        for (int v = 0; v < kRemapWaves; ++v) t1 += s_cnt[v * n_inst + i1];
+    // per-instance totals, then exclusive offsets in (instance, wave) order
+    int tot = 0;
+    if (tid < n_inst)
+        for (int v = 0; v < kRemapWaves; ++v) tot += s_cnt[v * n_inst + tid];
     int all;
-    const int base = block_exclusive_sum(t0 + t1, scratch, &all);
-    if (i0 < n_inst) s_tot[i0] = t0;
-    if (i1 < n_inst) s_tot[i1] = t1;
-    if (i0 < n_inst) {
+    const int base = block_exclusive_sum(tot, scratch, &all);
+    if (tid < n_inst) {
+        s_tot[tid] = tot;
         int run = base;
         for (int v = 0; v < kRemapWaves; ++v) {
-            const int c = s_cnt[v * n_inst + i0];
-            s_cnt[v * n_inst + i0] = run;
-            run += c;
-        }
-    }
-    if (i1 < n_inst) {
-        int run = base + t0;
-        for (int v = 0; v < kRemapWaves; ++v) {
-            const int c = s_cnt[v * n_inst + i1];
-            s_cnt[v * n_inst + i1] = run;
+            const int c = s_cnt[v * n_inst + tid];
+            s_cnt[v * n_inst + tid] = run;
             run += c;
         }
     }
@@ -140,8 +157,8 @@ __global__ __launch_bounds__(kRemapThreads) void remap_prune_kernel(RemapArgs a)
     for (int b0 = lo; b0 < hi; b0 += kWave) {
         const int i = b0 + lane;
         bool valid = i < hi;
-        int inst = valid ? a.out_ids[i] : 0;
-        valid = valid && a.out_mask[i] && (unsigned)inst < (unsigned)n_inst;
+        int inst = valid ? s_bal[i] : 0;
+        valid = valid && s_keep[i] && (unsigned)inst < (unsigned)n_inst;
         if (!valid) inst = 0;
         const uint64_t peers = match_peers(inst, valid, nbits);
         const int r = my_cnt[inst] + count_below(peers);
@@ -170,7 +187,7 @@ extern "C" int mep_remap_prune(int BS, int K, int E, int F, int world_size, int 
     if (expert_scales && scale_dtype != MEP_SCALE_F32 && scale_dtype != MEP_SCALE_BF16 &&
         scale_dtype != MEP_SCALE_F16)
         return MEP_ERR_PARAM;
-    if (BS < 1 || BS > 65536 || K < 1 || K > 16 || E < 1 || E > 1024 || world_size < 1 ||
+    if (BS < 1 || BS > kMaxBS || K < 1 || K > kMaxK || E < 1 || E > 1024 || world_size < 1 ||
         world_size > 1024 || place_per_rank < 1 || F < 2 || F > world_size + 1 ||
         (long long)world_size * place_per_rank > kMaxInst)
         return MEP_ERR_SHAPE;

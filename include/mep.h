@@ -182,7 +182,7 @@ enum { MEP_SCALE_F32 = 0, MEP_SCALE_BF16 = 1, MEP_SCALE_F16 = 2 };
  * Outputs: balanced_ids [BS*K] int32, balanced_mask [BS*K] uint8,
  *   send_pos [BS*K] int32 and send_count [world_size] int32 (both NULL or
  *   both given).
- * Limits ([UpdExp] "约束说明"): 1 <= BS <= 65536, 1 <= K <= 16, K <= E,
+ * Limits ([UpdExp] "约束说明"): 1 <= BS <= 512, 1 <= K <= 16, K <= E,
  *   1 <= E <= 1024, 2 <= F <= world_size+1, 1 <= world_size <= 1024,
  *   world_size*place_per_rank <= 1024, balance_mode in {0,1};
  *   mode 0 needs 0 <= local_rank_id < world_size.

@@ -112,6 +112,7 @@ def test_remap_validation(B):
     assert _remap(B, F=1) == B.MEP_ERR_SHAPE
     assert _remap(B, ws=600, ppr=2) == B.MEP_ERR_SHAPE      # > 1024 instances
     assert _remap(B, BS=0) == B.MEP_ERR_SHAPE
+    assert _remap(B, BS=513) == B.MEP_ERR_SHAPE             # op doc limit BS <= 512
     assert _remap(B, E=1025) == B.MEP_ERR_SHAPE
 
 
