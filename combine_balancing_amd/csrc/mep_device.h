@@ -42,15 +42,21 @@ __device__ __forceinline__ bool is_group_leader(uint64_t peers) {
     return (peers & above) == 0;
 }
 
-// Inclusive sum over the wave (lanes 0..lane).
+// Inclusive sum over the wave (lanes 0..lane). Within each row of 16 lanes a
+// Kogge-Stone scan uses DPP row shifts (ALU-speed cross-lane moves; lanes
+// whose source falls outside the row read 0); the three row totals are then
+// read as scalars and added to the later rows. Call with the whole wave
+// active.
 __device__ __forceinline__ int wave_inclusive_sum(int x) {
-    const int lane = lane_id();
-#pragma unroll
-    for (int d = 1; d < kWave; d <<= 1) {
-        const int y = __shfl_up(x, d, kWave);
-        if (lane >= d) x += y;
-    }
-    return x;
+    x += __builtin_amdgcn_update_dpp(0, x, 0x111, 0xf, 0xf, false);  // row_shr:1
+    x += __builtin_amdgcn_update_dpp(0, x, 0x112, 0xf, 0xf, false);  // row_shr:2
+    x += __builtin_amdgcn_update_dpp(0, x, 0x114, 0xf, 0xf, false);  // row_shr:4
+    x += __builtin_amdgcn_update_dpp(0, x, 0x118, 0xf, 0xf, false);  // row_shr:8
+    const int row = lane_id() >> 4;
+    const int r0 = __builtin_amdgcn_readlane(x, 15);
+    const int r1 = __builtin_amdgcn_readlane(x, 31);
+    const int r2 = __builtin_amdgcn_readlane(x, 47);
+    return x + (row >= 1 ? r0 : 0) + (row >= 2 ? r1 : 0) + (row >= 3 ? r2 : 0);
 }
 
 // Exclusive block-wide sum. `scratch` holds at least blockDim/64 + 1 ints of

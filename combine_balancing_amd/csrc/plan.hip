@@ -40,15 +40,19 @@ namespace mep {
 namespace {
 
 #ifndef MEP_PLAN_ROUTE_THREADS
-#define MEP_PLAN_ROUTE_THREADS 256
+#define MEP_PLAN_ROUTE_THREADS 1024
+#endif
+#ifndef MEP_PLAN_MAX_CHUNKS
+#define MEP_PLAN_MAX_CHUNKS 1024
 #endif
 #ifndef MEP_PLAN_CHUNK
 #define MEP_PLAN_CHUNK 1024
 #endif
 constexpr int kHistThreads = 256;
 constexpr int kScanThreads = 1024;
-constexpr int kScanItems = 4;
-constexpr int kMaxChunks = kScanThreads * kScanItems;
+constexpr int kMaxChunks = MEP_PLAN_MAX_CHUNKS;  // column length of the expert scan
+constexpr int kScanItems = (kMaxChunks + kScanThreads - 1) / kScanThreads;
+constexpr int kBuckets = 1024;  // piece lookup: excess index >> shift -> first piece
 constexpr int kGlobalThreads = 1024;
 constexpr int kRouteThreads = MEP_PLAN_ROUTE_THREADS;  // work-group of plan_routes
 constexpr int kMinChunk = MEP_PLAN_CHUNK;              // routes per chunk (at least)
@@ -57,7 +61,7 @@ constexpr int kMaxR = 1024;
 constexpr int kMaxE = 1024;
 constexpr int kStageIds = 4096;  // chunk sizes up to this keep their ids in LDS
 
-enum { SC_NP = 0, SC_EFIRST_M = 1, SC_NAT_M = 2, SC_FP_M = 3, SC_NIM = 4, SC_COUNT = 16 };
+enum { SC_NP = 0, SC_EFIRST_M = 1, SC_NAT_M = 2, SC_FP_M = 3, SC_NIM = 4, SC_SHIFT = 5, SC_COUNT = 16 };
 
 struct PlanDims {
     int R, E, S, K, m;
@@ -78,8 +82,9 @@ struct PlanWs {
     int* uex;       // [R+1] exclusive prefix of surplus
     int* dex;       // [R+1] exclusive prefix of deficit
     int* pstart;    // [E+R+1] excess index where each piece starts (sorted)
-    int* phost;     // [E+R+1] host rank of each piece
-    int* psend;     // [E+R+1] send base of each piece (this rank)
+    int4* prec;     // [E+R+1] per piece: host rank, slot of excess index 0 on
+                    //         the host, send base (this rank), unused
+    int* bucket;    // [kBuckets] piece holding excess index b << shift
     int* nsend;     // [E]     send base of each native instance (this rank)
     int* recvbase;  // [R][E]  receive base per (source, local instance)
     int* scal;      // [SC_COUNT]
@@ -148,13 +153,13 @@ __global__ __launch_bounds__(kScanThreads) void plan_scan(PlanDims d, int* __res
 // round trip at the start and written at the end.
 struct GlobalLds {
     int *cnt, *eex, *kept, *js, *prem, *prem1, *cjs, *cje;
-    int *rb, *L, *uex, *dex, *cdl, *cdu, *coin, *fp, *np, *gid, *sbase, *roff;
+    int *rb, *ef, *L, *uex, *dex, *cdl, *cdu, *coin, *fp, *np, *gid, *sbase, *roff;
     int *pst, *phost, *pexp, *ppos, *pn;
     int* scratch;
 };
 
 __host__ __device__ inline size_t global_lds_ints(int E, int R) {
-    return (size_t)8 * E + 1 + (size_t)12 * R + 9 + (size_t)5 * (E + R) + 1 +
+    return (size_t)8 * E + 1 + (size_t)13 * R + 10 + (size_t)5 * (E + R) + 1 +
            2 * (kGlobalThreads / kWave + 1);
 }
 
@@ -169,6 +174,7 @@ __device__ inline GlobalLds carve_global(int* p, int E, int R) {
     g.cjs = p; p += E;
     g.cje = p; p += E;
     g.rb = p; p += R + 1;
+    g.ef = p; p += R + 1;
     g.L = p; p += R;
     g.uex = p; p += R + 1;
     g.dex = p; p += R + 1;
@@ -191,10 +197,10 @@ __device__ inline GlobalLds carve_global(int* p, int E, int R) {
 
 // Local instance i of rank u: its expert, first position in (expert, f)
 // order and row count.
-__device__ __forceinline__ void inst_of(const GlobalLds& g, int E, int R, int u, int i, int* e,
-                                        int* P, int* n, int* pi) {
-    const int ef = efirst_of(u, R, E);
-    const int nat = efirst_of(u + 1, R, E) - ef;
+__device__ __forceinline__ void inst_of(const GlobalLds& g, int u, int i, int* e, int* P, int* n,
+                                        int* pi) {
+    const int ef = g.ef[u];
+    const int nat = g.ef[u + 1] - ef;
     if (i < nat) {
         *e = ef + i;
         *P = g.eex[*e];
@@ -246,7 +252,9 @@ __global__ __launch_bounds__(kGlobalThreads) void plan_global(PlanDims d, PlanWs
 
     // B. rank blocks, native loads, surplus and deficit prefixes
     for (int r = tid; r <= R; r += NT) {  // R may equal the block size
-        const int rb = g.eex[efirst_of(r, R, E)];
+        const int ef = efirst_of(r, R, E);
+        const int rb = g.eex[ef];
+        g.ef[r] = ef;
         g.rb[r] = rb;
         w.rb[r] = rb;
     }
@@ -361,7 +369,7 @@ __global__ __launch_bounds__(kGlobalThreads) void plan_global(PlanDims d, PlanWs
     // F. instance counts and gid bases
     int ic = 0;
     if (tid < R) {
-        ic = efirst_of(tid + 1, R, E) - efirst_of(tid, R, E) + g.np[tid];
+        ic = g.ef[tid + 1] - g.ef[tid] + g.np[tid];
         o.inst_count[tid] = ic;
     }
     int NI;
@@ -376,19 +384,33 @@ __global__ __launch_bounds__(kGlobalThreads) void plan_global(PlanDims d, PlanWs
     }
     __syncthreads();
 
-    // G. instance tables
-    const int E1 = E + 1;
-    for (int idx = tid; idx < R * E1; idx += NT) {
-        const int u = idx / E1;
-        const int i = idx - u * E1;
-        const int ef = efirst_of(u, R, E);
-        const int nat = efirst_of(u + 1, R, E) - ef;
-        const int n = nat + g.np[u];
-        int cu = C;
-        if (i < nat) cu = min(g.eex[ef + i] - g.rb[u], C);
-        else if (i < n) cu = g.L[u] + g.pst[g.fp[u] + i - nat] - g.dex[u];
-        o.inst_cu[idx] = cu;
-        if (i < E) o.inst_expert[u * E + i] = i < nat ? ef + i : (i < n ? g.pexp[g.fp[u] + i - nat] : -1);
+    // G. instance tables (idx = u*(E+1) + i walked without divisions)
+    {
+        const int E1 = E + 1;
+        const int step_u = NT / E1, step_i = NT - (NT / E1) * E1;
+        int u = tid / E1, i = tid - (tid / E1) * E1;
+        for (int idx = tid; idx < R * E1; idx += NT) {
+            const int ef = g.ef[u];
+            const int nat = g.ef[u + 1] - ef;
+            const int n = nat + g.np[u];
+            int cu = C, ie = -1;
+            if (i < nat) {
+                cu = min(g.eex[ef + i] - g.rb[u], C);
+                ie = ef + i;
+            } else if (i < n) {
+                const int pi = g.fp[u] + i - nat;
+                cu = g.L[u] + g.pst[pi] - g.dex[u];
+                ie = g.pexp[pi];
+            }
+            o.inst_cu[idx] = cu;
+            if (i < E) o.inst_expert[u * E + i] = ie;
+            u += step_u;
+            i += step_i;
+            if (i >= E1) {
+                i -= E1;
+                ++u;
+            }
+        }
     }
 
     // H. send bases of this rank: instances in gid order = (dest, slot)
@@ -400,7 +422,7 @@ __global__ __launch_bounds__(kGlobalThreads) void plan_global(PlanDims d, PlanWs
         for (int gi = g0; gi < g1; ++gi) {
             const int u = upper_bound(g.gid, R + 1, gi) - 1;
             int e, P, n, pi;
-            inst_of(g, E, R, u, gi - g.gid[u], &e, &P, &n, &pi);
+            inst_of(g, u, gi - g.gid[u], &e, &P, &n, &pi);
             const int Hm = g.prem1[e] - g.prem[e];
             sum += clampi(P + n - g.eex[e] - g.prem[e], 0, Hm) - clampi(P - g.eex[e] - g.prem[e], 0, Hm);
         }
@@ -409,12 +431,16 @@ __global__ __launch_bounds__(kGlobalThreads) void plan_global(PlanDims d, PlanWs
         for (int gi = g0; gi < g1; ++gi) {
             const int u = upper_bound(g.gid, R + 1, gi) - 1;
             int e, P, n, pi;
-            inst_of(g, E, R, u, gi - g.gid[u], &e, &P, &n, &pi);
+            inst_of(g, u, gi - g.gid[u], &e, &P, &n, &pi);
             const int Hm = g.prem1[e] - g.prem[e];
             const int q0 = clampi(P - g.eex[e] - g.prem[e], 0, Hm);
             const int cm = clampi(P + n - g.eex[e] - g.prem[e], 0, Hm) - q0;
-            if (pi < 0) w.nsend[e] = run - q0;
-            else w.psend[pi] = run - q0;
+            if (pi < 0) {
+                w.nsend[e] = run - q0;
+            } else {
+                const int host = g.phost[pi];
+                w.prec[pi] = make_int4(host, g.L[host] - g.dex[host], run - q0, 0);
+            }
             if (gi == g.gid[u]) g.sbase[u] = run;
             run += cm;
         }
@@ -424,8 +450,8 @@ __global__ __launch_bounds__(kGlobalThreads) void plan_global(PlanDims d, PlanWs
     // I. receive bases of this rank: items (source, local instance i) in
     //    arrival order; recvbase = sources' rows before the item minus the
     //    item's start rank within its expert.
-    const int ef_m = efirst_of(m, R, E);
-    const int nat_m = efirst_of(m + 1, R, E) - ef_m;
+    const int ef_m = g.ef[m];
+    const int nat_m = g.ef[m + 1] - ef_m;
     const int nim = nat_m + g.np[m];
     {
         const int items = R * nim;
@@ -435,7 +461,7 @@ __global__ __launch_bounds__(kGlobalThreads) void plan_global(PlanDims d, PlanWs
         for (int q = q0i; q < q1i; ++q) {
             const int src = q / nim, i = q - src * nim;
             int e, P, n, pi;
-            inst_of(g, E, R, m, i, &e, &P, &n, &pi);
+            inst_of(g, m, i, &e, &P, &n, &pi);
             const int pre = pre_of(d, w.chunk, g.cnt, src, e);
             const int Hs = pre_of(d, w.chunk, g.cnt, src + 1, e) - pre;
             sum += clampi(P + n - g.eex[e] - pre, 0, Hs) - clampi(P - g.eex[e] - pre, 0, Hs);
@@ -445,7 +471,7 @@ __global__ __launch_bounds__(kGlobalThreads) void plan_global(PlanDims d, PlanWs
         for (int q = q0i; q < q1i; ++q) {
             const int src = q / nim, i = q - src * nim;
             int e, P, n, pi;
-            inst_of(g, E, R, m, i, &e, &P, &n, &pi);
+            inst_of(g, m, i, &e, &P, &n, &pi);
             const int pre = pre_of(d, w.chunk, g.cnt, src, e);
             const int Hs = pre_of(d, w.chunk, g.cnt, src + 1, e) - pre;
             const int q0 = clampi(P - g.eex[e] - pre, 0, Hs);
@@ -462,10 +488,15 @@ __global__ __launch_bounds__(kGlobalThreads) void plan_global(PlanDims d, PlanWs
         o.recv_count[r] = g.roff[r + 1] - g.roff[r];
     }
 
-    // J. tables the per-route kernel stages
-    for (int i = tid; i <= NP; i += NT) {
-        w.pstart[i] = g.pst[i];
-        if (i < NP) w.phost[i] = g.phost[i];
+    // J. tables the per-route kernel stages: piece starts, and a bucket table
+    //    so that a route finds its piece with one lookup and a short walk
+
+    int shift = 0;
+    while (((long long)kBuckets << shift) < totU) ++shift;
+    for (int i = tid; i <= NP; i += NT) w.pstart[i] = g.pst[i];
+    for (int b = tid; b < kBuckets; b += NT) {
+        const long long start = (long long)b << shift;
+        w.bucket[b] = start < totU ? upper_bound(g.pst, NP, (int)start) - 1 : max(NP - 1, 0);
     }
     if (tid == 0) {
         w.scal[SC_NP] = NP;
@@ -473,35 +504,35 @@ __global__ __launch_bounds__(kGlobalThreads) void plan_global(PlanDims d, PlanWs
         w.scal[SC_NAT_M] = nat_m;
         w.scal[SC_FP_M] = g.fp[m];
         w.scal[SC_NIM] = nim;
+        w.scal[SC_SHIFT] = shift;
     }
 }
 
 // -------------------------------------------------------------- plan_routes
+// LDS per work-group: per-wave counters, two packed per-expert tables, the
+// receive bases of this source, piece starts and records, the bucket table
+// and (for chunks up to kStageIds routes) the chunk's ids.
 __host__ __device__ inline size_t routes_lds_ints(int E, int R, int T) {
-    return (size_t)(kRouteWaves + 3) * E + (size_t)4 * R + 1 + (size_t)3 * (E + R + 1) + E +
+    const size_t PM = (size_t)E + R + 1;
+    return (size_t)kRouteWaves * E + (size_t)4 * E + (size_t)2 * E + E + PM + 4 * PM + kBuckets +
            (T <= kStageIds ? T : 0);
 }
 
 __global__ __launch_bounds__(kRouteThreads) void plan_routes(PlanDims d, PlanWs w,
                                                              const int* __restrict__ ids,
                                                              PlanOut o) {
-    extern __shared__ int lds[];
+    extern __shared__ int4 lds4[];  // 16-byte aligned base
     const int E = d.E, R = d.R, C = d.C, m = d.m;
     const int tid = threadIdx.x;
     const int PM = E + R + 1;  // room for every piece start
-    int* s_cnt = lds;                      // [waves][E] per-wave running counts
-    int* s_base = s_cnt + kRouteWaves * E; // [E] position of the chunk's first route of e
-    int* s_q0 = s_base + E;                // [E] routes of e from this source before the chunk
-    int* s_nsend = s_q0 + E;               // [E]
-    int* s_rb = s_nsend + E;               // [R+1]
-    int* s_uex = s_rb + R + 1;             // [R]
-    int* s_L = s_uex + R;                  // [R]
-    int* s_dex = s_L + R;                  // [R]
-    int* s_ps = s_dex + R;                 // [PM]
-    int* s_phost = s_ps + PM;              // [PM]
-    int* s_psend = s_phost + PM;           // [PM]
-    int* s_rcv = s_psend + PM;             // [E] receive bases of this source
-    int* s_ids = s_rcv + E;                // [T] when T <= kStageIds
+    int4* s_ex0 = lds4;                                   // [E] {qbase, q0, nsend, home}
+    int4* s_prec = s_ex0 + E;                             // [PM] piece records
+    int2* s_ex1 = (int2*)(s_prec + PM);                   // [E] {jbase, native recv base}
+    int* s_cnt = (int*)(s_ex1 + E);                       // [waves][E]
+    int* s_rcv = s_cnt + kRouteWaves * E;                 // [E] recv base of local instance
+    int* s_ps = s_rcv + E;                                // [PM] piece starts
+    int* s_bkt = s_ps + PM;                               // [kBuckets]
+    int* s_ids = s_bkt + kBuckets;                        // [T] when T <= kStageIds
 
     const int c = blockIdx.x;
     const int src = c / d.cps, sub = c - src * d.cps;
@@ -510,31 +541,33 @@ __global__ __launch_bounds__(kRouteThreads) void plan_routes(PlanDims d, PlanWs 
     const int len = f1 - f0;
     const bool staged = d.T <= kStageIds;
 
-    // one round trip: every table this block reads, and its routes
+    // one round trip: every table this block reads, and its routes.
+    // For a route of expert e at rank rin among the chunk's routes of e:
+    //   q  = qbase[e] + rin   slot on the home rank if q < C
+    //   qs = q0[e] + rin      rank among this source's routes of e
+    //   j  = jbase[e] + rin   index in the global excess list otherwise
     const int NP = w.scal[SC_NP];
     const int ef_m = w.scal[SC_EFIRST_M];
     const int nat_m = w.scal[SC_NAT_M];
     const int fp_m = w.scal[SC_FP_M];
+    const int shift = w.scal[SC_SHIFT];
     for (int e = tid; e < E; e += kRouteThreads) {
+        const int h = home_of(e, R, E);
         const int off = w.chunk[c * E + e];
         const int pre = w.chunk[(src * d.cps) * E + e];
-        s_base[e] = w.eex[e] + off;
-        s_q0[e] = off - pre;
-        s_nsend[e] = w.nsend[e];
-        s_rcv[e] = w.recvbase[src * E + e];
+        const int qbase = w.eex[e] + off - w.rb[h];
+        const int rcv = w.recvbase[src * E + e];
+        const int nrcv = h == m ? w.recvbase[src * E + (e - ef_m)] : 0;
+        s_ex0[e] = make_int4(qbase, off - pre, w.nsend[e], h);
+        s_ex1[e] = make_int2(w.uex[h] + qbase - C, nrcv);
+        s_rcv[e] = rcv;
     }
     for (int i = tid; i < kRouteWaves * E; i += kRouteThreads) s_cnt[i] = 0;
-    for (int r = tid; r <= R; r += kRouteThreads) s_rb[r] = w.rb[r];
-    for (int r = tid; r < R; r += kRouteThreads) {
-        s_uex[r] = w.uex[r];
-        s_L[r] = w.load[r];
-        s_dex[r] = w.dex[r];
-    }
     for (int i = tid; i < PM; i += kRouteThreads) {
         s_ps[i] = w.pstart[i];
-        s_phost[i] = w.phost[i];
-        s_psend[i] = w.psend[i];
+        s_prec[i] = w.prec[i];
     }
+    for (int b = tid; b < kBuckets; b += kRouteThreads) s_bkt[b] = w.bucket[b];
     if (staged)
         for (int j = tid; j < len; j += kRouteThreads) s_ids[j] = ids[f0 + j];
     __syncthreads();
@@ -554,6 +587,7 @@ __global__ __launch_bounds__(kRouteThreads) void plan_routes(PlanDims d, PlanWs 
     __syncthreads();
     for (int e = tid; e < E; e += kRouteThreads) {
         int run = 0;
+#pragma unroll 4
         for (int v = 0; v < kRouteWaves; ++v) {
             const int t = s_cnt[v * E + e];
             s_cnt[v * E + e] = run;
@@ -573,42 +607,36 @@ __global__ __launch_bounds__(kRouteThreads) void plan_routes(PlanDims d, PlanWs 
         const uint64_t peers = match_peers(e, valid, d.nbits);
         const int rin = my_cnt[e] + count_below(peers);
         if (valid && is_group_leader(peers)) my_cnt[e] += __popcll(peers);
-        if (!valid) {
-            if (j < b && o.route_dest) {
-                o.route_dest[f] = -1;
-                o.route_slot[f] = -1;
-            }
-            continue;
-        }
-        const int qs = s_q0[e] + rin;    // rank among this source's routes of e
-        const int p = s_base[e] + rin;   // position in (expert, f) order
-        const int h = home_of(e, R, E);
-        const int q = p - s_rb[h];
-        int dest, slot, pi = -1;
-        if (q < C) {
-            dest = h;
-            slot = q;
-        } else {
-            const int jx = s_uex[h] + q - C;
-            pi = upper_bound(s_ps, NP, jx) - 1;
-            dest = pi >= 0 ? s_phost[pi] : -1;
-            if ((unsigned)dest >= (unsigned)R) {  // only for inconsistent inputs
-                if (o.route_dest) {
-                    o.route_dest[f] = -1;
-                    o.route_slot[f] = -1;
+        const int4 x0 = s_ex0[e];
+        const int2 x1 = s_ex1[e];
+        int dest = -1, slot = -1;
+        if (valid) {
+            const int q = x0.x + rin;
+            const int qs = x0.y + rin;
+            if (q < C) {
+                dest = x0.w;
+                slot = q;
+                if (src == m) o.send_pos[f - m * C] = x0.z + qs;
+                if (dest == m && (unsigned)slot < (unsigned)C) o.recv_pos[slot] = x1.y + qs;
+            } else {
+                const int jx = x1.x + rin;
+                const int bi = jx >> shift;
+                int pi = s_bkt[bi < 0 ? 0 : min(bi, kBuckets - 1)];
+                while (pi + 1 < NP && s_ps[pi + 1] <= jx) ++pi;
+                const int4 pr = s_prec[pi];
+                if ((unsigned)pr.x < (unsigned)R && pi < NP) {
+                    dest = pr.x;
+                    slot = pr.y + jx;
+                    if (src == m) o.send_pos[f - m * C] = pr.z + qs;
+                    const int i = nat_m + pi - fp_m;
+                    if (dest == m && (unsigned)slot < (unsigned)C && (unsigned)i < (unsigned)E)
+                        o.recv_pos[slot] = s_rcv[i] + qs;
                 }
-                continue;
             }
-            slot = s_L[dest] + jx - s_dex[dest];
         }
-        if (o.route_dest) {
+        if (j < b && o.route_dest) {
             o.route_dest[f] = dest;
             o.route_slot[f] = slot;
-        }
-        if (src == m) o.send_pos[f - m * C] = (pi < 0 ? s_nsend[e] : s_psend[pi]) + qs;
-        if (dest == m && (unsigned)slot < (unsigned)C) {
-            const int i = pi < 0 ? e - ef_m : nat_m + pi - fp_m;
-            if ((unsigned)i < (unsigned)E) o.recv_pos[slot] = s_rcv[i] + qs;
         }
     }
 }
@@ -638,7 +666,7 @@ bool plan_dims(int R, int E, int S, int K, int m, PlanDims* d) {
 }
 
 struct WsOffsets {
-    size_t chunk, cnt, eex, rb, load, uex, dex, pstart, phost, psend, nsend, recvbase, scal, total;
+    size_t chunk, cnt, eex, rb, load, uex, dex, pstart, prec, bucket, nsend, recvbase, scal, total;
 };
 
 WsOffsets ws_offsets(const PlanDims& d) {
@@ -658,8 +686,8 @@ WsOffsets ws_offsets(const PlanDims& d) {
     o.uex = take(R + 1);
     o.dex = take(R + 1);
     o.pstart = take(E + R + 1);
-    o.phost = take(E + R + 1);
-    o.psend = take(E + R + 1);
+    o.prec = take(4 * (E + R + 1));
+    o.bucket = take(kBuckets);
     o.nsend = take(E);
     o.recvbase = take(R * E);
     o.scal = take(SC_COUNT);
@@ -727,8 +755,8 @@ extern "C" int mep_plan(int R, int E, int S, int K, int my_rank, const int32_t* 
     w.uex = (int*)(ws + off.uex);
     w.dex = (int*)(ws + off.dex);
     w.pstart = (int*)(ws + off.pstart);
-    w.phost = (int*)(ws + off.phost);
-    w.psend = (int*)(ws + off.psend);
+    w.prec = (int4*)(ws + off.prec);
+    w.bucket = (int*)(ws + off.bucket);
     w.nsend = (int*)(ws + off.nsend);
     w.recvbase = (int*)(ws + off.recvbase);
     w.scal = (int*)(ws + off.scal);
