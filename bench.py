@@ -88,6 +88,10 @@ def main():
     ap.add_argument("--steps", type=int, default=50)
     ap.add_argument("--warmup", type=int, default=5)
     ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--copy-calibration", action="store_true",
+                    help="after the timed steps, run plain device-to-device copies of "
+                         "the group kernel's output size (a known-size reference for "
+                         "HBM byte counters)")
     args = ap.parse_args()
     if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) != 1:
         print("bench.py runs on exactly one GPU: the hot path is one rank's share "
@@ -208,6 +212,12 @@ def main():
                      "frac": round(group_gbs / HBM_PEAK_GBS, 4),
                      "traffic": _traffic("group_rows")},
     }
+    if args.copy_calibration:
+        nbytes = C * H * 2
+        for _ in range(3):
+            grouped.copy_(recv_raw)
+        torch.cuda.synchronize()
+        res["copy_calibration_bytes"] = nbytes
     if not args.no_cpu_baseline:
         import oracle
         plan_ref = oracle.plan(d["topk_ids"], R, E, S, K, 0)
