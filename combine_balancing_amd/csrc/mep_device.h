@@ -23,16 +23,27 @@ __device__ __forceinline__ int count_below(uint64_t mask) {
 
 // Lanes (among `valid` ones) whose key equals this lane's key, found with one
 // ballot per key bit: a wave-wide multi-split, so equal keys are ranked by
-// lane order without atomics (deterministic). Must be called by the whole
-// wave with a wave-uniform `nbits`.
-__device__ __forceinline__ uint64_t match_peers(int key, bool valid, int nbits) {
-    uint64_t peers = __ballot(valid);
-    for (int b = 0; b < nbits; ++b) {
-        const bool bit = (key >> b) & 1;
-        const uint64_t m = __ballot(valid && bit);
-        peers &= bit ? m : ~m;
+// lane order without atomics (deterministic). Keys must lie in
+// [0, 2^NBITS); the loop is fully unrolled (bits above a key's width are 0
+// on every lane and leave the groups unchanged). Call with the whole wave.
+constexpr int kKeyBits = 10;  // keys below 1024: experts and instances
+
+template <int NBITS = kKeyBits>
+__device__ __forceinline__ uint64_t match_peers(int key, bool valid) {
+    // Invalid lanes are dropped by the first ballot; the per-bit ballots need
+    // not exclude them again.
+    // Per bit: lb = 0 or ~0 (the lane's bit, sign-extended), m = ballot of
+    // the bit; lanes agreeing with this lane on the bit are ~(m ^ lb).
+    const uint64_t v = __ballot(valid);
+    uint32_t lo = (uint32_t)v, hi = (uint32_t)(v >> 32);
+#pragma unroll
+    for (int b = 0; b < NBITS; ++b) {
+        const int lb = (int)((uint32_t)key << (31 - b)) >> 31;
+        const uint64_t m = __ballot(lb != 0);
+        lo &= ~((uint32_t)m ^ (uint32_t)lb);
+        hi &= ~((uint32_t)(m >> 32) ^ (uint32_t)lb);
     }
-    return peers;
+    return ((uint64_t)hi << 32) | lo;
 }
 
 // True on the highest lane of its peer group.
@@ -40,6 +51,16 @@ __device__ __forceinline__ bool is_group_leader(uint64_t peers) {
     const int lane = lane_id();
     const uint64_t above = lane == 63 ? 0ull : (~0ull << (lane + 1));
     return (peers & above) == 0;
+}
+
+// Work-group barrier for LDS data: waits for this wave's LDS (and scalar)
+// operations, then meets the other waves. Unlike __syncthreads() it does not
+// wait for outstanding global stores, so a phase that writes outputs does
+// not stall the next one; use it only where no thread reads global memory
+// that another thread of the work-group wrote in the same launch. The memory
+// clobber keeps the compiler from moving memory accesses across it.
+__device__ __forceinline__ void lds_barrier() {
+    asm volatile("s_waitcnt lgkmcnt(0)\n\ts_barrier" ::: "memory");
 }
 
 // Inclusive sum over the wave (lanes 0..lane). Within each row of 16 lanes a
@@ -60,7 +81,7 @@ __device__ __forceinline__ int wave_inclusive_sum(int x) {
 }
 
 // Exclusive block-wide sum. `scratch` holds at least blockDim/64 + 1 ints of
-// LDS. Every thread of the block must call it. Returns the exclusive prefix;
+// LDS. Every thread of the block must call it (it uses lds_barrier). Returns the exclusive prefix;
 // *total receives the block sum.
 __device__ __forceinline__ int block_exclusive_sum(int v, int* scratch, int* total) {
     const int lane = threadIdx.x & (kWave - 1);
@@ -68,17 +89,17 @@ __device__ __forceinline__ int block_exclusive_sum(int v, int* scratch, int* tot
     const int nw = (blockDim.x + kWave - 1) / kWave;
     const int inc = wave_inclusive_sum(v);
     if (lane == kWave - 1 || (int)threadIdx.x == (int)blockDim.x - 1) scratch[wave] = inc;
-    __syncthreads();
+    lds_barrier();
     if (wave == 0) {
         const int w = lane < nw ? scratch[lane] : 0;
         const int s = wave_inclusive_sum(w);
         if (lane < nw) scratch[lane] = s - w;
         if (lane == nw - 1) scratch[nw] = s;
     }
-    __syncthreads();
+    lds_barrier();
     const int res = inc - v + scratch[wave];
     *total = scratch[nw];
-    __syncthreads();
+    lds_barrier();
     return res;
 }
 
@@ -97,7 +118,7 @@ __device__ __forceinline__ void block_exclusive_sum2(int a, int b, int* scratch,
         sa[wave] = ia;
         sb[wave] = ib;
     }
-    __syncthreads();
+    lds_barrier();
     if (wave == 0) {
         const int wa = lane < nw ? sa[lane] : 0;
         const int wb = lane < nw ? sb[lane] : 0;
@@ -112,12 +133,12 @@ __device__ __forceinline__ void block_exclusive_sum2(int a, int b, int* scratch,
             sb[nw] = xb;
         }
     }
-    __syncthreads();
+    lds_barrier();
     *ea = ia - a + sa[wave];
     *eb = ib - b + sb[wave];
     *ta = sa[nw];
     *tb = sb[nw];
-    __syncthreads();
+    lds_barrier();
 }
 
 // Smallest index i in [0, n) with a[i] >= x (n if none).
@@ -138,6 +159,26 @@ __device__ __forceinline__ int upper_bound(const int* a, int n, int x) {
         if (a[mid] <= x) lo = mid + 1; else hi = mid;
     }
     return lo;
+}
+
+// dst[i] = src[i] for i in [0, n), the block's threads striding by NT. The
+// loads of up to U strides are issued together before any store, so the
+// copy costs one memory round trip per U strides instead of one per stride.
+template <int NT, int U, typename T>
+__device__ __forceinline__ void stage(T* __restrict__ dst, const T* __restrict__ src, int n) {
+    for (int base = 0; base < n; base += NT * U) {
+        T v[U];
+#pragma unroll
+        for (int u = 0; u < U; ++u) {
+            const int i = base + u * NT + (int)threadIdx.x;
+            if (i < n) v[u] = src[i];
+        }
+#pragma unroll
+        for (int u = 0; u < U; ++u) {
+            const int i = base + u * NT + (int)threadIdx.x;
+            if (i < n) dst[i] = v[u];
+        }
+    }
 }
 
 __device__ __forceinline__ int clampi(int v, int lo, int hi) {

@@ -52,7 +52,8 @@ constexpr int kHistThreads = 256;
 constexpr int kScanThreads = 1024;
 constexpr int kMaxChunks = MEP_PLAN_MAX_CHUNKS;  // column length of the expert scan
 constexpr int kScanItems = (kMaxChunks + kScanThreads - 1) / kScanThreads;
-constexpr int kBuckets = 1024;  // piece lookup: excess index >> shift -> first piece
+constexpr int kBuckets = 1024;
+constexpr size_t kMaxLds = 160 * 1024;  // LDS a gfx950 work-group may allocate  // piece lookup: excess index >> shift -> first piece
 constexpr int kGlobalThreads = 1024;
 constexpr int kRouteThreads = MEP_PLAN_ROUTE_THREADS;  // work-group of plan_routes
 constexpr int kMinChunk = MEP_PLAN_CHUNK;              // routes per chunk (at least)
@@ -70,7 +71,6 @@ struct PlanDims {
     int T;        // routes per chunk
     int cps;      // chunks per source rank
     int nchunks;  // R*cps
-    int nbits;    // bits needed for E-1
 };
 
 struct PlanWs {
@@ -83,10 +83,11 @@ struct PlanWs {
     int* dex;       // [R+1] exclusive prefix of deficit
     int* pstart;    // [E+R+1] excess index where each piece starts (sorted)
     int4* prec;     // [E+R+1] per piece: host rank, slot of excess index 0 on
-                    //         the host, send base (this rank), unused
+                    //         the host, send base (this rank), expert
     int* bucket;    // [kBuckets] piece holding excess index b << shift
     int* nsend;     // [E]     send base of each native instance (this rank)
     int* recvbase;  // [R][E]  receive base per (source, local instance)
+    int4* rinfo;    // [R]     per rank: first native expert, natives, pieces, first piece
     int* scal;      // [SC_COUNT]
 };
 
@@ -113,12 +114,20 @@ __global__ __launch_bounds__(kHistThreads) void plan_hist(PlanDims d, const int*
     const int f0 = src * d.C + sub * d.T;
     const int f1 = min(f0 + d.T, (src + 1) * d.C);
     for (int e = threadIdx.x; e < d.E; e += blockDim.x) s_hist[e] = 0;
-    __syncthreads();
-    for (int f = f0 + threadIdx.x; f < f1; f += blockDim.x) {
-        const int e = ids[f];
-        if ((unsigned)e < (unsigned)d.E) atomicAdd(&s_hist[e], 1);
+    lds_barrier();
+    constexpr int U = 8;  // ids in flight per thread
+    for (int base = f0; base < f1; base += kHistThreads * U) {
+        int e[U];
+#pragma unroll
+        for (int u = 0; u < U; ++u) {
+            const int f = base + u * kHistThreads + (int)threadIdx.x;
+            e[u] = f < f1 ? ids[f] : -1;
+        }
+#pragma unroll
+        for (int u = 0; u < U; ++u)
+            if ((unsigned)e[u] < (unsigned)d.E) atomicAdd(&s_hist[e[u]], 1);
     }
-    __syncthreads();
+    lds_barrier();
     for (int e = threadIdx.x; e < d.E; e += blockDim.x) chunk[c * d.E + e] = s_hist[e];
 }
 
@@ -220,6 +229,7 @@ __device__ __forceinline__ int pre_of(const PlanDims& d, const int* chunk, const
     return src >= d.R ? cnt[e] : chunk[(src * d.cps) * d.E + e];
 }
 
+// One element per thread in the per-expert and per-rank phases (E, R <= NT).
 __global__ __launch_bounds__(kGlobalThreads) void plan_global(PlanDims d, PlanWs w, PlanOut o) {
     extern __shared__ int lds[];
     const int E = d.E, R = d.R, C = d.C, m = d.m;
@@ -248,7 +258,7 @@ __global__ __launch_bounds__(kGlobalThreads) void plan_global(PlanDims d, PlanWs
         g.eex[E] = total;
         w.eex[E] = total;
     }
-    __syncthreads();
+    lds_barrier();
 
     // B. rank blocks, native loads, surplus and deficit prefixes
     for (int r = tid; r <= R; r += NT) {  // R may equal the block size
@@ -258,7 +268,7 @@ __global__ __launch_bounds__(kGlobalThreads) void plan_global(PlanDims d, PlanWs
         g.rb[r] = rb;
         w.rb[r] = rb;
     }
-    __syncthreads();
+    lds_barrier();
     int U = 0, D = 0;
     if (tid < R) {
         const int Lr = g.rb[tid + 1] - g.rb[tid];
@@ -282,7 +292,7 @@ __global__ __launch_bounds__(kGlobalThreads) void plan_global(PlanDims d, PlanWs
         w.uex[R] = totU;
         w.dex[R] = totD;
     }
-    __syncthreads();
+    lds_barrier();
 
     // C. rows of each expert kept at home, start of its excess; compacted
     //    lists of spilling experts and under-loaded ranks
@@ -308,7 +318,7 @@ __global__ __launch_bounds__(kGlobalThreads) void plan_global(PlanDims d, PlanWs
         g.cdu[ui] = tid;
     }
     if (tid < R) g.np[tid] = 0;
-    __syncthreads();
+    lds_barrier();
 
     // D. deficit starts that coincide with an expert's excess start
     int coin = 0;
@@ -321,7 +331,7 @@ __global__ __launch_bounds__(kGlobalThreads) void plan_global(PlanDims d, PlanWs
     const int ci = block_exclusive_sum(coin, scratch, &NC);
     if (tid < NU) g.coin[tid] = ci;
     if (tid == 0) g.coin[NU] = NC;
-    __syncthreads();
+    lds_barrier();
     const int NP = NS + NU - NC;
 
     // E. pieces (redundant instances): the excess list [0, totU) cut at every
@@ -358,13 +368,13 @@ __global__ __launch_bounds__(kGlobalThreads) void plan_global(PlanDims d, PlanWs
     }
     if (tid < NU) g.fp[g.cdu[tid]] = tid + lower_bound(g.cjs, NS, g.cdl[tid]) - g.coin[tid];
     if (tid == 0) g.pst[NP] = totU;
-    __syncthreads();
+    lds_barrier();
     if (tid < NU) {
         const int u = g.cdu[tid];
         const int nxt = tid + 1 < NU ? g.fp[g.cdu[tid + 1]] : NP;
         g.np[u] = nxt - g.fp[u];
     }
-    __syncthreads();
+    lds_barrier();
 
     // F. instance counts and gid bases
     int ic = 0;
@@ -382,36 +392,11 @@ __global__ __launch_bounds__(kGlobalThreads) void plan_global(PlanDims d, PlanWs
         g.gid[R] = NI;
         o.inst_gid_base[R] = NI;
     }
-    __syncthreads();
+    lds_barrier();
 
-    // G. instance tables (idx = u*(E+1) + i walked without divisions)
-    {
-        const int E1 = E + 1;
-        const int step_u = NT / E1, step_i = NT - (NT / E1) * E1;
-        int u = tid / E1, i = tid - (tid / E1) * E1;
-        for (int idx = tid; idx < R * E1; idx += NT) {
-            const int ef = g.ef[u];
-            const int nat = g.ef[u + 1] - ef;
-            const int n = nat + g.np[u];
-            int cu = C, ie = -1;
-            if (i < nat) {
-                cu = min(g.eex[ef + i] - g.rb[u], C);
-                ie = ef + i;
-            } else if (i < n) {
-                const int pi = g.fp[u] + i - nat;
-                cu = g.L[u] + g.pst[pi] - g.dex[u];
-                ie = g.pexp[pi];
-            }
-            o.inst_cu[idx] = cu;
-            if (i < E) o.inst_expert[u * E + i] = ie;
-            u += step_u;
-            i += step_i;
-            if (i >= E1) {
-                i -= E1;
-                ++u;
-            }
-        }
-    }
+    // G. per-rank instance layout for the table fill done by plan_routes
+    for (int u = tid; u < R; u += NT)
+        w.rinfo[u] = make_int4(g.ef[u], g.ef[u + 1] - g.ef[u], g.np[u], g.fp[u]);
 
     // H. send bases of this rank: instances in gid order = (dest, slot)
     //    order; c_m(I) = this rank's routes inside instance I.
@@ -439,7 +424,7 @@ __global__ __launch_bounds__(kGlobalThreads) void plan_global(PlanDims d, PlanWs
                 w.nsend[e] = run - q0;
             } else {
                 const int host = g.phost[pi];
-                w.prec[pi] = make_int4(host, g.L[host] - g.dex[host], run - q0, 0);
+                w.prec[pi] = make_int4(host, g.L[host] - g.dex[host], run - q0, g.pexp[pi]);
             }
             if (gi == g.gid[u]) g.sbase[u] = run;
             run += cm;
@@ -482,7 +467,7 @@ __global__ __launch_bounds__(kGlobalThreads) void plan_global(PlanDims d, PlanWs
         }
         if (tid == 0) g.roff[R] = tot;
     }
-    __syncthreads();
+    lds_barrier();
     for (int r = tid; r < R; r += NT) {
         o.send_count[r] = g.sbase[r + 1] - g.sbase[r];
         o.recv_count[r] = g.roff[r + 1] - g.roff[r];
@@ -514,7 +499,7 @@ __global__ __launch_bounds__(kGlobalThreads) void plan_global(PlanDims d, PlanWs
 // and (for chunks up to kStageIds routes) the chunk's ids.
 __host__ __device__ inline size_t routes_lds_ints(int E, int R, int T) {
     const size_t PM = (size_t)E + R + 1;
-    return (size_t)kRouteWaves * E + (size_t)4 * E + (size_t)2 * E + E + PM + 4 * PM + kBuckets +
+    return (size_t)kRouteWaves * E + (size_t)4 * E + (size_t)4 * E + PM + 4 * PM + kBuckets +
            (T <= kStageIds ? T : 0);
 }
 
@@ -527,10 +512,9 @@ __global__ __launch_bounds__(kRouteThreads) void plan_routes(PlanDims d, PlanWs 
     const int PM = E + R + 1;  // room for every piece start
     int4* s_ex0 = lds4;                                   // [E] {qbase, q0, nsend, home}
     int4* s_prec = s_ex0 + E;                             // [PM] piece records
-    int2* s_ex1 = (int2*)(s_prec + PM);                   // [E] {jbase, native recv base}
+    int4* s_ex1 = s_prec + PM;  // [E] {jbase, native recv base, native cu, recv base of local instance e}
     int* s_cnt = (int*)(s_ex1 + E);                       // [waves][E]
-    int* s_rcv = s_cnt + kRouteWaves * E;                 // [E] recv base of local instance
-    int* s_ps = s_rcv + E;                                // [PM] piece starts
+    int* s_ps = s_cnt + kRouteWaves * E;                  // [PM] piece starts
     int* s_bkt = s_ps + PM;                               // [kBuckets]
     int* s_ids = s_bkt + kBuckets;                        // [T] when T <= kStageIds
 
@@ -555,22 +539,51 @@ __global__ __launch_bounds__(kRouteThreads) void plan_routes(PlanDims d, PlanWs 
         const int h = home_of(e, R, E);
         const int off = w.chunk[c * E + e];
         const int pre = w.chunk[(src * d.cps) * E + e];
-        const int qbase = w.eex[e] + off - w.rb[h];
+        const int eex = w.eex[e], rbh = w.rb[h];
+        const int qbase = eex + off - rbh;
         const int rcv = w.recvbase[src * E + e];
         const int nrcv = h == m ? w.recvbase[src * E + (e - ef_m)] : 0;
         s_ex0[e] = make_int4(qbase, off - pre, w.nsend[e], h);
-        s_ex1[e] = make_int2(w.uex[h] + qbase - C, nrcv);
-        s_rcv[e] = rcv;
+        s_ex1[e] = make_int4(w.uex[h] + qbase - C, nrcv, min(eex - rbh, C), rcv);
     }
     for (int i = tid; i < kRouteWaves * E; i += kRouteThreads) s_cnt[i] = 0;
-    for (int i = tid; i < PM; i += kRouteThreads) {
-        s_ps[i] = w.pstart[i];
-        s_prec[i] = w.prec[i];
+    stage<kRouteThreads, 2>(s_ps, w.pstart, PM);
+    stage<kRouteThreads, 2>(s_prec, w.prec, PM);
+    stage<kRouteThreads, 1>(s_bkt, w.bucket, kBuckets);
+    if (staged) stage<kRouteThreads, kStageIds / kRouteThreads>(s_ids, ids + f0, len);
+    lds_barrier();
+
+    // this block's slice of the instance tables inst_cu [R][E+1] and
+    // inst_expert [R][E]: idx = u*(E+1) + i, walked without divisions
+    {
+        const int E1 = E + 1;
+        const int total = R * E1;
+        const int per = (total + gridDim.x - 1) / gridDim.x;
+        const int lo = min(blockIdx.x * per, total), hi = min(lo + per, total);
+        const int step_u = kRouteThreads / E1, step_i = kRouteThreads - step_u * E1;
+        int u = (lo + tid) / E1, i = (lo + tid) - u * E1;
+        for (int idx = lo + tid; idx < hi; idx += kRouteThreads) {
+            const int4 ri = w.rinfo[u];  // {first native, natives, pieces, first piece}
+            int cu = C, ie = -1;
+            if (i < ri.y) {
+                ie = ri.x + i;
+                cu = s_ex1[ie].z;
+            } else if (i < ri.y + ri.z) {
+                const int pi = ri.w + i - ri.y;
+                const int4 pr = s_prec[pi];
+                cu = pr.y + s_ps[pi];
+                ie = pr.w;
+            }
+            o.inst_cu[idx] = cu;
+            if (i < E) o.inst_expert[u * E + i] = ie;
+            u += step_u;
+            i += step_i;
+            if (i >= E1) {
+                i -= E1;
+                ++u;
+            }
+        }
     }
-    for (int b = tid; b < kBuckets; b += kRouteThreads) s_bkt[b] = w.bucket[b];
-    if (staged)
-        for (int j = tid; j < len; j += kRouteThreads) s_ids[j] = ids[f0 + j];
-    __syncthreads();
 
     const int wave = tid / kWave;
     const int lane = tid & (kWave - 1);
@@ -584,7 +597,7 @@ __global__ __launch_bounds__(kRouteThreads) void plan_routes(PlanDims d, PlanWs 
         const int e = staged ? s_ids[j] : ids[f0 + j];
         if ((unsigned)e < (unsigned)E) atomicAdd(&my_cnt[e], 1);
     }
-    __syncthreads();
+    lds_barrier();
     for (int e = tid; e < E; e += kRouteThreads) {
         int run = 0;
 #pragma unroll 4
@@ -594,7 +607,7 @@ __global__ __launch_bounds__(kRouteThreads) void plan_routes(PlanDims d, PlanWs 
             run += t;
         }
     }
-    __syncthreads();
+    lds_barrier();
 
     // pass 2: stable rank within the chunk, then placement
     for (int base = a; base < b; base += kWave) {
@@ -604,11 +617,11 @@ __global__ __launch_bounds__(kRouteThreads) void plan_routes(PlanDims d, PlanWs 
         int e = valid ? (staged ? s_ids[j] : ids[f]) : 0;
         valid = valid && (unsigned)e < (unsigned)E;
         if (!valid) e = 0;
-        const uint64_t peers = match_peers(e, valid, d.nbits);
+        const uint64_t peers = match_peers(e, valid);
         const int rin = my_cnt[e] + count_below(peers);
         if (valid && is_group_leader(peers)) my_cnt[e] += __popcll(peers);
         const int4 x0 = s_ex0[e];
-        const int2 x1 = s_ex1[e];
+        const int4 x1 = s_ex1[e];
         int dest = -1, slot = -1;
         if (valid) {
             const int q = x0.x + rin;
@@ -630,7 +643,7 @@ __global__ __launch_bounds__(kRouteThreads) void plan_routes(PlanDims d, PlanWs 
                     if (src == m) o.send_pos[f - m * C] = pr.z + qs;
                     const int i = nat_m + pi - fp_m;
                     if (dest == m && (unsigned)slot < (unsigned)C && (unsigned)i < (unsigned)E)
-                        o.recv_pos[slot] = s_rcv[i] + qs;
+                        o.recv_pos[slot] = s_ex1[i].w + qs;
                 }
             }
         }
@@ -659,14 +672,11 @@ bool plan_dims(int R, int E, int S, int K, int m, PlanDims* d) {
     d->T = (int)std::min<long long>(T, C);
     d->cps = (int)((C + d->T - 1) / d->T);
     d->nchunks = R * d->cps;
-    int nb = 0;
-    while ((1 << nb) < E) ++nb;
-    d->nbits = nb;
     return true;
 }
 
 struct WsOffsets {
-    size_t chunk, cnt, eex, rb, load, uex, dex, pstart, prec, bucket, nsend, recvbase, scal, total;
+    size_t chunk, cnt, eex, rb, load, uex, dex, pstart, prec, bucket, nsend, recvbase, rinfo, scal, total;
 };
 
 WsOffsets ws_offsets(const PlanDims& d) {
@@ -690,6 +700,7 @@ WsOffsets ws_offsets(const PlanDims& d) {
     o.bucket = take(kBuckets);
     o.nsend = take(E);
     o.recvbase = take(R * E);
+    o.rinfo = take(4 * R);
     o.scal = take(SC_COUNT);
     o.total = at;
     return o;
@@ -703,7 +714,7 @@ bool lds_ready() {
     // Allow the two single-pass kernels to use more than 64 KiB of LDS when
     // the sizes call for it (gfx950 has 160 KiB per CU).
     static const bool ok = [] {
-        const int lim = 160 * 1024;
+        const int lim = (int)kMaxLds;
         bool good = hipFuncSetAttribute((const void*)plan_global,
                                         hipFuncAttributeMaxDynamicSharedMemorySize,
                                         lim) == hipSuccess;
@@ -743,6 +754,7 @@ extern "C" int mep_plan(int R, int E, int S, int K, int my_rank, const int32_t* 
     const WsOffsets off = ws_offsets(d);
     if (workspace_bytes < off.total || ((uintptr_t)workspace & 255u) != 0) return MEP_ERR_PARAM;
     const size_t glds = global_lds_bytes(d), rlds = routes_lds_bytes(d);
+    if (glds > kMaxLds || rlds > kMaxLds) return MEP_ERR_SHAPE;  // not reachable within the limits
     if ((glds > 64 * 1024 || rlds > 64 * 1024) && !lds_ready()) return MEP_ERR_HIP;
 
     char* ws = (char*)workspace;
@@ -759,6 +771,7 @@ extern "C" int mep_plan(int R, int E, int S, int K, int my_rank, const int32_t* 
     w.bucket = (int*)(ws + off.bucket);
     w.nsend = (int*)(ws + off.nsend);
     w.recvbase = (int*)(ws + off.recvbase);
+    w.rinfo = (int4*)(ws + off.rinfo);
     w.scal = (int*)(ws + off.scal);
     PlanOut o{expert_count, rank_load, route_dest, route_slot, inst_count, inst_expert,
               inst_cu, inst_gid_base, send_pos, send_count, recv_pos, recv_count};

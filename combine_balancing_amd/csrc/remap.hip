@@ -22,10 +22,13 @@ namespace {
 constexpr int kRemapThreads = 1024;
 constexpr int kRemapWaves = kRemapThreads / kWave;
 constexpr int kMaxInst = 1024;
+constexpr int kMaxE = 1024;
 constexpr int kMaxBS = 512;
 constexpr int kMaxK = 16;
 constexpr int kMaxEntries = kMaxBS * kMaxK;
 constexpr int kPerThread = kMaxEntries / kRemapThreads;
+constexpr int kCountWaves = kRemapWaves;  // waves that build the send map
+constexpr int kStageTable = kCountWaves * kMaxInst;  // eplb_table entries kept in LDS
 
 struct RemapArgs {
     int BS, K, E, F, ws, ppr, rank, mode, scale_dtype;
@@ -40,127 +43,170 @@ struct RemapArgs {
     int* __restrict__ send_count;
 };
 
-__device__ __forceinline__ float load_scale(const void* p, int dtype, int i) {
-    if (dtype == MEP_SCALE_F32) return ((const float*)p)[i];
-    const uint16_t h = ((const uint16_t*)p)[i];
-    if (dtype == MEP_SCALE_BF16) return __uint_as_float((uint32_t)h << 16);
-    return (float)__builtin_bit_cast(_Float16, h);
+// A scale's bit pattern widened exactly to fp32.
+__device__ __forceinline__ float scale_value(uint32_t raw, int dtype) {
+    if (dtype == MEP_SCALE_F32) return __uint_as_float(raw);
+    if (dtype == MEP_SCALE_BF16) return __uint_as_float(raw << 16);
+    return (float)__builtin_bit_cast(_Float16, (uint16_t)raw);
 }
 
-// Entry i = t*K + k of the thread's r-th slot: i = tid + r * kRemapThreads.
+// Entry i = t*K + k of the thread's r-th slot: i = tid + r * kRemapThreads
+// (coalesced loads and stores). Token and column indices use exact
+// multiply-shift reciprocals instead of integer divisions: t = (i*kmag) >> 21
+// for i < 8192 and K <= 16, and t / count = (t*m) >> 20 for t < 512 and
+// count <= 1024, with kmag = ceil(2^21/K) and m = ceil(2^20/count).
 __global__ __launch_bounds__(kRemapThreads) void remap_prune_kernel(RemapArgs a) {
-    __shared__ float s_sc[kMaxEntries];               // scales widened to fp32
+    // s_tab is dead once the ids are remapped; the send-map counters reuse
+    // its space.
+    __shared__ int s_region[kCountWaves * kMaxInst];
+    int* s_tab = s_region;                            // [kStageTable] eplb_table, when it fits
+    int* s_cnt = s_region;                            // [kCountWaves][n_inst] send-map counts
     __shared__ int s_bal[kMaxEntries];                // remapped ids
     __shared__ uint8_t s_keep[kMaxEntries];           // prune mask
+    __shared__ float s_sc[kMaxK * (kMaxBS + 1)];      // scales as fp32, [k][t] skewed by one
     __shared__ float s_sum[kMaxBS];                   // per-token threshold sums
-    __shared__ int s_cnt[kRemapWaves * kMaxInst];     // send-map counts
+    __shared__ uint8_t s_act[kMaxBS];
+    __shared__ float s_thr[kMaxK];
+    __shared__ int s_col[kMaxE];                      // mode 0: column; mode 1: reciprocal of count
     __shared__ int s_tot[kMaxInst];
     __shared__ int scratch[kRemapThreads / kWave + 1];
     const int n = a.BS * a.K;
     const int tid = threadIdx.x;
     const int n_inst = a.ws * a.ppr;
     const bool pruning = a.scales != nullptr;
+    const int tab_n = a.E * a.F;
+    const bool tab_staged = tab_n <= kStageTable;
+    const unsigned kmag = ((1u << 21) + a.K - 1) / a.K;
+    const int S1 = a.BS + 1;
 
-    // 1. ids, their table rows' counts and (for pruning) the scales: the
-    //    loads of all of a thread's entries are issued together.
-    int e[kPerThread], cnt[kPerThread];
+    // 1. one round trip: ids, scales, thresholds, the active mask and (when
+    //    it fits) the whole table
+    int e[kPerThread];
+    uint32_t raw[kPerThread];  // scale bit patterns; converted after every load is issued
 #pragma unroll
     for (int r = 0; r < kPerThread; ++r) {
         const int i = tid + r * kRemapThreads;
         e[r] = i < n ? a.ids[i] : -1;
-        if (pruning && i < n) s_sc[i] = load_scale(a.scales, a.scale_dtype, i);
     }
+    if (pruning) {
+        if (a.scale_dtype == MEP_SCALE_F32) {
 #pragma unroll
-    for (int r = 0; r < kPerThread; ++r)
-        cnt[r] = (unsigned)e[r] < (unsigned)a.E ? a.table[(size_t)e[r] * a.F] : 1;
-    int bal[kPerThread];
+            for (int r = 0; r < kPerThread; ++r) {
+                const int i = tid + r * kRemapThreads;
+                raw[r] = i < n ? ((const uint32_t*)a.scales)[i] : 0u;
+            }
+        } else {
 #pragma unroll
-    for (int r = 0; r < kPerThread; ++r) {
-        const int i = tid + r * kRemapThreads;
-        const int t = i / a.K;
-        int col = 1;
-        if (cnt[r] > 1) {
-            if (a.mode == 0) col = a.rank / ((a.ws + cnt[r] - 1) / cnt[r]) + 1;
-            else col = t % cnt[r] + 1;
+            for (int r = 0; r < kPerThread; ++r) {
+                const int i = tid + r * kRemapThreads;
+                raw[r] = i < n ? ((const uint16_t*)a.scales)[i] : 0u;
+            }
         }
-        col = clampi(col, 1, a.F - 1);
-        bal[r] = (unsigned)e[r] < (unsigned)a.E ? a.table[(size_t)e[r] * a.F + col] : -1;
     }
-    __syncthreads();
+    if (tab_staged) stage<kRemapThreads, kStageTable / kRemapThreads>(s_tab, a.table, tab_n);
+    if (pruning && tid < a.K) s_thr[tid] = a.thr[tid];
+    if (tid < a.BS) s_act[tid] = (pruning && a.active) ? (a.active[tid] != 0) : 1;
+    if (pruning) {
+#pragma unroll
+        for (int r = 0; r < kPerThread; ++r) {
+            const int i = tid + r * kRemapThreads;
+            const int t = (int)(((unsigned)i * kmag) >> 21);
+            if (i < n) s_sc[(i - t * a.K) * S1 + t] = scale_value(raw[r], a.scale_dtype);
+        }
+    }
+    lds_barrier();
+    const int* tab = tab_staged ? s_tab : a.table;
 
-    // 2. per-token sum of scale x threshold, in k order from +0 (fp32, no FMA)
+    // 2. per expert: the mode-0 column (it depends on the rank and the
+    //    expert's count only) or the count's reciprocal for mode 1; per
+    //    token: sum of scale x threshold in k order from +0 (fp32, no FMA)
+    if (tid < a.E) {
+        const int count = tab[(size_t)tid * a.F];
+        if (a.mode == 0) s_col[tid] = count > 1 ? a.rank / ((a.ws + count - 1) / count) + 1 : 1;
+        else s_col[tid] = count > 1 ? (int)(((1u << 20) + count - 1) / count) : 0;
+    }
     if (pruning && tid < a.BS) {
         float sum = 0.0f;
         for (int k = 0; k < a.K; ++k) {
-            const float prod = s_sc[tid * a.K + k] * a.thr[k];
+            const float prod = s_sc[k * S1 + tid] * s_thr[k];
             sum = sum + prod;
         }
         s_sum[tid] = sum;
     }
-    __syncthreads();
+    lds_barrier();
 
-    // 3. masks; outputs
+    // 3. remap and mask every entry; outputs
 #pragma unroll
     for (int r = 0; r < kPerThread; ++r) {
         const int i = tid + r * kRemapThreads;
         if (i >= n) continue;
-        const int t = i / a.K;
-        uint8_t keep = 1;
-        if (pruning) {
-            const bool act = a.active ? a.active[t] != 0 : true;
-            keep = (uint8_t)(act && !(s_sc[i] < s_sum[t]));
+        const int t = (int)(((unsigned)i * kmag) >> 21);
+        int bal = -1;
+        if ((unsigned)e[r] < (unsigned)a.E) {
+            const int* row = tab + (size_t)e[r] * a.F;
+            int col;
+            if (a.mode == 0) {
+                col = s_col[e[r]];
+            } else {
+                const int count = row[0];
+                col = count > 1 ? t - count * (int)(((unsigned)t * (unsigned)s_col[e[r]]) >> 20) + 1
+                                : 1;
+            }
+            bal = row[clampi(col, 1, a.F - 1)];
         }
-        a.out_ids[i] = bal[r];
+        const uint8_t keep =
+            pruning ? (uint8_t)(s_act[t] && !(s_sc[(i - t * a.K) * S1 + t] < s_sum[t])) : (uint8_t)1;
+        a.out_ids[i] = bal;
         a.out_mask[i] = keep;
-        s_bal[i] = bal[r];
+        s_bal[i] = bal;
         s_keep[i] = keep;
     }
     if (!a.send_pos) return;
 
-    // 4. send map: stable counting sort of kept routes by instance
-    for (int i = tid; i < kRemapWaves * n_inst; i += kRemapThreads) s_cnt[i] = 0;
-    __syncthreads();
+    // 4. send map: stable counting sort of kept routes by instance; the
+    //    first kCountWaves waves each own a contiguous range of entries
+    lds_barrier();  // s_cnt reuses the table's space read just above
+    for (int i = tid; i < kCountWaves * n_inst; i += kRemapThreads) s_cnt[i] = 0;
+    lds_barrier();
     const int wave = tid / kWave;
     const int lane = tid & (kWave - 1);
-    const int seg = (((n + kRemapWaves - 1) / kRemapWaves) + kWave - 1) & ~(kWave - 1);
-    const int lo = min(wave * seg, n);
-    const int hi = min(lo + seg, n);
-    int* my_cnt = s_cnt + wave * n_inst;
+    const int seg = (((n + kCountWaves - 1) / kCountWaves) + kWave - 1) & ~(kWave - 1);
+    const int lo = wave < kCountWaves ? min(wave * seg, n) : n;
+    const int hi = wave < kCountWaves ? min(lo + seg, n) : n;
+    int* my_cnt = s_cnt + min(wave, kCountWaves - 1) * n_inst;
     for (int i = lo + lane; i < hi; i += kWave) {
         const int inst = s_bal[i];
         if (s_keep[i] && (unsigned)inst < (unsigned)n_inst) atomicAdd(&my_cnt[inst], 1);
     }
-    __syncthreads();
+    lds_barrier();
     // per-instance totals, then exclusive offsets in (instance, wave) order
     int tot = 0;
     if (tid < n_inst)
-        for (int v = 0; v < kRemapWaves; ++v) tot += s_cnt[v * n_inst + tid];
+        for (int v = 0; v < kCountWaves; ++v) tot += s_cnt[v * n_inst + tid];
     int all;
     const int base = block_exclusive_sum(tot, scratch, &all);
     if (tid < n_inst) {
         s_tot[tid] = tot;
         int run = base;
-        for (int v = 0; v < kRemapWaves; ++v) {
+        for (int v = 0; v < kCountWaves; ++v) {
             const int c = s_cnt[v * n_inst + tid];
             s_cnt[v * n_inst + tid] = run;
             run += c;
         }
     }
-    __syncthreads();
+    lds_barrier();
     for (int card = tid; card < a.ws; card += kRemapThreads) {
         int c = 0;
         for (int j = 0; j < a.ppr; ++j) c += s_tot[card * a.ppr + j];
         a.send_count[card] = c;
     }
-    int nbits = 0;
-    while ((1 << nbits) < n_inst) ++nbits;
     for (int b0 = lo; b0 < hi; b0 += kWave) {
         const int i = b0 + lane;
         bool valid = i < hi;
         int inst = valid ? s_bal[i] : 0;
         valid = valid && s_keep[i] && (unsigned)inst < (unsigned)n_inst;
         if (!valid) inst = 0;
-        const uint64_t peers = match_peers(inst, valid, nbits);
+        const uint64_t peers = match_peers(inst, valid);
         const int r = my_cnt[inst] + count_below(peers);
         if (valid && is_group_leader(peers)) my_cnt[inst] += __popcll(peers);
         if (i < hi) a.send_pos[i] = valid ? r : -1;
