@@ -82,12 +82,111 @@ def cpu_baseline(d, plan_ref):
                       f"({total} algorithmic bytes) in {dt:.2f} s"}
 
 
+def skew_sweep(torch, cba, synth, steps):
+    """Plan and dispatch+combine time as router imbalance grows (expert-level
+    maxvio 0.2, 1, 10, 20) at R=8, E=384, S=8192, K=8, H=7168, rank 0. The
+    received rows and returned expert outputs are seeded stand-ins (their
+    content does not affect the time); the routing, hence every index map,
+    is the sweep point's own."""
+    c = synth.SWEEP
+    R, E, S, K, H = c["R"], c["E"], c["S"], c["K"], c["H"]
+    C = S * K
+    g = torch.Generator(device="cuda")
+    g.manual_seed(c["seed"])
+    x = torch.randn(S, H, device="cuda", generator=g).to(torch.bfloat16)
+    recv_raw = torch.randn(C, H, device="cuda", generator=g).to(torch.bfloat16)
+    y_ret = torch.randn(C, H, device="cuda", generator=g).to(torch.bfloat16)
+    send_buf = torch.empty(C, H, dtype=torch.bfloat16, device="cuda")
+    grouped = torch.empty(C, H, dtype=torch.bfloat16, device="cuda")
+    out = torch.empty(S, H, dtype=torch.bfloat16, device="cuda")
+    ws = cba.plan_workspace(R, E, S, K)
+    pout = cba.plan_outputs(R, E, S, K)
+    b = algorithmic_bytes(S, K, H)
+    dc_bytes = b["pack"] + b["group"] + b["combine"]
+    stream = torch.cuda.current_stream()
+    points = []
+    for target in synth.SWEEP_TARGETS:
+        d = synth.make_sweep_routing(target)
+        ids = _dev(torch, d["topk_ids"].reshape(-1))
+        scores = _dev(torch, d["scores"][0])
+        times = {"plan": [], "dispatch_combine": []}
+        for it in range(steps + 3):
+            ev = [torch.cuda.Event(enable_timing=True) for _ in range(3)]
+            ev[0].record(stream)
+            cba.plan(ids, R, E, S, K, my_rank=0, workspace=ws, out=pout)
+            ev[1].record(stream)
+            cba.dispatch(K, x=x, send_pos=pout["send_pos"], send_buf=send_buf)
+            cba.dispatch(K, recv_raw=recv_raw, recv_pos=pout["recv_pos"], recv_grouped=grouped)
+            cba.combine(y_ret, pout["send_pos"], scores, out_bf16=out)
+            ev[2].record(stream)
+            torch.cuda.synchronize()
+            if it >= 3:
+                times["plan"].append(ev[0].elapsed_time(ev[1]) * 1e3)
+                times["dispatch_combine"].append(ev[1].elapsed_time(ev[2]) * 1e3)
+        loads = pout["rank_load"].cpu().numpy()
+        n_inst = int(pout["inst_gid_base"][-1].item())
+        dc = float(np.median(times["dispatch_combine"]))
+        points.append({"target_maxvio": target,
+                       "expert_maxvio": round(d["maxvio_expert"], 3),
+                       "rank_maxvio_native": round(float(loads.max()) / C - 1.0, 3),
+                       "instances": n_inst, "redundant_instances": n_inst - E,
+                       "plan_us": round(float(np.median(times["plan"])), 2),
+                       "dispatch_combine_us": round(dc, 2),
+                       "dispatch_combine_GBs": round(dc_bytes / (dc * 1e-6) / 1e9, 1)})
+    return {"workload": f"R={R} E={E} S={S} K={K} H={H} bf16, rank 0; maxvio at expert "
+                        "granularity (max expert load / mean - 1)", "points": points}
+
+
+def zero_copy(torch, cba, d, pout, steps):
+    """The zero-copy pair at the same workload: rank 0 pushes its rows
+    straight into the R grouped buffers and pulls the expert outputs back
+    from them. On one GPU the R buffers are slices of one [R, C, H]
+    allocation standing in for the peers' memory (over xGMI the same kernels
+    write and read remote HBM through mapped peer pointers)."""
+    R, S, K, H, C = d["R"], d["S"], d["K"], d["H"], d["C"]
+    x = _dev(torch, d["x"])
+    scores = _dev(torch, d["scores"][0])
+    grouped = torch.empty(R, C, H, dtype=torch.bfloat16, device="cuda")
+    g = torch.Generator(device="cuda")
+    g.manual_seed(11)
+    y = torch.randn(R, C, H, device="cuda", generator=g).to(torch.bfloat16)
+    gp, yp = cba.peer_table(grouped), cba.peer_table(y)
+    rd, rs = pout["route_dest"][:C], pout["route_slot"][:C]
+    out = torch.empty(S, H, dtype=torch.bfloat16, device="cuda")
+    stream = torch.cuda.current_stream()
+    t = {"push": [], "pull": []}
+    for it in range(steps + 3):
+        ev = [torch.cuda.Event(enable_timing=True) for _ in range(3)]
+        ev[0].record(stream)
+        cba.dispatch_to_peers(K, x, rd, rs, gp, C)
+        ev[1].record(stream)
+        cba.combine_from_peers(yp, C, H, rd, rs, scores, out_bf16=out)
+        ev[2].record(stream)
+        torch.cuda.synchronize()
+        if it >= 3:
+            t["push"].append(ev[0].elapsed_time(ev[1]) * 1e3)
+            t["pull"].append(ev[1].elapsed_time(ev[2]) * 1e3)
+    us = {k: float(np.mean(v)) for k, v in t.items()}
+    row = H * 2
+    nb = {"push": S * row + C * row + 2 * C * 4, "pull": C * row + S * row + C * 12}
+    del grouped, y
+    return {"push_us": round(us["push"], 2), "pull_us": round(us["pull"], 2),
+            "push_GBs": round(nb["push"] / (us["push"] * 1e-6) / 1e9, 1),
+            "pull_GBs": round(nb["pull"] / (us["pull"] * 1e-6) / 1e9, 1),
+            "dispatch_combine_us": round(us["push"] + us["pull"], 2),
+            "algorithmic_bytes": nb}
+
+
 def main():
     ap = argparse.ArgumentParser()
     ap.add_argument("--gpus", type=int, default=1)
     ap.add_argument("--steps", type=int, default=50)
     ap.add_argument("--warmup", type=int, default=5)
     ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--no-skew-sweep", action="store_true",
+                    help="skip the imbalance sweep (R=8 E=384 S=8192 K=8 H=7168)")
+    ap.add_argument("--no-zero-copy", action="store_true",
+                    help="skip the zero-copy push/pull timing")
     ap.add_argument("--copy-calibration", action="store_true",
                     help="after the timed steps, run plain device-to-device copies of "
                          "the group kernel's output size (a known-size reference for "
@@ -212,6 +311,10 @@ def main():
                      "frac": round(group_gbs / HBM_PEAK_GBS, 4),
                      "traffic": _traffic("group_rows")},
     }
+    if not args.no_zero_copy:
+        res["zero_copy"] = zero_copy(torch, cba, d, pout, steps=max(5, min(args.steps, 20)))
+    if not args.no_skew_sweep:
+        res["skew_sweep"] = skew_sweep(torch, cba, synth, steps=max(5, min(args.steps, 20)))
     if args.copy_calibration:
         nbytes = C * H * 2
         for _ in range(3):

@@ -6,6 +6,6 @@ under their C names, ``api`` the tensor-level calls. Importing the package
 does not load the library; the first call does, and raises if it has not
 been built (``python -m combine_balancing_amd.build``).
 """
-from .api import (combine, dispatch, plan, plan_outputs, plan_workspace,  # noqa: F401
-                  remap_prune)
+from .api import (combine, combine_from_peers, dispatch, dispatch_to_peers,  # noqa: F401
+                  peer_table, plan, plan_outputs, plan_workspace, remap_prune, ungroup)
 from ._binding import MepError, lib  # noqa: F401

@@ -51,6 +51,12 @@ def lib():
     L.mep_dispatch.restype = I
     L.mep_combine.argtypes = [I, I, I, P, I, P, P, P, P, P]
     L.mep_combine.restype = I
+    L.mep_dispatch_to_peers.argtypes = [I, I, I, I, I, P, P, P, P, P]
+    L.mep_dispatch_to_peers.restype = I
+    L.mep_combine_from_peers.argtypes = [I, I, I, I, I, P, P, P, P, P, P, P]
+    L.mep_combine_from_peers.restype = I
+    L.mep_ungroup.argtypes = [I, I, P, P, P, P]
+    L.mep_ungroup.restype = I
     _lib = L
     return L
 
@@ -99,3 +105,18 @@ def mep_dispatch(T, K, H, x, send_pos, send_buf, n_recv, recv_pos, recv_raw,
 
 def mep_combine(T, K, H, y_ret, n_y, send_pos, scores, out_bf16, out_f32, stream) -> int:
     return lib().mep_combine(T, K, H, y_ret, n_y, send_pos, scores, out_bf16, out_f32, stream)
+
+
+def mep_dispatch_to_peers(T, K, H, R, C, x, route_dest, route_slot, peer_bufs, stream) -> int:
+    return lib().mep_dispatch_to_peers(T, K, H, R, C, x, route_dest, route_slot, peer_bufs,
+                                       stream)
+
+
+def mep_combine_from_peers(T, K, H, R, C, peer_bufs, route_dest, route_slot, scores, out_bf16,
+                           out_f32, stream) -> int:
+    return lib().mep_combine_from_peers(T, K, H, R, C, peer_bufs, route_dest, route_slot, scores,
+                                        out_bf16, out_f32, stream)
+
+
+def mep_ungroup(n, H, recv_pos, y_grouped, y_arrival, stream) -> int:
+    return lib().mep_ungroup(n, H, recv_pos, y_grouped, y_arrival, stream)

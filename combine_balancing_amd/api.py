@@ -204,3 +204,64 @@ def combine(y_ret, send_pos, scores, out_bf16=True, out_f32=False, stream=None):
         _stream_handle(stream))
     B.check("mep_combine", rc)
     return out_bf16, out_f32
+
+
+def peer_table(bufs):
+    """Device array of row-buffer addresses (one per rank) for the zero-copy
+    calls. `bufs`: a list of R device tensors, or one [R, C, H] tensor."""
+    if isinstance(bufs, torch.Tensor):
+        bufs = list(bufs.unbind(0))
+    for b in bufs:
+        _need(b, "peer buffer", _BF16_LIKE)
+    ptrs = torch.tensor([b.data_ptr() for b in bufs], dtype=torch.int64)
+    return ptrs.to(bufs[0].device)
+
+
+def dispatch_to_peers(K, x, route_dest, route_slot, peers, C, stream=None):
+    """mep_dispatch_to_peers. x [T,H]; route_dest/route_slot [T*K] (this
+    rank's routes); peers: device pointer table from peer_table()."""
+    T, H = x.shape
+    R = peers.numel()
+    rc = B.mep_dispatch_to_peers(
+        T, K, H, R, C, _need(x, "x", _BF16_LIKE),
+        _need(route_dest, "route_dest", torch.int32, T * K),
+        _need(route_slot, "route_slot", torch.int32, T * K),
+        _need(peers, "peers", torch.int64, R), _stream_handle(stream))
+    B.check("mep_dispatch_to_peers", rc)
+
+
+def combine_from_peers(peers, C, H, route_dest, route_slot, scores, out_bf16=True, out_f32=False,
+                       stream=None):
+    """mep_combine_from_peers. Returns (out_bf16, out_f32)."""
+    T, K = scores.shape
+    R = peers.numel()
+    dev = scores.device
+    if out_bf16 is True:
+        out_bf16 = torch.empty(T, H, dtype=torch.bfloat16, device=dev)
+    elif out_bf16 is False:
+        out_bf16 = None
+    if out_f32 is True:
+        out_f32 = torch.empty(T, H, dtype=torch.float32, device=dev)
+    elif out_f32 is False:
+        out_f32 = None
+    rc = B.mep_combine_from_peers(
+        T, K, H, R, C, _need(peers, "peers", torch.int64, R),
+        _need(route_dest, "route_dest", torch.int32, T * K),
+        _need(route_slot, "route_slot", torch.int32, T * K),
+        _need(scores, "scores", torch.float32, T * K),
+        _opt(out_bf16, "out_bf16", _BF16_LIKE, T * H), _opt(out_f32, "out_f32", torch.float32, T * H),
+        _stream_handle(stream))
+    B.check("mep_combine_from_peers", rc)
+    return out_bf16, out_f32
+
+
+def ungroup(y_grouped, recv_pos, y_arrival=None, stream=None):
+    """mep_ungroup: y_arrival[recv_pos[t]] = y_grouped[t]."""
+    n, H = y_grouped.shape
+    if y_arrival is None:
+        y_arrival = torch.empty_like(y_grouped)
+    rc = B.mep_ungroup(n, H, _need(recv_pos, "recv_pos", torch.int32, n),
+                       _need(y_grouped, "y_grouped", _BF16_LIKE),
+                       _need(y_arrival, "y_arrival", _BF16_LIKE, n * H), _stream_handle(stream))
+    B.check("mep_ungroup", rc)
+    return y_arrival

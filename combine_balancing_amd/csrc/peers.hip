@@ -1,0 +1,276 @@
+// Zero-copy dispatch and combine, and the expert-side return.
+//
+// Method ("MoonEP" technical overview, architecture section): tokens are
+// written straight to their final position on the receiving rank, already
+// grouped by expert instance, and the application works on views of that
+// buffer; the combine side reads expert outputs where they are. With the
+// plan's global (destination, slot) of every route, a rank can therefore
+// write each of its rows into the destination's grouped buffer directly
+// (no send buffer, no receive-side grouping) and later read each returned
+// expert output from the destination's grouped output buffer.
+//
+// The destination buffers are named by a device array of R row pointers
+// (peer memory mapped into this process on a multi-GPU system; on one GPU,
+// slices of one allocation). mep_ungroup is the return step of the
+// non-zero-copy path: grouped expert outputs back to arrival order.
+//
+// Kernel shapes follow the pack and combine kernels (one wave per token for
+// the push, one work-group per token for the pull, one work-group per row for
+// the ungroup); all three are HBM-bound row movers.
+#include <algorithm>
+
+#include "rows.h"
+
+namespace mep {
+namespace {
+
+using namespace rows;
+
+__device__ __forceinline__ const u32x4* read_ptr_lane(const u32x4* p, int lane) {
+    const uint64_t v = (uint64_t)(uintptr_t)p;
+    const uint32_t lo = __builtin_amdgcn_readlane((uint32_t)v, lane);
+    const uint32_t hi = __builtin_amdgcn_readlane((uint32_t)(v >> 32), lane);
+    return (const u32x4*)(uintptr_t)(((uint64_t)hi << 32) | lo);
+}
+
+// peers[route_dest[t*K+k]][route_slot[t*K+k]] = x[t] for every valid route.
+template <int VPL>
+__global__ __launch_bounds__(kPackThreads) void push_rows(const u32x4* __restrict__ x,
+                                                          const int* __restrict__ rdest,
+                                                          const int* __restrict__ rslot,
+                                                          u32x4* const* __restrict__ peers, int T,
+                                                          int K, int nvec, int R, int C) {
+    const int t = wave_row();
+    if (t >= T) return;
+    const int lane = lane_id();
+    const u32x4* dst = nullptr;  // this lane's route (lane k < K)
+    if (lane < K) {
+        const int d = rdest[(size_t)t * K + lane];
+        const int sl = rslot[(size_t)t * K + lane];
+        if ((unsigned)d < (unsigned)R && (unsigned)sl < (unsigned)C)
+            dst = peers[d] + (size_t)sl * nvec;
+    }
+    const u32x4* src = x + (size_t)t * nvec;
+    for (int v0 = 0; v0 < nvec; v0 += kWave * VPL) {
+        u32x4 r[VPL];
+#pragma unroll
+        for (int i = 0; i < VPL; ++i) {
+            const int v = v0 + i * kWave + lane;
+            if (v < nvec) r[i] = __builtin_nontemporal_load(src + v);
+        }
+        // the K destinations are read across lanes with the whole wave
+        // active; each is then wave-uniform
+        for (int k = 0; k < K; ++k) {
+            u32x4* p = (u32x4*)read_ptr_lane(dst, k);
+            if (!p) continue;
+#pragma unroll
+            for (int i = 0; i < VPL; ++i) {
+                const int v = v0 + i * kWave + lane;
+                if (v < nvec) __builtin_nontemporal_store(r[i], p + v);
+            }
+        }
+    }
+}
+
+// out[t] = sum over k in order of score * peers[dest][slot], fp32, from +0.
+template <int KT, int VPT>
+__global__ __launch_bounds__(kCombineThreads) void pull_combine(
+    const u32x4* const* __restrict__ peers, const int* __restrict__ rdest,
+    const int* __restrict__ rslot, const float* __restrict__ scores, u32x4* __restrict__ out_bf16,
+    f32x4* __restrict__ out_f32, int T, int nvec, int R, int C, int tpr, int rpb) {
+    const int r = threadIdx.x / tpr;
+    const int tid = threadIdx.x - r * tpr;
+    const int t = blockIdx.x * rpb + r;
+    if (t >= T) return;
+    // skipped routes read row 0 of rank 0's buffer so that all K loads issue
+    // together; their terms are left out exactly
+    const u32x4* src[KT];
+    float sc[KT];
+    uint32_t use = 0;
+#pragma unroll
+    for (int k = 0; k < KT; ++k) {
+        const int d = rdest[(size_t)t * KT + k];
+        const int sl = rslot[(size_t)t * KT + k];
+        const bool ok = (unsigned)d < (unsigned)R && (unsigned)sl < (unsigned)C;
+        use |= (uint32_t)ok << k;
+        src[k] = ok ? peers[d] + (size_t)sl * nvec : peers[0];
+        sc[k] = scores[(size_t)t * KT + k];
+    }
+    for (int v0 = 0; v0 < nvec; v0 += tpr * VPT) {
+        u32x4 yk[VPT][KT];
+#pragma unroll
+        for (int i = 0; i < VPT; ++i) {
+            const int v = min(v0 + i * tpr + tid, nvec - 1);
+#pragma unroll
+            for (int k = 0; k < KT; ++k) yk[i][k] = __builtin_nontemporal_load(src[k] + v);
+        }
+#pragma unroll
+        for (int i = 0; i < VPT; ++i) {
+            const int v = v0 + i * tpr + tid;
+            float acc[8];
+#pragma unroll
+            for (int j = 0; j < 8; ++j) acc[j] = 0.0f;
+#pragma unroll
+            for (int k = 0; k < KT; ++k)
+                if ((use >> k) & 1u) accumulate(acc, yk[i][k], sc[k]);
+            if (v < nvec) store_out(acc, out_bf16, out_f32, (size_t)t * nvec + v);
+        }
+    }
+}
+
+// Any K up to 64: one route at a time, in k order.
+__global__ __launch_bounds__(kCombineThreads) void pull_combine_any(
+    const u32x4* const* __restrict__ peers, const int* __restrict__ rdest,
+    const int* __restrict__ rslot, const float* __restrict__ scores, u32x4* __restrict__ out_bf16,
+    f32x4* __restrict__ out_f32, int T, int K, int nvec, int R, int C, int tpr, int rpb) {
+    const int r = threadIdx.x / tpr;
+    const int tid = threadIdx.x - r * tpr;
+    const int t = blockIdx.x * rpb + r;
+    if (t >= T) return;
+    for (int v = tid; v < nvec; v += tpr) {
+        float acc[8];
+#pragma unroll
+        for (int j = 0; j < 8; ++j) acc[j] = 0.0f;
+        for (int k = 0; k < K; ++k) {
+            const int d = rdest[(size_t)t * K + k];
+            const int sl = rslot[(size_t)t * K + k];
+            if ((unsigned)d >= (unsigned)R || (unsigned)sl >= (unsigned)C) continue;
+            accumulate(acc, peers[d][(size_t)sl * nvec + v], scores[(size_t)t * K + k]);
+        }
+        store_out(acc, out_bf16, out_f32, (size_t)t * nvec + v);
+    }
+}
+
+// y_arrival[recv_pos[t]] = y_grouped[t]: the inverse of the grouping.
+template <int VPT>
+__global__ __launch_bounds__(kMaxTpr) void ungroup_rows(const u32x4* __restrict__ in,
+                                                        const int* __restrict__ pos,
+                                                        u32x4* __restrict__ out, int n, int nvec,
+                                                        int tpr, int rpb) {
+    const int r = threadIdx.x / tpr;
+    const int tid = threadIdx.x - r * tpr;
+    const int t = blockIdx.x * rpb + r;
+    if (t >= n) return;
+    const int to = pos[t];
+    if ((unsigned)to >= (unsigned)n) return;
+    const u32x4* src = in + (size_t)t * nvec;
+    u32x4* dst = out + (size_t)to * nvec;
+    for (int v0 = 0; v0 < nvec; v0 += tpr * VPT) {
+        u32x4 q[VPT];
+#pragma unroll
+        for (int i = 0; i < VPT; ++i) {
+            const int v = v0 + i * tpr + tid;
+            if (v < nvec) q[i] = __builtin_nontemporal_load(src + v);
+        }
+#pragma unroll
+        for (int i = 0; i < VPT; ++i) {
+            const int v = v0 + i * tpr + tid;
+            if (v < nvec) __builtin_nontemporal_store(q[i], dst + v);
+        }
+    }
+}
+
+template <int VPL>
+void launch_push(hipStream_t s, const u32x4* x, const int* rd, const int* rs, u32x4* const* peers,
+                 int T, int K, int nvec, int R, int C) {
+    const dim3 g((T + kPackRows - 1) / kPackRows);
+    hipLaunchKernelGGL(push_rows<VPL>, g, dim3(kPackThreads), 0, s, x, rd, rs, peers, T, K, nvec,
+                       R, C);
+}
+
+template <int KT>
+void launch_pull(hipStream_t s, const u32x4* const* peers, const int* rd, const int* rs,
+                 const float* sc, u32x4* ob, f32x4* of, int T, int nvec, int R, int C) {
+    constexpr int VPT = KT > 8 ? 2 : 4;
+    const RowShape rsh = row_shape(nvec, VPT, kCombineThreads);
+    const dim3 g((T + rsh.rpb - 1) / rsh.rpb), b(rsh.tpr * rsh.rpb);
+    hipLaunchKernelGGL((pull_combine<KT, VPT>), g, b, 0, s, peers, rd, rs, sc, ob, of, T, nvec, R,
+                       C, rsh.tpr, rsh.rpb);
+}
+
+}  // namespace
+}  // namespace mep
+
+using namespace mep;
+using namespace mep::rows;
+
+extern "C" int mep_dispatch_to_peers(int T, int K, int H, int R, int C, const uint16_t* x,
+                                     const int32_t* route_dest, const int32_t* route_slot,
+                                     uint16_t* const* peer_bufs, void* stream) {
+    if (T < 0 || K < 1 || K > 64 || H < 8 || H > 65536 || (H % 8) != 0 || R < 1 || C < 1 ||
+        (long long)T * K >= (1ll << 31))
+        return MEP_ERR_SHAPE;
+    if (T == 0) return MEP_OK;
+    if (!x || !route_dest || !route_slot || !peer_bufs) return MEP_ERR_NULLPTR;
+    if (!aligned16(x)) return MEP_ERR_SHAPE;
+    const int nvec = H / 8;
+    const int vpl = std::min(kMaxVpl, std::max(1, (nvec + kWave - 1) / kWave));
+    MEP_VPL_SWITCH(vpl, launch_push, (hipStream_t)stream, (const u32x4*)x,
+                   (const int*)route_dest, (const int*)route_slot, (u32x4* const*)peer_bufs, T, K,
+                   nvec, R, C);
+    MEP_LAUNCH_CHECK();
+    return MEP_OK;
+}
+
+extern "C" int mep_combine_from_peers(int T, int K, int H, int R, int C,
+                                      const uint16_t* const* peer_bufs,
+                                      const int32_t* route_dest, const int32_t* route_slot,
+                                      const float* scores, uint16_t* out_bf16, float* out_f32,
+                                      void* stream) {
+    if (T < 0 || K < 1 || K > 64 || H < 8 || H > 65536 || (H % 8) != 0 || R < 1 || C < 1 ||
+        (long long)T * K >= (1ll << 31))
+        return MEP_ERR_SHAPE;
+    if (T == 0) return MEP_OK;
+    if (!peer_bufs || !route_dest || !route_slot || !scores) return MEP_ERR_NULLPTR;
+    if (!out_bf16 && !out_f32) return MEP_ERR_NULLPTR;
+    if ((out_bf16 && !aligned16(out_bf16)) || (out_f32 && !aligned16(out_f32))) return MEP_ERR_SHAPE;
+    hipStream_t s = (hipStream_t)stream;
+    const int nvec = H / 8;
+    const u32x4* const* p = (const u32x4* const*)peer_bufs;
+    const int* rd = (const int*)route_dest;
+    const int* rs = (const int*)route_slot;
+    u32x4* ob = (u32x4*)out_bf16;
+    f32x4* of = (f32x4*)out_f32;
+    switch (K) {
+        case 1: launch_pull<1>(s, p, rd, rs, scores, ob, of, T, nvec, R, C); break;
+        case 2: launch_pull<2>(s, p, rd, rs, scores, ob, of, T, nvec, R, C); break;
+        case 4: launch_pull<4>(s, p, rd, rs, scores, ob, of, T, nvec, R, C); break;
+        case 6: launch_pull<6>(s, p, rd, rs, scores, ob, of, T, nvec, R, C); break;
+        case 8: launch_pull<8>(s, p, rd, rs, scores, ob, of, T, nvec, R, C); break;
+        case 16: launch_pull<16>(s, p, rd, rs, scores, ob, of, T, nvec, R, C); break;
+        default: {
+            const RowShape rsh = row_shape(nvec, 1, kCombineThreads);
+            hipLaunchKernelGGL(pull_combine_any, dim3((T + rsh.rpb - 1) / rsh.rpb),
+                               dim3(rsh.tpr * rsh.rpb), 0, s, p, rd, rs, scores, ob, of, T, K,
+                               nvec, R, C, rsh.tpr, rsh.rpb);
+            break;
+        }
+    }
+    MEP_LAUNCH_CHECK();
+    return MEP_OK;
+}
+
+extern "C" int mep_ungroup(int n, int H, const int32_t* recv_pos, const uint16_t* y_grouped,
+                           uint16_t* y_arrival, void* stream) {
+    if (n < 0 || H < 8 || H > 65536 || (H % 8) != 0) return MEP_ERR_SHAPE;
+    if (n == 0) return MEP_OK;
+    if (!recv_pos || !y_grouped || !y_arrival) return MEP_ERR_NULLPTR;
+    if (!aligned16(y_grouped) || !aligned16(y_arrival)) return MEP_ERR_SHAPE;
+    const int nvec = H / 8;
+    int vpt = 1;
+    while (vpt < 8 && nvec > kMaxTpr * vpt) vpt *= 2;
+    const RowShape rsh = row_shape(nvec, vpt, kMaxTpr);
+    const dim3 g((n + rsh.rpb - 1) / rsh.rpb), b(rsh.tpr * rsh.rpb);
+    hipStream_t s = (hipStream_t)stream;
+    const u32x4* in = (const u32x4*)y_grouped;
+    const int* pos = (const int*)recv_pos;
+    u32x4* out = (u32x4*)y_arrival;
+    switch (vpt) {
+        case 1: hipLaunchKernelGGL(ungroup_rows<1>, g, b, 0, s, in, pos, out, n, nvec, rsh.tpr, rsh.rpb); break;
+        case 2: hipLaunchKernelGGL(ungroup_rows<2>, g, b, 0, s, in, pos, out, n, nvec, rsh.tpr, rsh.rpb); break;
+        case 4: hipLaunchKernelGGL(ungroup_rows<4>, g, b, 0, s, in, pos, out, n, nvec, rsh.tpr, rsh.rpb); break;
+        default: hipLaunchKernelGGL(ungroup_rows<8>, g, b, 0, s, in, pos, out, n, nvec, rsh.tpr, rsh.rpb); break;
+    }
+    MEP_LAUNCH_CHECK();
+    return MEP_OK;
+}

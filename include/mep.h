@@ -250,6 +250,62 @@ int mep_combine(int T, int K, int H, const uint16_t* y_ret, int n_y,
                 uint16_t* out_bf16, float* out_f32,
                 void* stream);
 
+/* ------------------------------------------------ zero-copy and return */
+
+/*
+ * mep_dispatch_to_peers - zero-copy dispatch ([MoonEP-TD] architecture
+ * section: tokens are written directly to their final position on the
+ * receiving rank, grouped by expert, and used in place). Each of this rank's
+ * routes writes its token row straight into the destination's grouped
+ * receive buffer, with no send buffer and no receive-side grouping:
+ *   peer_bufs[route_dest[t*K+k]][route_slot[t*K+k], :] = x[t, :]
+ *   x          [T,H] bf16, this rank's tokens;
+ *   route_dest, route_slot [T*K] int32: this rank's slice of mep_plan's
+ *              route maps (routes (my_rank, t, k)); entries outside
+ *              [0,R) x [0,C) are skipped;
+ *   peer_bufs  DEVICE array of R device pointers, peer_bufs[d] the grouped
+ *              receive buffer [C,H] bf16 of rank d, 16-byte aligned (memory
+ *              of other GPUs mapped into this process on a multi-GPU system;
+ *              slices of one allocation on one GPU).
+ * Run by every rank, this fills each rank's grouped buffer with exactly what
+ * pack -> exchange -> group produces. Sizes as mep_dispatch's pack, R, C >= 1;
+ * T == 0 does nothing. Errors: MEP_ERR_NULLPTR, MEP_ERR_SHAPE, MEP_ERR_HIP.
+ */
+int mep_dispatch_to_peers(int T, int K, int H, int R, int C, const uint16_t* x,
+                          const int32_t* route_dest, const int32_t* route_slot,
+                          uint16_t* const* peer_bufs, void* stream);
+
+/*
+ * mep_combine_from_peers - zero-copy combine: the K expert outputs of each
+ * token are read where the experts wrote them, in the destinations' grouped
+ * output buffers, and reduced exactly as mep_combine does (fp32, fixed k
+ * order, from +0; bf16 round-to-nearest-even):
+ *   out[t,h] = sum over k of scores[t*K+k] * peer_bufs[dest][slot, h]
+ * with (dest, slot) = (route_dest, route_slot)[t*K+k] of this rank's routes;
+ * out-of-range entries are skipped. peer_bufs: DEVICE array of R device
+ * pointers to [C,H] bf16 grouped expert outputs. Outputs and errors as
+ * mep_combine. With the same values it gives the same bits as mep_combine
+ * on the returned rows.
+ */
+int mep_combine_from_peers(int T, int K, int H, int R, int C,
+                           const uint16_t* const* peer_bufs,
+                           const int32_t* route_dest, const int32_t* route_slot,
+                           const float* scores, uint16_t* out_bf16,
+                           float* out_f32, void* stream);
+
+/*
+ * mep_ungroup - the return step of the non-zero-copy path: expert outputs
+ * in grouped order go back to arrival (source-major) order, the inverse of
+ * mep_dispatch's grouping:
+ *   y_arrival[recv_pos[t], :] = y_grouped[t, :] for t in [0, n)
+ * (recv_pos from mep_plan; entries outside [0, n) are skipped). The source
+ * segments of y_arrival are then what each source rank receives back, in
+ * its send order. n >= 0 (0 does nothing), H as mep_dispatch.
+ * Errors: MEP_ERR_NULLPTR, MEP_ERR_SHAPE, MEP_ERR_HIP.
+ */
+int mep_ungroup(int n, int H, const int32_t* recv_pos, const uint16_t* y_grouped,
+                uint16_t* y_arrival, void* stream);
+
 #ifdef __cplusplus
 }
 #endif

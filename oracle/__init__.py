@@ -55,6 +55,12 @@ def _load():
     lib.oracle_group.restype = I
     lib.oracle_combine.argtypes = [I, I, I, P, P, P, P, P]
     lib.oracle_combine.restype = I
+    lib.oracle_push.argtypes = [I, I, I, I, I, P, P, P, P]
+    lib.oracle_push.restype = I
+    lib.oracle_pull_combine.argtypes = [I, I, I, I, I, P, P, P, P, P, P]
+    lib.oracle_pull_combine.restype = I
+    lib.oracle_ungroup.argtypes = [I, I, P, P, P]
+    lib.oracle_ungroup.restype = I
     lib.oracle_bf16_from_float.argtypes = [P, P, ctypes.c_int64]
     lib.oracle_bf16_from_float.restype = None
     lib.oracle_float_from_fp16.argtypes = [P, P, ctypes.c_int64]
@@ -199,6 +205,47 @@ def combine(y_ret, send_pos, scores, want_bf16=True, want_f32=True):
     return ob, of
 
 
+def push(x, route_dest, route_slot, K, R, C, grouped=None):
+    """Zero-copy dispatch into all R grouped buffers [R, C, H] (oracle_push)."""
+    lib = _load()
+    x = _c(x, np.uint16)
+    T, H = x.shape
+    rd = _c(route_dest, np.int32).reshape(-1)
+    rs = _c(route_slot, np.int32).reshape(-1)
+    if rd.size != T * K or rs.size != T * K:
+        raise ValueError("route maps must hold T*K entries")
+    if grouped is None:
+        grouped = np.zeros((R, C, H), np.uint16)
+    _check(lib.oracle_push(T, K, H, R, C, _p(x), _p(rd), _p(rs), _p(grouped)), "oracle_push")
+    return grouped
+
+
+def pull_combine(grouped, route_dest, route_slot, scores, want_bf16=True, want_f32=True):
+    """Zero-copy combine from grouped buffers [R, C, H] (oracle_pull_combine)."""
+    lib = _load()
+    g = _c(grouped, np.uint16)
+    R, C, H = g.shape
+    sc = _c(scores, np.float32)
+    T, K = sc.shape
+    rd = _c(route_dest, np.int32).reshape(-1)
+    rs = _c(route_slot, np.int32).reshape(-1)
+    ob = np.zeros((T, H), np.uint16) if want_bf16 else None
+    of = np.zeros((T, H), np.float32) if want_f32 else None
+    _check(lib.oracle_pull_combine(T, K, H, R, C, _p(g), _p(rd), _p(rs), _p(sc), _p(ob), _p(of)),
+           "oracle_pull_combine")
+    return ob, of
+
+
+def ungroup(y_grouped, recv_pos):
+    """y_arrival[recv_pos[t]] = y_grouped[t] (oracle_ungroup)."""
+    lib = _load()
+    y = _c(y_grouped, np.uint16)
+    rp = _c(recv_pos, np.int32).reshape(-1)
+    out = np.zeros_like(y)
+    _check(lib.oracle_ungroup(rp.size, y.shape[1], _p(rp), _p(y), _p(out)), "oracle_ungroup")
+    return out
+
+
 def bf16_from_float(a):
     """fp32 -> bf16 round-to-nearest-even (the oracle's own conversion)."""
     lib = _load()
@@ -245,9 +292,7 @@ def chain(x_all, plans, scores_all, expert_fn):
         res[d]["recv_grouped"] = group(raw, plans[d]["recv_pos"])
         yg = expert_fn(d, res[d]["recv_grouped"], plans[d])
         res[d]["y_grouped"] = yg
-        y_arr = np.empty_like(yg)
-        y_arr[plans[d]["recv_pos"]] = yg          # back to arrival order
-        res[d]["y_arrival"] = y_arr
+        res[d]["y_arrival"] = ungroup(yg, plans[d]["recv_pos"])   # back to arrival order
     for src in range(R):
         parts = []
         for d in range(R):

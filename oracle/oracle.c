@@ -465,3 +465,65 @@ void oracle_bf16_from_float(const float* in, uint16_t* out, int64_t n) {
 void oracle_float_from_fp16(const uint16_t* in, float* out, int64_t n) {
     for (int64_t i = 0; i < n; i++) out[i] = fp16_to_float(in[i]);
 }
+
+/* ------------------------------------------------ zero-copy and return */
+
+/*
+ * oracle_push: zero-copy dispatch ([MoonEP-TD]: rows written straight to
+ * their grouped position on the receiving rank). All R grouped buffers are
+ * one host array [R*C][H]: for every route (t,k) of this rank,
+ *   grouped[route_dest*C + route_slot] = x[t]   (out-of-range maps skipped).
+ */
+int oracle_push(int T, int K, int H, int R, int C, const uint16_t* x,
+                const int32_t* route_dest, const int32_t* route_slot, uint16_t* grouped) {
+    if (T < 0 || K < 1 || H < 1 || R < 1 || C < 1) return OR_ERR_ARG;
+    for (int64_t t = 0; t < T; t++)
+        for (int k = 0; k < K; k++) {
+            int32_t d = route_dest[t * K + k], s = route_slot[t * K + k];
+            if (d < 0 || d >= R || s < 0 || s >= C) continue;
+            for (int64_t h = 0; h < H; h++)
+                grouped[((int64_t)d * C + s) * H + h] = x[t * H + h];
+        }
+    return OR_OK;
+}
+
+/*
+ * oracle_pull_combine: zero-copy combine, the same reduction as
+ * oracle_combine with each route's expert output read from its grouped
+ * position: y = grouped[route_dest*C + route_slot].
+ */
+int oracle_pull_combine(int T, int K, int H, int R, int C, const uint16_t* grouped,
+                        const int32_t* route_dest, const int32_t* route_slot,
+                        const float* scores, uint16_t* out_bf16, float* out_f32) {
+    if (T < 0 || K < 1 || H < 1 || R < 1 || C < 1) return OR_ERR_ARG;
+    for (int64_t t = 0; t < T; t++)
+        for (int64_t h = 0; h < H; h++) {
+            float acc = 0.0f;
+            for (int k = 0; k < K; k++) {
+                int32_t d = route_dest[t * K + k], s = route_slot[t * K + k];
+                if (d < 0 || d >= R || s < 0 || s >= C) continue;
+                float y = bf16_to_float(grouped[((int64_t)d * C + s) * H + h]);
+                float prod = scores[t * K + k] * y;
+                acc = acc + prod;
+            }
+            if (out_f32) out_f32[t * H + h] = acc;
+            if (out_bf16) out_bf16[t * H + h] = float_to_bf16_rne(acc);
+        }
+    return OR_OK;
+}
+
+/*
+ * oracle_ungroup: y_arrival[recv_pos[t]] = y_grouped[t], the inverse of
+ * oracle_group (entries outside [0, n) skipped).
+ */
+int oracle_ungroup(int n, int H, const int32_t* recv_pos, const uint16_t* y_grouped,
+                   uint16_t* y_arrival) {
+    if (n < 0 || H < 1) return OR_ERR_ARG;
+    for (int64_t t = 0; t < n; t++) {
+        int32_t to = recv_pos[t];
+        if (to < 0 || to >= n) continue;
+        for (int64_t h = 0; h < H; h++)
+            y_arrival[(int64_t)to * H + h] = y_grouped[t * H + h];
+    }
+    return OR_OK;
+}

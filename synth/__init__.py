@@ -189,3 +189,46 @@ def make_scores(rng: np.random.Generator, T: int, K: int) -> np.ndarray:
     """fp32 combine weights: softmax of N(0,1) draws, sorted descending."""
     v = -np.sort(-rng.standard_normal((T, K), dtype=np.float32), axis=1)
     return _softmax_f32(v)
+
+
+# ------------------------------------------------------------ skew sweep
+# The pages' comparison benchmark: EP=8 ranks, S=8192 tokens per rank, E=384
+# experts, K=8, H=7168, imbalance (maxvio) 0.2, 1, 10 and 20 from a shared
+# routing seed. maxvio there is read at expert granularity (a rank-level
+# maxvio cannot exceed R-1 = 7): max_e cnt[e] / (N/E) - 1, with N = R*S*K.
+SWEEP = dict(R=8, E=384, S=8192, K=8, H=7168, seed=6)
+SWEEP_TARGETS = (0.2, 1.0, 10.0, 20.0)
+
+
+def expert_maxvio(ids: np.ndarray, E: int) -> float:
+    cnt = np.bincount(np.asarray(ids).reshape(-1), minlength=E)
+    return float(cnt.max()) / (cnt.sum() / E) - 1.0
+
+
+def _sweep_alpha(target: float, E: int, K: int, seed: int, n_cal: int = 16384) -> float:
+    """Strength of a -alpha*ln(e+1) router bias giving expert maxvio ~target,
+    by bisection on a fixed calibration sample of logits."""
+    rng = np.random.default_rng(seed)
+    z = rng.standard_normal((n_cal, E), dtype=np.float32)
+    base = -np.log(np.arange(E, dtype=np.float64) + 1.0).astype(np.float32)
+    lo, hi = 0.0, 8.0
+    for _ in range(40):
+        mid = 0.5 * (lo + hi)
+        mv = expert_maxvio(_topk_desc(z + np.float32(mid) * base, K), E)
+        if mv < target:
+            lo = mid
+        else:
+            hi = mid
+    return 0.5 * (lo + hi)
+
+
+def make_sweep_routing(target: float):
+    """Routing table [R,S,K] of the skew sweep at one maxvio target."""
+    c = SWEEP
+    R, E, S, K = c["R"], c["E"], c["S"], c["K"]
+    alpha = _sweep_alpha(target, E, K, c["seed"] * 1000 + int(round(target * 10)))
+    rng = np.random.default_rng(c["seed"])
+    bias = (np.float32(alpha) * -np.log(np.arange(E, dtype=np.float64) + 1.0)).astype(np.float32)
+    ids, scores = _route(rng, R * S, E, K, bias)
+    return dict(topk_ids=ids.reshape(R, S, K), scores=scores.reshape(R, S, K), alpha=alpha,
+                maxvio_expert=expert_maxvio(ids, E), rng=rng, **{k: c[k] for k in ("R", "E", "S", "K", "H")})

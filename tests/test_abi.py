@@ -33,7 +33,8 @@ def B():
 def test_header_declares_the_four_entry_points():
     names = _declared()
     for n in ("mep_plan", "mep_remap_prune", "mep_dispatch", "mep_combine",
-              "mep_plan_workspace_size", "mep_status_str", "mep_version"):
+              "mep_plan_workspace_size", "mep_status_str", "mep_version",
+              "mep_dispatch_to_peers", "mep_combine_from_peers", "mep_ungroup"):
         assert n in names
 
 
@@ -141,3 +142,21 @@ def test_package_has_no_fallback(monkeypatch, tmp_path):
     monkeypatch.setattr(_binding, "_lib", None)
     with pytest.raises(RuntimeError, match="missing"):
         _binding.lib()
+
+
+def test_zero_copy_and_ungroup_validation(B):
+    P = B.mep_dispatch_to_peers
+    assert P(0, 2, 64, 4, 8, None, None, None, None, None) == B.MEP_OK
+    assert P(4, 2, 64, 4, 8, None, 16, 16, 16, None) == B.MEP_ERR_NULLPTR
+    assert P(4, 2, 60, 4, 8, 16, 16, 16, 16, None) == B.MEP_ERR_SHAPE
+    assert P(4, 2, 64, 0, 8, 16, 16, 16, 16, None) == B.MEP_ERR_SHAPE
+    assert P(4, 2, 64, 4, 8, 8, 16, 16, 16, None) == B.MEP_ERR_SHAPE      # unaligned x
+    Q = B.mep_combine_from_peers
+    assert Q(0, 2, 64, 4, 8, None, None, None, None, None, None, None) == B.MEP_OK
+    assert Q(4, 2, 64, 4, 8, 16, 16, 16, 16, None, None, None) == B.MEP_ERR_NULLPTR
+    assert Q(4, 0, 64, 4, 8, 16, 16, 16, 16, 16, None, None) == B.MEP_ERR_SHAPE
+    U = B.mep_ungroup
+    assert U(0, 64, None, None, None, None) == B.MEP_OK
+    assert U(4, 64, None, 16, 16, None) == B.MEP_ERR_NULLPTR
+    assert U(4, 12, 16, 16, 16, None) == B.MEP_ERR_SHAPE
+    assert U(-1, 64, 16, 16, 16, None) == B.MEP_ERR_SHAPE

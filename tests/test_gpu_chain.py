@@ -68,12 +68,10 @@ def test_chain(orc, name):
         assert np.array_equal(host(raw), ref[dst]["recv_raw"])
         assert np.array_equal(host(grouped), ref[dst]["recv_grouped"])
         assert np.array_equal(host(yg), ref[dst]["y_grouped"])
-        # back to arrival order: the inverse of grouping is grouping by the
-        # inverse permutation
-        inv = torch.empty_like(plans[dst]["recv_pos"])
-        inv[plans[dst]["recv_pos"].long()] = torch.arange(inv.numel(), dtype=torch.int32,
-                                                          device="cuda")
-        _, ya = cba.dispatch(K, recv_raw=yg, recv_pos=inv)
+        # back to arrival order (the expert-side return)
+        ya = cba.ungroup(yg, plans[dst]["recv_pos"])
+        torch.cuda.synchronize()
+        assert np.array_equal(host(ya), ref[dst]["y_arrival"])
         y_arrival.append(ya)
     note(f"chain {name}: combine")
     for src in range(R):
@@ -86,3 +84,76 @@ def test_chain(orc, name):
         assert np.all(bf16_ulp_diff(host(ob), ref[src]["out_bf16"]) <= 1)
         rf = ref[src]["out_f32"].astype(np.float64)
         assert np.all(np.abs(host(of).astype(np.float64) - rf) <= 1e-6 * np.abs(rf) + 1e-30)
+
+
+@pytest.mark.parametrize("name", ["tiny", "small"])
+def test_zero_copy_chain(orc, name):
+    # Every logical rank writes its rows straight into the grouped buffers
+    # (slices of one [R, C, H] allocation stand in for the peers' memory):
+    # each buffer must equal what pack -> exchange -> group produced; reading
+    # the expert outputs in place must give the oracle's combine.
+    torch = require_gpu()
+    import combine_balancing_amd as cba
+    d = synth.make_plan_inputs(name)
+    R, E, S, K, H = d["R"], d["E"], d["S"], d["K"], d["H"]
+    C = S * K
+    ref_plans = [orc.plan(d["topk_ids"], R, E, S, K, m=m) for m in range(R)]
+    ref = orc.chain(d["x_all"], ref_plans, d["scores"], _oracle_expert(orc))
+    note(f"zero-copy chain {name}: plan")
+    p = cba.plan(dev(d["topk_ids"].reshape(-1)), R, E, S, K, my_rank=0)
+    grouped = torch.zeros(R, C, H, dtype=torch.bfloat16, device="cuda")
+    peers = cba.peer_table(grouped)
+    note(f"zero-copy chain {name}: push")
+    for m in range(R):
+        cba.dispatch_to_peers(K, dev(d["x_all"][m]), p["route_dest"][m * C:(m + 1) * C],
+                              p["route_slot"][m * C:(m + 1) * C], peers, C)
+    torch.cuda.synchronize()
+    for r in range(R):
+        assert np.array_equal(host(grouped[r]), ref[r]["recv_grouped"])
+    y = torch.stack([dev(ref[r]["y_grouped"]).view(torch.bfloat16) for r in range(R)])
+    ypeers = cba.peer_table(y)
+    note(f"zero-copy chain {name}: pull")
+    for m in range(R):
+        ob, of = cba.combine_from_peers(ypeers, C, H, p["route_dest"][m * C:(m + 1) * C],
+                                        p["route_slot"][m * C:(m + 1) * C],
+                                        dev(d["scores"][m]), out_bf16=True, out_f32=True)
+        torch.cuda.synchronize()
+        assert np.all(bf16_ulp_diff(host(ob), ref[m]["out_bf16"]) <= 1)
+        rf = ref[m]["out_f32"].astype(np.float64)
+        assert np.all(np.abs(host(of).astype(np.float64) - rf) <= 1e-6 * np.abs(rf) + 1e-30)
+
+
+def test_zero_copy_headline_shape(orc):
+    # rank 0 of the R=8, E=256, S=4096, K=8, H=7168 workload: every pushed
+    # row lands at its (destination, slot); the pull equals the oracle's on
+    # sampled tokens
+    torch = require_gpu()
+    import combine_balancing_amd as cba
+    d = synth.make_plan_inputs("dsv3", stand_ins=False)
+    R, E, S, K, H, C = d["R"], d["E"], d["S"], d["K"], d["H"], d["C"]
+    p = orc.plan(d["topk_ids"], R, E, S, K, m=0)
+    rd, rs = dev(p["route_dest"][:C]), dev(p["route_slot"][:C])
+    grouped = torch.zeros(R, C, H, dtype=torch.bfloat16, device="cuda")
+    note("zero-copy push dsv3")
+    cba.dispatch_to_peers(K, dev(d["x"]), rd, rs, cba.peer_table(grouped), C)
+    torch.cuda.synchronize()
+    g = host(grouped)
+    want = orc.push(d["x"], p["route_dest"][:C], p["route_slot"][:C], K, R, C)
+    assert np.array_equal(g, want)
+    note("zero-copy pull dsv3")
+    gen = torch.Generator(device="cuda")
+    gen.manual_seed(123)
+    y = torch.randn(R, C, H, device="cuda", generator=gen).to(torch.bfloat16)
+    sc = d["scores"][0]
+    ob, of = cba.combine_from_peers(cba.peer_table(y), C, H, rd, rs, dev(sc), out_bf16=True,
+                                    out_f32=True)
+    torch.cuda.synchronize()
+    yh = host(y)
+    rng = np.random.default_rng(7)
+    tok = np.sort(rng.choice(S, 256, replace=False))
+    rb, rf = orc.pull_combine(yh, p["route_dest"][:C].reshape(S, K)[tok],
+                              p["route_slot"][:C].reshape(S, K)[tok], sc[tok])
+    assert np.all(bf16_ulp_diff(host(ob)[tok], rb) <= 1)
+    rf64 = rf.astype(np.float64)
+    mag = np.abs(rf64).max()
+    assert np.all(np.abs(host(of)[tok].astype(np.float64) - rf64) <= 1e-6 * mag)

@@ -124,3 +124,17 @@ def test_plan_rejects_bad_arguments():
     ws = cba.plan_workspace(2, 4, 4, 2)
     with pytest.raises(B.MepError):
         cba.plan(ids, 2, 4, 4, 2, my_rank=0, workspace=ws[:16])
+
+
+@pytest.mark.parametrize("target", [0.2, 20.0])
+def test_plan_skew_sweep(orc, target):
+    # the imbalance sweep's shape (R=8, E=384, S=8192, K=8) at its mildest and
+    # strongest point: every plan output bit-exact
+    require_gpu()
+    d = synth.make_sweep_routing(target)
+    R, E, S, K = d["R"], d["E"], d["S"], d["K"]
+    for m in (0, 5):
+        note(f"plan sweep maxvio={target} m={m}")
+        got = _gpu_plan(d["topk_ids"], R, E, S, K, m)
+        ref = orc.plan(d["topk_ids"], R, E, S, K, m=m)
+        _assert_same(ref, got, f"sweep {target} m={m}")

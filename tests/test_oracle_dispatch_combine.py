@@ -175,3 +175,38 @@ def test_full_chain_over_all_ranks(orc, name):
         # y is rounded to bf16 per route: relative error 2^-8 per term
         tol = (2.0 ** -8 + (K + 2) * U) * np.abs(xm) * (np.abs(sc) * f).sum(axis=1, keepdims=True)
         assert np.all(np.abs(res[m]["out_f32"] - approx) <= tol)
+
+
+def test_ungroup_inverts_group(orc):
+    rng = np.random.default_rng(17)
+    raw = rng.integers(0, 65536, (40, 16)).astype(np.uint16)
+    rp = rng.permutation(40).astype(np.int32)
+    g = orc.group(raw, rp)
+    assert np.array_equal(orc.ungroup(g, rp), raw)
+    ref = np.zeros_like(raw)
+    ref[rp] = raw
+    assert np.array_equal(orc.ungroup(raw, rp), ref)
+
+
+@pytest.mark.parametrize("name", ["tiny", "small"])
+def test_zero_copy_equals_pack_exchange_group(orc, name):
+    # Writing every route's row straight to its (destination, slot) gives,
+    # for every rank, the buffer that pack -> exchange -> group gives; reading
+    # expert outputs in place gives the combine of the returned rows.
+    d = synth.make_plan_inputs(name)
+    R, E, S, K, H = d["R"], d["E"], d["S"], d["K"], d["H"]
+    C = S * K
+    plans = [orc.plan(d["topk_ids"], R, E, S, K, m=m) for m in range(R)]
+    res = orc.chain(d["x_all"], plans, d["scores"], _synthetic_expert(orc))
+    rd, rs = plans[0]["route_dest"], plans[0]["route_slot"]
+    grouped = np.zeros((R, C, H), np.uint16)
+    for m in range(R):
+        orc.push(d["x_all"][m], rd[m * C:(m + 1) * C], rs[m * C:(m + 1) * C], K, R, C, grouped)
+    for r in range(R):
+        assert np.array_equal(grouped[r], res[r]["recv_grouped"])
+    y_grouped = np.stack([res[r]["y_grouped"] for r in range(R)])
+    for m in range(R):
+        ob, of = orc.pull_combine(y_grouped, rd[m * C:(m + 1) * C], rs[m * C:(m + 1) * C],
+                                  d["scores"][m])
+        assert np.array_equal(ob, res[m]["out_bf16"])
+        assert np.array_equal(of, res[m]["out_f32"])

@@ -44,3 +44,9 @@ def test_eplb_inputs():
 def test_bf16_truncation():
     v = np.array([1.0, -2.5, 1.00390625 + 2 ** -10], np.float32)
     assert synth.bf16_from_f32_trunc(v).tolist() == [0x3F80, 0xC020, 0x3F80]
+
+
+def test_sweep_hits_its_targets():
+    # the calibration alone (no full draw): alpha grows with the target
+    a = [synth._sweep_alpha(t, 384, 8, 99, n_cal=2048) for t in (0.2, 1.0, 10.0, 20.0)]
+    assert all(x < y for x, y in zip(a, a[1:]))
