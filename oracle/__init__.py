@@ -28,7 +28,7 @@ def build(verbose: bool = False) -> str:
     src = os.path.join(_HERE, "oracle.c")
     tmp = LIB_PATH + ".tmp"
     cmd = ["gcc", "-std=c99", "-O2", "-ffp-contract=off", "-fno-fast-math",
-           "-Wall", "-Wextra", "-fPIC", "-shared", "-o", tmp, src]
+           "-Wall", "-Wextra", "-fPIC", "-shared", "-o", tmp, src, "-lm"]
     if verbose:
         print(" ".join(cmd))
     subprocess.run(cmd, check=True)
@@ -61,6 +61,9 @@ def _load():
     lib.oracle_pull_combine.restype = I
     lib.oracle_ungroup.argtypes = [I, I, P, P, P]
     lib.oracle_ungroup.restype = I
+    lib.oracle_combine_add_rmsnorm.argtypes = [I, I, I, P, I, P, P, P, P, ctypes.c_double,
+                                               P, P, P, P]
+    lib.oracle_combine_add_rmsnorm.restype = I
     lib.oracle_bf16_from_float.argtypes = [P, P, ctypes.c_int64]
     lib.oracle_bf16_from_float.restype = None
     lib.oracle_float_from_fp16.argtypes = [P, P, ctypes.c_int64]
@@ -243,6 +246,29 @@ def ungroup(y_grouped, recv_pos):
     rp = _c(recv_pos, np.int32).reshape(-1)
     out = np.zeros_like(y)
     _check(lib.oracle_ungroup(rp.size, y.shape[1], _p(rp), _p(y), _p(out)), "oracle_ungroup")
+    return out
+
+
+def combine_add_rmsnorm(y_ret, send_pos, scores, residual, gamma, eps, n_y=None):
+    """Combine + residual add + RMSNorm (oracle_combine_add_rmsnorm).
+    Returns dict(x_out bf16 [T,H], x_f32 [T,H], rstd float64 [T], y float64 [T,H])."""
+    lib = _load()
+    y = _c(y_ret, np.uint16)
+    sc = _c(scores, np.float32)
+    T, K = sc.shape
+    H = y.shape[1]
+    sp = _c(send_pos, np.int32).reshape(-1)
+    res = _c(residual, np.uint16).reshape(T, H)
+    g = _c(gamma, np.uint16).reshape(H)
+    if sp.size != T * K:
+        raise ValueError("send_pos must hold T*K entries")
+    n_y = y.shape[0] if n_y is None else n_y
+    out = {"x_out": np.zeros((T, H), np.uint16), "x_f32": np.zeros((T, H), np.float32),
+           "rstd": np.zeros(T, np.float64), "y": np.zeros((T, H), np.float64)}
+    _check(lib.oracle_combine_add_rmsnorm(T, K, H, _p(y), n_y, _p(sp), _p(sc), _p(res), _p(g),
+                                          float(eps), _p(out["x_out"]), _p(out["x_f32"]),
+                                          _p(out["rstd"]), _p(out["y"])),
+           "oracle_combine_add_rmsnorm")
     return out
 
 

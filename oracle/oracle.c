@@ -28,6 +28,7 @@
  * Build: gcc -O2 -ffp-contract=off -fPIC -shared (no FMA contraction, so
  * every fp32 multiply and add is rounded on its own).
  */
+#include <math.h>
 #include <stdint.h>
 #include <stdlib.h>
 #include <string.h>
@@ -454,6 +455,52 @@ int oracle_combine(int T, int K, int H, const uint16_t* y_ret,
             if (out_f32) out_f32[t * H + h] = acc;
             if (out_bf16) out_bf16[t * H + h] = float_to_bf16_rne(acc);
         }
+    return OR_OK;
+}
+
+/*
+ * oracle_combine_add_rmsnorm: the combine, then a residual add and an RMS
+ * normalisation of the sum ([UpdExp] call example: the combine variant that
+ * also takes the residual x and a gamma vector and returns y, rstd and the
+ * summed x). The pages name those tensors but print no formula; the reading
+ * taken is the usual add + RMSNorm, normalising the unrounded sum:
+ *   a[t,h]  = the fp32 accumulator of oracle_combine (same k order)
+ *   x[t,h]  = fl(a[t,h] + float(residual[t,h]))          fp32, one rounding
+ *   x_out   = round-to-nearest-even bf16 of x
+ *   rstd[t] = 1 / sqrt(sum_h x[t,h]^2 / H + eps)          in fp64
+ *   y[t,h]  = x[t,h] * rstd[t] * float(gamma[h])          in fp64
+ * The squares of fp32 values are exact in fp64, so rstd and y are the
+ * definition up to fp64 rounding. x_f32 may be NULL.
+ */
+int oracle_combine_add_rmsnorm(int T, int K, int H, const uint16_t* y_ret, int n_y,
+                               const int32_t* send_pos, const float* scores,
+                               const uint16_t* residual, const uint16_t* gamma, double eps,
+                               uint16_t* x_out, float* x_f32, double* rstd, double* y) {
+    if (T < 0 || K < 1 || H < 1 || n_y < 0 || !(eps >= 0.0)) return OR_ERR_ARG;
+    float* xs = (float*)malloc(sizeof(float) * (size_t)(H > 0 ? H : 1));
+    if (!xs) return OR_ERR_ALLOC;
+    for (int64_t t = 0; t < T; t++) {
+        double ss = 0.0;
+        for (int64_t h = 0; h < H; h++) {
+            float acc = 0.0f;
+            for (int k = 0; k < K; k++) {
+                int32_t row = send_pos[t * K + k];
+                if (row < 0 || row >= n_y) continue;
+                float prod = scores[t * K + k] * bf16_to_float(y_ret[(int64_t)row * H + h]);
+                acc = acc + prod;
+            }
+            float x = acc + bf16_to_float(residual[t * H + h]);
+            xs[h] = x;
+            ss += (double)x * (double)x;
+            x_out[t * H + h] = float_to_bf16_rne(x);
+            if (x_f32) x_f32[t * H + h] = x;
+        }
+        double r = 1.0 / sqrt(ss / (double)H + eps);
+        rstd[t] = r;
+        for (int64_t h = 0; h < H; h++)
+            y[t * H + h] = (double)xs[h] * r * (double)bf16_to_float(gamma[h]);
+    }
+    free(xs);
     return OR_OK;
 }
 
