@@ -57,6 +57,8 @@ def lib():
     L.mep_combine_from_peers.restype = I
     L.mep_ungroup.argtypes = [I, I, P, P, P, P]
     L.mep_ungroup.restype = I
+    L.mep_combine_add_rmsnorm.argtypes = [I, I, I, P, I, P, P, P, P, ctypes.c_float, P, P, P, P]
+    L.mep_combine_add_rmsnorm.restype = I
     _lib = L
     return L
 
@@ -120,3 +122,9 @@ def mep_combine_from_peers(T, K, H, R, C, peer_bufs, route_dest, route_slot, sco
 
 def mep_ungroup(n, H, recv_pos, y_grouped, y_arrival, stream) -> int:
     return lib().mep_ungroup(n, H, recv_pos, y_grouped, y_arrival, stream)
+
+
+def mep_combine_add_rmsnorm(T, K, H, y_ret, n_y, send_pos, scores, residual, gamma, eps, x_out,
+                            y_out, rstd_out, stream) -> int:
+    return lib().mep_combine_add_rmsnorm(T, K, H, y_ret, n_y, send_pos, scores, residual, gamma,
+                                         eps, x_out, y_out, rstd_out, stream)

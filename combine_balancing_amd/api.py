@@ -265,3 +265,31 @@ def ungroup(y_grouped, recv_pos, y_arrival=None, stream=None):
                        _need(y_arrival, "y_arrival", _BF16_LIKE, n * H), _stream_handle(stream))
     B.check("mep_ungroup", rc)
     return y_arrival
+
+
+def combine_add_rmsnorm(y_ret, send_pos, scores, residual, gamma, eps=1e-6, x_out=True,
+                        y_out=None, rstd_out=True, stream=None):
+    """mep_combine_add_rmsnorm. Returns (y_out, x_out, rstd_out); x_out and
+    rstd_out are None when passed as False."""
+    T, K = scores.shape
+    n_y, H = (0, residual.shape[-1]) if y_ret is None else y_ret.shape
+    dev = scores.device
+    if y_out is None:
+        y_out = torch.empty(T, H, dtype=torch.bfloat16, device=dev)
+    if x_out is True:
+        x_out = torch.empty(T, H, dtype=torch.bfloat16, device=dev)
+    elif x_out is False:
+        x_out = None
+    if rstd_out is True:
+        rstd_out = torch.empty(T, dtype=torch.float32, device=dev)
+    elif rstd_out is False:
+        rstd_out = None
+    rc = B.mep_combine_add_rmsnorm(
+        T, K, H, _opt(y_ret, "y_ret", _BF16_LIKE), n_y,
+        _need(send_pos, "send_pos", torch.int32, T * K),
+        _need(scores, "scores", torch.float32, T * K),
+        _need(residual, "residual", _BF16_LIKE, T * H), _need(gamma, "gamma", _BF16_LIKE, H),
+        float(eps), _opt(x_out, "x_out", _BF16_LIKE, T * H), _need(y_out, "y_out", _BF16_LIKE, T * H),
+        _opt(rstd_out, "rstd_out", torch.float32, T), _stream_handle(stream))
+    B.check("mep_combine_add_rmsnorm", rc)
+    return y_out, x_out, rstd_out

@@ -306,6 +306,34 @@ int mep_combine_from_peers(int T, int K, int H, int R, int C,
 int mep_ungroup(int n, int H, const int32_t* recv_pos, const uint16_t* y_grouped,
                 uint16_t* y_arrival, void* stream);
 
+/*
+ * mep_combine_add_rmsnorm - the combine fused with the residual add and RMS
+ * normalisation that follow it ([UpdExp] call example: the combine variant
+ * taking the residual x and gamma and returning y, rstd and the summed x;
+ * the pages give no formula, the usual add + RMSNorm is computed):
+ *   a[t,h]  = the fp32 accumulator of mep_combine (same k order and skips)
+ *   x[t,h]  = fl(a[t,h] + float(residual[t,h]))
+ *   rstd[t] = 1 / sqrt(sum over h of x[t,h]^2 / H + eps), fp32
+ *   y[t,h]  = fl(fl(x[t,h] * rstd[t]) * float(gamma[h])), bf16 nearest even
+ *   x_out[t,h] = x[t,h] rounded to bf16 nearest even
+ *   y_ret [n_y,H], send_pos [T*K], scores [T*K] as mep_combine;
+ *   residual [T,H] bf16; gamma [H] bf16; eps >= 0;
+ *   outputs: y_out [T,H] bf16 (required), x_out [T,H] bf16 and
+ *   rstd_out [T] fp32 (either may be NULL). Row pointers 16-byte aligned.
+ * x_out is bit-identical to mep_combine's out_bf16 of a + residual; the sum
+ * of squares is reduced in fp32 in a tree order, so rstd and y carry fp32
+ * rounding of that sum (relative error well under 1e-5 for H <= 16384).
+ * Sizes: T >= 0 (0 does nothing), 1 <= K <= 64, 8 <= H <= 16384,
+ * H % 8 == 0, n_y >= 0 (y_ret may be NULL only if n_y == 0).
+ * Errors: MEP_ERR_NULLPTR, MEP_ERR_PARAM (eps negative or not finite),
+ * MEP_ERR_SHAPE, MEP_ERR_HIP.
+ */
+int mep_combine_add_rmsnorm(int T, int K, int H, const uint16_t* y_ret, int n_y,
+                            const int32_t* send_pos, const float* scores,
+                            const uint16_t* residual, const uint16_t* gamma, float eps,
+                            uint16_t* x_out, uint16_t* y_out, float* rstd_out,
+                            void* stream);
+
 #ifdef __cplusplus
 }
 #endif

@@ -34,7 +34,8 @@ def test_header_declares_the_four_entry_points():
     names = _declared()
     for n in ("mep_plan", "mep_remap_prune", "mep_dispatch", "mep_combine",
               "mep_plan_workspace_size", "mep_status_str", "mep_version",
-              "mep_dispatch_to_peers", "mep_combine_from_peers", "mep_ungroup"):
+              "mep_dispatch_to_peers", "mep_combine_from_peers", "mep_ungroup",
+              "mep_combine_add_rmsnorm"):
         assert n in names
 
 
@@ -160,3 +161,15 @@ def test_zero_copy_and_ungroup_validation(B):
     assert U(4, 64, None, 16, 16, None) == B.MEP_ERR_NULLPTR
     assert U(4, 12, 16, 16, 16, None) == B.MEP_ERR_SHAPE
     assert U(-1, 64, 16, 16, 16, None) == B.MEP_ERR_SHAPE
+
+
+def test_combine_add_rmsnorm_validation(B):
+    f = B.mep_combine_add_rmsnorm
+    assert f(0, 2, 64, None, 0, None, None, None, None, 1e-6, None, None, None, None) == B.MEP_OK
+    assert f(4, 2, 64, 16, 4, 16, 16, 16, 16, -1.0, None, 16, None, None) == B.MEP_ERR_PARAM
+    assert f(4, 2, 64, 16, 4, 16, 16, 16, 16, float("nan"), None, 16, None, None) == B.MEP_ERR_PARAM
+    assert f(4, 2, 16392, 16, 4, 16, 16, 16, 16, 1e-6, None, 16, None, None) == B.MEP_ERR_SHAPE
+    assert f(4, 2, 60, 16, 4, 16, 16, 16, 16, 1e-6, None, 16, None, None) == B.MEP_ERR_SHAPE
+    assert f(4, 2, 64, 16, 4, 16, 16, 16, 16, 1e-6, None, None, None, None) == B.MEP_ERR_NULLPTR
+    assert f(4, 2, 64, None, 4, 16, 16, 16, 16, 1e-6, None, 16, None, None) == B.MEP_ERR_NULLPTR
+    assert f(4, 2, 64, 16, 4, 16, 16, 8, 16, 1e-6, None, 16, None, None) == B.MEP_ERR_SHAPE
