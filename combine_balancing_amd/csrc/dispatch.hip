@@ -11,11 +11,15 @@
 // All three kernels move whole bf16 rows and are HBM-bound (no
 // contraction, no MFMA). Every access is a 16-byte vector and consecutive
 // threads touch consecutive vectors of a row, so each wave-wide access is a
-// contiguous 1 KiB segment. Per-row indices and scores are uniform across
-// the threads that use them and come through scalar loads. Outputs are
-// written once and not re-read by these kernels, and inputs are read once,
-// so loads and stores are non-temporal. There is no reuse between
-// work-groups, so the work-group -> XCD assignment does not matter here.
+// contiguous 1 KiB segment. Outputs are written once and not re-read by
+// these kernels, and inputs are read once, so loads and stores are
+// non-temporal. There is no reuse between work-groups, so the
+// work-group -> XCD assignment does not matter here.
+//
+// Launch shapes (measured on MI355X at H=7168): pack and combine are flat,
+// one thread per (token, vector) in 256-thread work-groups, which keeps the
+// most stores (pack) and row loads (combine) in flight; the grouping copy
+// runs one work-group per row, which reaches the read+write copy ceiling.
 #include <algorithm>
 
 #include "rows.h"
@@ -27,36 +31,26 @@ using namespace rows;
 
 // ------------------------------------------------------------------- pack
 // send_buf[send_pos[t*K+k]] = x[t] for each k with 0 <= send_pos < nrows.
-template <int VPL>
-__global__ __launch_bounds__(kPackThreads) void pack_rows(const u32x4* __restrict__ x,
+// One thread per (token, vector): the token's row is read once and stored to
+// each of its K send rows.
+template <int KT>
+__global__ __launch_bounds__(kFlatThreads) void pack_flat(const u32x4* __restrict__ x,
                                                           const int* __restrict__ send_pos,
-                                                          u32x4* __restrict__ send_buf, int T, int K,
-                                                          int nvec, int nrows) {
-    const int t = wave_row();
-    if (t >= T) return;
-    const int lane = lane_id();
-    int my_pos = lane < K ? send_pos[(size_t)t * K + lane] : -1;
-    if ((unsigned)my_pos >= (unsigned)nrows) my_pos = -1;
-    const u32x4* src = x + (size_t)t * nvec;
-    for (int v0 = 0; v0 < nvec; v0 += kWave * VPL) {
-        u32x4 r[VPL];
+                                                          u32x4* __restrict__ send_buf,
+                                                          uint32_t total, int K, int nrows,
+                                                          FastDiv rowdiv) {
+    const uint32_t i = blockIdx.x * kFlatThreads + threadIdx.x;
+    if (i >= total) return;
+    const uint32_t t = fast_div(i, rowdiv);
+    const uint32_t v = i - t * rowdiv.d;
+    const int kk = KT > 0 ? KT : K;
+    const int* sp = send_pos + (size_t)t * kk;
+    const u32x4 w = __builtin_nontemporal_load(x + i);
 #pragma unroll
-        for (int i = 0; i < VPL; ++i) {
-            const int v = v0 + i * kWave + lane;
-            if (v < nvec) r[i] = __builtin_nontemporal_load(src + v);
-        }
-        // each route's position is read across lanes with the whole wave
-        // active, then is wave-uniform
-        for (int k = 0; k < K; ++k) {
-            const int pos = __builtin_amdgcn_readlane(my_pos, k);
-            if (pos < 0) continue;
-            u32x4* dst = send_buf + (size_t)pos * nvec;
-#pragma unroll
-            for (int i = 0; i < VPL; ++i) {
-                const int v = v0 + i * kWave + lane;
-                if (v < nvec) __builtin_nontemporal_store(r[i], dst + v);
-            }
-        }
+    for (int k = 0; k < kk; ++k) {
+        const int p = sp[k];
+        if ((unsigned)p < (unsigned)nrows)
+            __builtin_nontemporal_store(w, send_buf + (size_t)p * rowdiv.d + v);
     }
 }
 
@@ -93,23 +87,21 @@ __global__ __launch_bounds__(kMaxTpr) void group_rows(const u32x4* __restrict__ 
 
 // ---------------------------------------------------------------- combine
 // acc = +0; for k in order: acc = acc + score_k * y[pos_k] (each op rounded
-// to fp32: built without FMA contraction). One work-group per token (rpb
-// tokens per group for small rows); each thread owns VPT vectors and keeps
-// their K loads in flight together.
-template <int KT, int VPT>
-__global__ __launch_bounds__(kCombineThreads) void combine_rows(const u32x4* __restrict__ y, int n_y,
-                                                                const int* __restrict__ send_pos,
-                                                                const float* __restrict__ scores,
-                                                                u32x4* __restrict__ out_bf16,
-                                                                f32x4* __restrict__ out_f32, int T,
-                                                                int nvec, int tpr, int rpb) {
-    const int r = threadIdx.x / tpr;
-    const int tid = threadIdx.x - r * tpr;
-    const int t = blockIdx.x * rpb + r;
-    if (t >= T) return;
-    // Skipped routes (negative or out-of-range rows) still load row 0 so that
-    // all K loads issue together; their terms are then left out exactly.
-    int pos[KT];
+// to fp32: built without FMA contraction). One thread per (token, vector)
+// with its K loads in flight together; skipped routes load row 0 and are
+// left out exactly.
+template <int KT>
+__global__ __launch_bounds__(kFlatThreads) void combine_flat(const u32x4* __restrict__ y, int n_y,
+                                                             const int* __restrict__ send_pos,
+                                                             const float* __restrict__ scores,
+                                                             u32x4* __restrict__ out_bf16,
+                                                             f32x4* __restrict__ out_f32,
+                                                             uint32_t total, FastDiv rowdiv) {
+    const uint32_t i = blockIdx.x * kFlatThreads + threadIdx.x;
+    if (i >= total) return;
+    const uint32_t t = fast_div(i, rowdiv);
+    const uint32_t v = i - t * rowdiv.d;
+    u32x4 yk[KT];
     float sc[KT];
     uint32_t use = 0;
 #pragma unroll
@@ -117,63 +109,41 @@ __global__ __launch_bounds__(kCombineThreads) void combine_rows(const u32x4* __r
         const int p = send_pos[(size_t)t * KT + k];
         const bool ok = (unsigned)p < (unsigned)n_y;
         use |= (uint32_t)ok << k;
-        pos[k] = ok ? p : 0;
+        yk[k] = __builtin_nontemporal_load(y + (size_t)(ok ? p : 0) * rowdiv.d + v);
         sc[k] = scores[(size_t)t * KT + k];
     }
-    for (int v0 = 0; v0 < nvec; v0 += tpr * VPT) {
-        u32x4 yk[VPT][KT];
+    float acc[8];
 #pragma unroll
-        for (int i = 0; i < VPT; ++i) {
-            const int v = min(v0 + i * tpr + tid, nvec - 1);
+    for (int j = 0; j < 8; ++j) acc[j] = 0.0f;
 #pragma unroll
-            for (int k = 0; k < KT; ++k)
-                yk[i][k] = __builtin_nontemporal_load(y + (size_t)pos[k] * nvec + v);
-        }
-#pragma unroll
-        for (int i = 0; i < VPT; ++i) {
-            const int v = v0 + i * tpr + tid;
-            float acc[8];
-#pragma unroll
-            for (int j = 0; j < 8; ++j) acc[j] = 0.0f;
-#pragma unroll
-            for (int k = 0; k < KT; ++k)
-                if ((use >> k) & 1u) accumulate(acc, yk[i][k], sc[k]);
-            if (v < nvec) store_out(acc, out_bf16, out_f32, (size_t)t * nvec + v);
-        }
-    }
+    for (int k = 0; k < KT; ++k)
+        if ((use >> k) & 1u) accumulate(acc, yk[k], sc[k]);
+    store_out(acc, out_bf16, out_f32, i);
 }
 
-// Any K up to 64: one route at a time, in k order.
-__global__ __launch_bounds__(kCombineThreads) void combine_rows_any(
+// Any K up to 64 (and the case with no rows to read): one route at a time,
+// in k order, loading only valid routes.
+__global__ __launch_bounds__(kFlatThreads) void combine_flat_any(
     const u32x4* __restrict__ y, int n_y, const int* __restrict__ send_pos,
     const float* __restrict__ scores, u32x4* __restrict__ out_bf16, f32x4* __restrict__ out_f32,
-    int T, int K, int nvec, int tpr, int rpb) {
-    const int r = threadIdx.x / tpr;
-    const int tid = threadIdx.x - r * tpr;
-    const int t = blockIdx.x * rpb + r;
-    if (t >= T) return;
-    for (int v = tid; v < nvec; v += tpr) {
-        float acc[8];
+    uint32_t total, int K, FastDiv rowdiv) {
+    const uint32_t i = blockIdx.x * kFlatThreads + threadIdx.x;
+    if (i >= total) return;
+    const uint32_t t = fast_div(i, rowdiv);
+    const uint32_t v = i - t * rowdiv.d;
+    float acc[8];
 #pragma unroll
-        for (int j = 0; j < 8; ++j) acc[j] = 0.0f;
-        for (int k = 0; k < K; ++k) {
-            const int p = send_pos[(size_t)t * K + k];
-            if ((unsigned)p >= (unsigned)n_y) continue;
-            accumulate(acc, y[(size_t)p * nvec + v], scores[(size_t)t * K + k]);
-        }
-        store_out(acc, out_bf16, out_f32, (size_t)t * nvec + v);
+    for (int j = 0; j < 8; ++j) acc[j] = 0.0f;
+    for (int k = 0; k < K; ++k) {
+        const int p = send_pos[(size_t)t * K + k];
+        if ((unsigned)p >= (unsigned)n_y) continue;
+        accumulate(acc, __builtin_nontemporal_load(y + (size_t)p * rowdiv.d + v),
+                   scores[(size_t)t * K + k]);
     }
+    store_out(acc, out_bf16, out_f32, i);
 }
 
 // ------------------------------------------------------------------- host
-template <int VPL>
-void launch_pack(hipStream_t s, const u32x4* x, const int* sp, u32x4* buf, int T, int K,
-                 int nvec, int nrows) {
-    const dim3 g((T + kPackRows - 1) / kPackRows);
-    hipLaunchKernelGGL(pack_rows<VPL>, g, dim3(kPackThreads), 0, s, x, sp, buf, T, K, nvec,
-                       nrows);
-}
-
 void launch_group(hipStream_t s, const u32x4* raw, const int* rp, u32x4* out, int n, int nvec) {
     // one vector per thread up to 1024 vectors (16 KiB rows), then 2, 4, 8
     int vpt = 1;
@@ -188,20 +158,11 @@ void launch_group(hipStream_t s, const u32x4* raw, const int* rp, u32x4* out, in
     }
 }
 
-// Vectors per thread in combine: about 32 row loads in flight per thread.
-template <int KT>
-constexpr int combine_vpt() {
-    return KT > 8 ? 2 : 4;
-}
-
 template <int KT>
 void launch_combine(hipStream_t s, const u32x4* y, int n_y, const int* sp, const float* sc,
-                    u32x4* ob, f32x4* of, int T, int nvec) {
-    constexpr int VPT = combine_vpt<KT>();
-    const RowShape rs = row_shape(nvec, VPT, kCombineThreads);
-    const dim3 g((T + rs.rpb - 1) / rs.rpb), b(rs.tpr * rs.rpb);
-    hipLaunchKernelGGL((combine_rows<KT, VPT>), g, b, 0, s, y, n_y, sp, sc, ob, of, T, nvec,
-                       rs.tpr, rs.rpb);
+                    u32x4* ob, f32x4* of, uint32_t total, FastDiv dv) {
+    hipLaunchKernelGGL(combine_flat<KT>, dim3((total + kFlatThreads - 1) / kFlatThreads),
+                       dim3(kFlatThreads), 0, s, y, n_y, sp, sc, ob, of, total, dv);
 }
 
 }  // namespace
@@ -218,7 +179,8 @@ extern "C" int mep_dispatch(int T, int K, int H, const uint16_t* x, const int32_
     if (do_pack && (!send_pos || !send_buf)) return MEP_ERR_NULLPTR;
     if (do_group && (!recv_pos || !recv_grouped)) return MEP_ERR_NULLPTR;
     if (H < 8 || H > 65536 || (H % 8) != 0) return MEP_ERR_SHAPE;
-    if (do_pack && (T < 0 || K < 1 || K > 64 || (long long)T * K >= (1ll << 31)))
+    if (do_pack && (T < 0 || K < 1 || K > 64 || (long long)T * K >= (1ll << 31) ||
+                    !flat_fits(T, H / 8)))
         return MEP_ERR_SHAPE;
     if (do_group && n_recv < 0) return MEP_ERR_SHAPE;
     if (do_pack && (!aligned16(x) || !aligned16(send_buf))) return MEP_ERR_SHAPE;
@@ -226,9 +188,21 @@ extern "C" int mep_dispatch(int T, int K, int H, const uint16_t* x, const int32_
     hipStream_t s = (hipStream_t)stream;
     const int nvec = H / 8;
     if (do_pack && T > 0) {
-        const int vpl = std::min(kMaxVpl, std::max(1, (nvec + kWave - 1) / kWave));
-        MEP_VPL_SWITCH(vpl, launch_pack, s, (const u32x4*)x, (const int*)send_pos,
-                       (u32x4*)send_buf, T, K, nvec, T * K);
+        const uint32_t total = (uint32_t)T * (uint32_t)nvec;
+        const dim3 g((total + kFlatThreads - 1) / kFlatThreads), b(kFlatThreads);
+        const FastDiv dv = make_fastdiv((uint32_t)nvec);
+        const u32x4* xv = (const u32x4*)x;
+        const int* sp = (const int*)send_pos;
+        u32x4* buf = (u32x4*)send_buf;
+        switch (K) {
+            case 1: hipLaunchKernelGGL(pack_flat<1>, g, b, 0, s, xv, sp, buf, total, K, T * K, dv); break;
+            case 2: hipLaunchKernelGGL(pack_flat<2>, g, b, 0, s, xv, sp, buf, total, K, T * K, dv); break;
+            case 4: hipLaunchKernelGGL(pack_flat<4>, g, b, 0, s, xv, sp, buf, total, K, T * K, dv); break;
+            case 6: hipLaunchKernelGGL(pack_flat<6>, g, b, 0, s, xv, sp, buf, total, K, T * K, dv); break;
+            case 8: hipLaunchKernelGGL(pack_flat<8>, g, b, 0, s, xv, sp, buf, total, K, T * K, dv); break;
+            case 16: hipLaunchKernelGGL(pack_flat<16>, g, b, 0, s, xv, sp, buf, total, K, T * K, dv); break;
+            default: hipLaunchKernelGGL(pack_flat<0>, g, b, 0, s, xv, sp, buf, total, K, T * K, dv); break;
+        }
         MEP_LAUNCH_CHECK();
     }
     if (do_group && n_recv > 0) {
@@ -247,7 +221,7 @@ extern "C" int mep_combine(int T, int K, int H, const uint16_t* y_ret, int n_y,
     if (T == 0) return MEP_OK;  // nothing to do; empty buffers may be NULL
     if (!y_ret || !send_pos || !scores) return MEP_ERR_NULLPTR;
     if (!out_bf16 && !out_f32) return MEP_ERR_NULLPTR;
-    if ((long long)T * K >= (1ll << 31)) return MEP_ERR_SHAPE;
+    if ((long long)T * K >= (1ll << 31) || !flat_fits(T, H / 8)) return MEP_ERR_SHAPE;
     if (!aligned16(y_ret) || (out_bf16 && !aligned16(out_bf16)) || (out_f32 && !aligned16(out_f32)))
         return MEP_ERR_SHAPE;
     hipStream_t s = (hipStream_t)stream;
@@ -256,30 +230,30 @@ extern "C" int mep_combine(int T, int K, int H, const uint16_t* y_ret, int n_y,
     const int* sp = (const int*)send_pos;
     u32x4* ob = (u32x4*)out_bf16;
     f32x4* of = (f32x4*)out_f32;
+    const uint32_t total = (uint32_t)T * (uint32_t)nvec;
+    const FastDiv dv = make_fastdiv((uint32_t)nvec);
+    // with no rows to read, the generic kernel (which loads valid routes only)
     switch (n_y > 0 ? K : 0) {
-        case 1: launch_combine<1>(s, y, n_y, sp, scores, ob, of, T, nvec); break;
-        case 2: launch_combine<2>(s, y, n_y, sp, scores, ob, of, T, nvec); break;
-        case 3: launch_combine<3>(s, y, n_y, sp, scores, ob, of, T, nvec); break;
-        case 4: launch_combine<4>(s, y, n_y, sp, scores, ob, of, T, nvec); break;
-        case 5: launch_combine<5>(s, y, n_y, sp, scores, ob, of, T, nvec); break;
-        case 6: launch_combine<6>(s, y, n_y, sp, scores, ob, of, T, nvec); break;
-        case 7: launch_combine<7>(s, y, n_y, sp, scores, ob, of, T, nvec); break;
-        case 8: launch_combine<8>(s, y, n_y, sp, scores, ob, of, T, nvec); break;
-        case 9: launch_combine<9>(s, y, n_y, sp, scores, ob, of, T, nvec); break;
-        case 10: launch_combine<10>(s, y, n_y, sp, scores, ob, of, T, nvec); break;
-        case 11: launch_combine<11>(s, y, n_y, sp, scores, ob, of, T, nvec); break;
-        case 12: launch_combine<12>(s, y, n_y, sp, scores, ob, of, T, nvec); break;
-        case 13: launch_combine<13>(s, y, n_y, sp, scores, ob, of, T, nvec); break;
-        case 14: launch_combine<14>(s, y, n_y, sp, scores, ob, of, T, nvec); break;
-        case 15: launch_combine<15>(s, y, n_y, sp, scores, ob, of, T, nvec); break;
-        case 16: launch_combine<16>(s, y, n_y, sp, scores, ob, of, T, nvec); break;
-        default: {
-            const RowShape rs = row_shape(nvec, 1, kCombineThreads);
-            hipLaunchKernelGGL(combine_rows_any, dim3((T + rs.rpb - 1) / rs.rpb),
-                               dim3(rs.tpr * rs.rpb), 0, s, y, n_y, sp, scores, ob, of, T, K,
-                               nvec, rs.tpr, rs.rpb);
+        case 1: launch_combine<1>(s, y, n_y, sp, scores, ob, of, total, dv); break;
+        case 2: launch_combine<2>(s, y, n_y, sp, scores, ob, of, total, dv); break;
+        case 3: launch_combine<3>(s, y, n_y, sp, scores, ob, of, total, dv); break;
+        case 4: launch_combine<4>(s, y, n_y, sp, scores, ob, of, total, dv); break;
+        case 5: launch_combine<5>(s, y, n_y, sp, scores, ob, of, total, dv); break;
+        case 6: launch_combine<6>(s, y, n_y, sp, scores, ob, of, total, dv); break;
+        case 7: launch_combine<7>(s, y, n_y, sp, scores, ob, of, total, dv); break;
+        case 8: launch_combine<8>(s, y, n_y, sp, scores, ob, of, total, dv); break;
+        case 9: launch_combine<9>(s, y, n_y, sp, scores, ob, of, total, dv); break;
+        case 10: launch_combine<10>(s, y, n_y, sp, scores, ob, of, total, dv); break;
+        case 11: launch_combine<11>(s, y, n_y, sp, scores, ob, of, total, dv); break;
+        case 12: launch_combine<12>(s, y, n_y, sp, scores, ob, of, total, dv); break;
+        case 13: launch_combine<13>(s, y, n_y, sp, scores, ob, of, total, dv); break;
+        case 14: launch_combine<14>(s, y, n_y, sp, scores, ob, of, total, dv); break;
+        case 15: launch_combine<15>(s, y, n_y, sp, scores, ob, of, total, dv); break;
+        case 16: launch_combine<16>(s, y, n_y, sp, scores, ob, of, total, dv); break;
+        default:
+            hipLaunchKernelGGL(combine_flat_any, dim3((total + kFlatThreads - 1) / kFlatThreads),
+                               dim3(kFlatThreads), 0, s, y, n_y, sp, scores, ob, of, total, K, dv);
             break;
-        }
     }
     MEP_LAUNCH_CHECK();
     return MEP_OK;

@@ -14,9 +14,9 @@
 // slices of one allocation). mep_ungroup is the return step of the
 // non-zero-copy path: grouped expert outputs back to arrival order.
 //
-// Kernel shapes follow the pack and combine kernels (one wave per token for
-// the push, one work-group per token for the pull, one work-group per row for
-// the ungroup); all three are HBM-bound row movers.
+// Kernel shapes follow the pack, combine and grouping kernels (flat, one
+// thread per (token, vector), for the push and the pull; one work-group per
+// row for the ungroup); all three are HBM-bound row movers.
 #include <algorithm>
 
 #include "rows.h"
@@ -26,65 +26,44 @@ namespace {
 
 using namespace rows;
 
-__device__ __forceinline__ const u32x4* read_ptr_lane(const u32x4* p, int lane) {
-    const uint64_t v = (uint64_t)(uintptr_t)p;
-    const uint32_t lo = __builtin_amdgcn_readlane((uint32_t)v, lane);
-    const uint32_t hi = __builtin_amdgcn_readlane((uint32_t)(v >> 32), lane);
-    return (const u32x4*)(uintptr_t)(((uint64_t)hi << 32) | lo);
-}
-
 // peers[route_dest[t*K+k]][route_slot[t*K+k]] = x[t] for every valid route.
-template <int VPL>
-__global__ __launch_bounds__(kPackThreads) void push_rows(const u32x4* __restrict__ x,
+// One thread per (token, vector), as the pack: the row is read once and
+// stored to each of the K destinations.
+template <int KT>
+__global__ __launch_bounds__(kFlatThreads) void push_flat(const u32x4* __restrict__ x,
                                                           const int* __restrict__ rdest,
                                                           const int* __restrict__ rslot,
-                                                          u32x4* const* __restrict__ peers, int T,
-                                                          int K, int nvec, int R, int C) {
-    const int t = wave_row();
-    if (t >= T) return;
-    const int lane = lane_id();
-    const u32x4* dst = nullptr;  // this lane's route (lane k < K)
-    if (lane < K) {
-        const int d = rdest[(size_t)t * K + lane];
-        const int sl = rslot[(size_t)t * K + lane];
+                                                          u32x4* const* __restrict__ peers,
+                                                          uint32_t total, int K, int R, int C,
+                                                          FastDiv rowdiv) {
+    const uint32_t i = blockIdx.x * kFlatThreads + threadIdx.x;
+    if (i >= total) return;
+    const uint32_t t = fast_div(i, rowdiv);
+    const uint32_t v = i - t * rowdiv.d;
+    const int kk = KT > 0 ? KT : K;
+    const u32x4 w = __builtin_nontemporal_load(x + i);
+#pragma unroll
+    for (int k = 0; k < kk; ++k) {
+        const int d = rdest[(size_t)t * kk + k];
+        const int sl = rslot[(size_t)t * kk + k];
         if ((unsigned)d < (unsigned)R && (unsigned)sl < (unsigned)C)
-            dst = peers[d] + (size_t)sl * nvec;
-    }
-    const u32x4* src = x + (size_t)t * nvec;
-    for (int v0 = 0; v0 < nvec; v0 += kWave * VPL) {
-        u32x4 r[VPL];
-#pragma unroll
-        for (int i = 0; i < VPL; ++i) {
-            const int v = v0 + i * kWave + lane;
-            if (v < nvec) r[i] = __builtin_nontemporal_load(src + v);
-        }
-        // the K destinations are read across lanes with the whole wave
-        // active; each is then wave-uniform
-        for (int k = 0; k < K; ++k) {
-            u32x4* p = (u32x4*)read_ptr_lane(dst, k);
-            if (!p) continue;
-#pragma unroll
-            for (int i = 0; i < VPL; ++i) {
-                const int v = v0 + i * kWave + lane;
-                if (v < nvec) __builtin_nontemporal_store(r[i], p + v);
-            }
-        }
+            __builtin_nontemporal_store(w, peers[d] + (size_t)sl * rowdiv.d + v);
     }
 }
 
 // out[t] = sum over k in order of score * peers[dest][slot], fp32, from +0.
-template <int KT, int VPT>
-__global__ __launch_bounds__(kCombineThreads) void pull_combine(
+// One thread per (token, vector) with its K loads in flight together;
+// skipped routes read row 0 of rank 0's buffer and are left out exactly.
+template <int KT>
+__global__ __launch_bounds__(kFlatThreads) void pull_flat(
     const u32x4* const* __restrict__ peers, const int* __restrict__ rdest,
     const int* __restrict__ rslot, const float* __restrict__ scores, u32x4* __restrict__ out_bf16,
-    f32x4* __restrict__ out_f32, int T, int nvec, int R, int C, int tpr, int rpb) {
-    const int r = threadIdx.x / tpr;
-    const int tid = threadIdx.x - r * tpr;
-    const int t = blockIdx.x * rpb + r;
-    if (t >= T) return;
-    // skipped routes read row 0 of rank 0's buffer so that all K loads issue
-    // together; their terms are left out exactly
-    const u32x4* src[KT];
+    f32x4* __restrict__ out_f32, uint32_t total, int R, int C, FastDiv rowdiv) {
+    const uint32_t i = blockIdx.x * kFlatThreads + threadIdx.x;
+    if (i >= total) return;
+    const uint32_t t = fast_div(i, rowdiv);
+    const uint32_t v = i - t * rowdiv.d;
+    u32x4 yk[KT];
     float sc[KT];
     uint32_t use = 0;
 #pragma unroll
@@ -93,52 +72,39 @@ __global__ __launch_bounds__(kCombineThreads) void pull_combine(
         const int sl = rslot[(size_t)t * KT + k];
         const bool ok = (unsigned)d < (unsigned)R && (unsigned)sl < (unsigned)C;
         use |= (uint32_t)ok << k;
-        src[k] = ok ? peers[d] + (size_t)sl * nvec : peers[0];
+        const u32x4* src = ok ? peers[d] + (size_t)sl * rowdiv.d : peers[0];
+        yk[k] = __builtin_nontemporal_load(src + v);
         sc[k] = scores[(size_t)t * KT + k];
     }
-    for (int v0 = 0; v0 < nvec; v0 += tpr * VPT) {
-        u32x4 yk[VPT][KT];
+    float acc[8];
 #pragma unroll
-        for (int i = 0; i < VPT; ++i) {
-            const int v = min(v0 + i * tpr + tid, nvec - 1);
+    for (int j = 0; j < 8; ++j) acc[j] = 0.0f;
 #pragma unroll
-            for (int k = 0; k < KT; ++k) yk[i][k] = __builtin_nontemporal_load(src[k] + v);
-        }
-#pragma unroll
-        for (int i = 0; i < VPT; ++i) {
-            const int v = v0 + i * tpr + tid;
-            float acc[8];
-#pragma unroll
-            for (int j = 0; j < 8; ++j) acc[j] = 0.0f;
-#pragma unroll
-            for (int k = 0; k < KT; ++k)
-                if ((use >> k) & 1u) accumulate(acc, yk[i][k], sc[k]);
-            if (v < nvec) store_out(acc, out_bf16, out_f32, (size_t)t * nvec + v);
-        }
-    }
+    for (int k = 0; k < KT; ++k)
+        if ((use >> k) & 1u) accumulate(acc, yk[k], sc[k]);
+    store_out(acc, out_bf16, out_f32, i);
 }
 
-// Any K up to 64: one route at a time, in k order.
-__global__ __launch_bounds__(kCombineThreads) void pull_combine_any(
+// Any K up to 64: one route at a time, in k order, loading valid routes only.
+__global__ __launch_bounds__(kFlatThreads) void pull_flat_any(
     const u32x4* const* __restrict__ peers, const int* __restrict__ rdest,
     const int* __restrict__ rslot, const float* __restrict__ scores, u32x4* __restrict__ out_bf16,
-    f32x4* __restrict__ out_f32, int T, int K, int nvec, int R, int C, int tpr, int rpb) {
-    const int r = threadIdx.x / tpr;
-    const int tid = threadIdx.x - r * tpr;
-    const int t = blockIdx.x * rpb + r;
-    if (t >= T) return;
-    for (int v = tid; v < nvec; v += tpr) {
-        float acc[8];
+    f32x4* __restrict__ out_f32, uint32_t total, int K, int R, int C, FastDiv rowdiv) {
+    const uint32_t i = blockIdx.x * kFlatThreads + threadIdx.x;
+    if (i >= total) return;
+    const uint32_t t = fast_div(i, rowdiv);
+    const uint32_t v = i - t * rowdiv.d;
+    float acc[8];
 #pragma unroll
-        for (int j = 0; j < 8; ++j) acc[j] = 0.0f;
-        for (int k = 0; k < K; ++k) {
-            const int d = rdest[(size_t)t * K + k];
-            const int sl = rslot[(size_t)t * K + k];
-            if ((unsigned)d >= (unsigned)R || (unsigned)sl >= (unsigned)C) continue;
-            accumulate(acc, peers[d][(size_t)sl * nvec + v], scores[(size_t)t * K + k]);
-        }
-        store_out(acc, out_bf16, out_f32, (size_t)t * nvec + v);
+    for (int j = 0; j < 8; ++j) acc[j] = 0.0f;
+    for (int k = 0; k < K; ++k) {
+        const int d = rdest[(size_t)t * K + k];
+        const int sl = rslot[(size_t)t * K + k];
+        if ((unsigned)d >= (unsigned)R || (unsigned)sl >= (unsigned)C) continue;
+        accumulate(acc, __builtin_nontemporal_load(peers[d] + (size_t)sl * rowdiv.d + v),
+                   scores[(size_t)t * K + k]);
     }
+    store_out(acc, out_bf16, out_f32, i);
 }
 
 // y_arrival[recv_pos[t]] = y_grouped[t]: the inverse of the grouping.
@@ -170,22 +136,12 @@ __global__ __launch_bounds__(kMaxTpr) void ungroup_rows(const u32x4* __restrict_
     }
 }
 
-template <int VPL>
-void launch_push(hipStream_t s, const u32x4* x, const int* rd, const int* rs, u32x4* const* peers,
-                 int T, int K, int nvec, int R, int C) {
-    const dim3 g((T + kPackRows - 1) / kPackRows);
-    hipLaunchKernelGGL(push_rows<VPL>, g, dim3(kPackThreads), 0, s, x, rd, rs, peers, T, K, nvec,
-                       R, C);
-}
-
 template <int KT>
 void launch_pull(hipStream_t s, const u32x4* const* peers, const int* rd, const int* rs,
-                 const float* sc, u32x4* ob, f32x4* of, int T, int nvec, int R, int C) {
-    constexpr int VPT = KT > 8 ? 2 : 4;
-    const RowShape rsh = row_shape(nvec, VPT, kCombineThreads);
-    const dim3 g((T + rsh.rpb - 1) / rsh.rpb), b(rsh.tpr * rsh.rpb);
-    hipLaunchKernelGGL((pull_combine<KT, VPT>), g, b, 0, s, peers, rd, rs, sc, ob, of, T, nvec, R,
-                       C, rsh.tpr, rsh.rpb);
+                 const float* sc, u32x4* ob, f32x4* of, uint32_t total, int R, int C,
+                 FastDiv dv) {
+    hipLaunchKernelGGL(pull_flat<KT>, dim3((total + kFlatThreads - 1) / kFlatThreads),
+                       dim3(kFlatThreads), 0, s, peers, rd, rs, sc, ob, of, total, R, C, dv);
 }
 
 }  // namespace
@@ -198,16 +154,28 @@ extern "C" int mep_dispatch_to_peers(int T, int K, int H, int R, int C, const ui
                                      const int32_t* route_dest, const int32_t* route_slot,
                                      uint16_t* const* peer_bufs, void* stream) {
     if (T < 0 || K < 1 || K > 64 || H < 8 || H > 65536 || (H % 8) != 0 || R < 1 || C < 1 ||
-        (long long)T * K >= (1ll << 31))
+        (long long)T * K >= (1ll << 31) || !flat_fits(T, H / 8))
         return MEP_ERR_SHAPE;
     if (T == 0) return MEP_OK;
     if (!x || !route_dest || !route_slot || !peer_bufs) return MEP_ERR_NULLPTR;
     if (!aligned16(x)) return MEP_ERR_SHAPE;
-    const int nvec = H / 8;
-    const int vpl = std::min(kMaxVpl, std::max(1, (nvec + kWave - 1) / kWave));
-    MEP_VPL_SWITCH(vpl, launch_push, (hipStream_t)stream, (const u32x4*)x,
-                   (const int*)route_dest, (const int*)route_slot, (u32x4* const*)peer_bufs, T, K,
-                   nvec, R, C);
+    const uint32_t total = (uint32_t)T * (uint32_t)(H / 8);
+    const dim3 g((total + kFlatThreads - 1) / kFlatThreads), b(kFlatThreads);
+    const FastDiv dv = make_fastdiv((uint32_t)(H / 8));
+    hipStream_t s = (hipStream_t)stream;
+    const u32x4* xv = (const u32x4*)x;
+    const int* rd = (const int*)route_dest;
+    const int* rs = (const int*)route_slot;
+    u32x4* const* p = (u32x4* const*)peer_bufs;
+    switch (K) {
+        case 1: hipLaunchKernelGGL(push_flat<1>, g, b, 0, s, xv, rd, rs, p, total, K, R, C, dv); break;
+        case 2: hipLaunchKernelGGL(push_flat<2>, g, b, 0, s, xv, rd, rs, p, total, K, R, C, dv); break;
+        case 4: hipLaunchKernelGGL(push_flat<4>, g, b, 0, s, xv, rd, rs, p, total, K, R, C, dv); break;
+        case 6: hipLaunchKernelGGL(push_flat<6>, g, b, 0, s, xv, rd, rs, p, total, K, R, C, dv); break;
+        case 8: hipLaunchKernelGGL(push_flat<8>, g, b, 0, s, xv, rd, rs, p, total, K, R, C, dv); break;
+        case 16: hipLaunchKernelGGL(push_flat<16>, g, b, 0, s, xv, rd, rs, p, total, K, R, C, dv); break;
+        default: hipLaunchKernelGGL(push_flat<0>, g, b, 0, s, xv, rd, rs, p, total, K, R, C, dv); break;
+    }
     MEP_LAUNCH_CHECK();
     return MEP_OK;
 }
@@ -218,33 +186,32 @@ extern "C" int mep_combine_from_peers(int T, int K, int H, int R, int C,
                                       const float* scores, uint16_t* out_bf16, float* out_f32,
                                       void* stream) {
     if (T < 0 || K < 1 || K > 64 || H < 8 || H > 65536 || (H % 8) != 0 || R < 1 || C < 1 ||
-        (long long)T * K >= (1ll << 31))
+        (long long)T * K >= (1ll << 31) || !flat_fits(T, H / 8))
         return MEP_ERR_SHAPE;
     if (T == 0) return MEP_OK;
     if (!peer_bufs || !route_dest || !route_slot || !scores) return MEP_ERR_NULLPTR;
     if (!out_bf16 && !out_f32) return MEP_ERR_NULLPTR;
     if ((out_bf16 && !aligned16(out_bf16)) || (out_f32 && !aligned16(out_f32))) return MEP_ERR_SHAPE;
     hipStream_t s = (hipStream_t)stream;
-    const int nvec = H / 8;
     const u32x4* const* p = (const u32x4* const*)peer_bufs;
     const int* rd = (const int*)route_dest;
     const int* rs = (const int*)route_slot;
     u32x4* ob = (u32x4*)out_bf16;
     f32x4* of = (f32x4*)out_f32;
+    const uint32_t total = (uint32_t)T * (uint32_t)(H / 8);
+    const FastDiv dv = make_fastdiv((uint32_t)(H / 8));
     switch (K) {
-        case 1: launch_pull<1>(s, p, rd, rs, scores, ob, of, T, nvec, R, C); break;
-        case 2: launch_pull<2>(s, p, rd, rs, scores, ob, of, T, nvec, R, C); break;
-        case 4: launch_pull<4>(s, p, rd, rs, scores, ob, of, T, nvec, R, C); break;
-        case 6: launch_pull<6>(s, p, rd, rs, scores, ob, of, T, nvec, R, C); break;
-        case 8: launch_pull<8>(s, p, rd, rs, scores, ob, of, T, nvec, R, C); break;
-        case 16: launch_pull<16>(s, p, rd, rs, scores, ob, of, T, nvec, R, C); break;
-        default: {
-            const RowShape rsh = row_shape(nvec, 1, kCombineThreads);
-            hipLaunchKernelGGL(pull_combine_any, dim3((T + rsh.rpb - 1) / rsh.rpb),
-                               dim3(rsh.tpr * rsh.rpb), 0, s, p, rd, rs, scores, ob, of, T, K,
-                               nvec, R, C, rsh.tpr, rsh.rpb);
+        case 1: launch_pull<1>(s, p, rd, rs, scores, ob, of, total, R, C, dv); break;
+        case 2: launch_pull<2>(s, p, rd, rs, scores, ob, of, total, R, C, dv); break;
+        case 4: launch_pull<4>(s, p, rd, rs, scores, ob, of, total, R, C, dv); break;
+        case 6: launch_pull<6>(s, p, rd, rs, scores, ob, of, total, R, C, dv); break;
+        case 8: launch_pull<8>(s, p, rd, rs, scores, ob, of, total, R, C, dv); break;
+        case 16: launch_pull<16>(s, p, rd, rs, scores, ob, of, total, R, C, dv); break;
+        default:
+            hipLaunchKernelGGL(pull_flat_any, dim3((total + kFlatThreads - 1) / kFlatThreads),
+                               dim3(kFlatThreads), 0, s, p, rd, rs, scores, ob, of, total, K, R,
+                               C, dv);
             break;
-        }
     }
     MEP_LAUNCH_CHECK();
     return MEP_OK;

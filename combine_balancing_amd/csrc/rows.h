@@ -10,21 +10,10 @@ namespace rows {
 typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
 typedef float f32x4 __attribute__((ext_vector_type(4)));
 
-// Launch shapes (chosen by measurement on MI355X at H=7168):
-//  - pack: one wave per token; the row (up to 16 vectors per lane) is loaded
-//    once and each vector is stored to the K destinations back to back.
-//  - group and combine: one work-group per row (per token for combine),
-//    each thread owning VPT vectors of it, so a whole 14 KiB row is in flight
-//    at once; small rows share a work-group (RPB rows per group).
-constexpr int kPackThreads = 256;
-constexpr int kPackRows = kPackThreads / kWave;
-constexpr int kMaxVpl = 16;
+// Row-per-work-group launches (grouping copies, the fused norm): up to
+// 1024 threads per row, each owning VPT vectors of it, so a whole row is in
+// flight at once; short rows share a work-group (RPB rows per group).
 constexpr int kMaxTpr = 1024;
-constexpr int kCombineThreads = 256;  // K*VPT row loads in flight need the VGPRs
-
-__device__ __forceinline__ int wave_row() {
-    return __builtin_amdgcn_readfirstlane((int)(blockIdx.x * kPackRows + threadIdx.x / kWave));
-}
 
 __device__ __forceinline__ void accumulate(float* acc, u32x4 w, float s) {
 #pragma unroll
@@ -53,6 +42,35 @@ __device__ __forceinline__ void store_out(const float* acc, u32x4* __restrict__ 
 
 inline bool aligned16(const void* p) { return ((uintptr_t)p & 15u) == 0; }
 
+// Flat launches: one thread per 16-byte vector of a [rows, nvec] block, 256
+// threads per work-group, rows found by a division of the flat index. Many
+// light work-groups keep more stores in flight than a few heavy ones (on
+// MI355X a 256-thread, one-vector-per-thread write reaches ~6.4 TB/s where
+// 896-thread row groups stay near 4.7 TB/s).
+constexpr int kFlatThreads = 256;
+
+// q = n / d for 0 <= n < 2^31 by one 64-bit multiply and a shift, with
+// s = ceil(log2 d) and m = ceil(2^(32+s) / d) < 2^33: the rounding error of m
+// times n stays below 2^(32+s) / d, so the quotient is exact.
+struct FastDiv {
+    uint64_t m;
+    uint32_t s;
+    uint32_t d;
+};
+
+inline FastDiv make_fastdiv(uint32_t d) {
+    uint32_t s = 0;
+    while ((1ull << s) < d) ++s;
+    const unsigned __int128 num = (unsigned __int128)1 << (32 + s);
+    return {(uint64_t)((num + d - 1) / d), s, d};
+}
+
+__device__ __forceinline__ uint32_t fast_div(uint32_t n, FastDiv f) {
+    return (uint32_t)(((uint64_t)n * f.m) >> (32 + f.s));
+}
+
+inline bool flat_fits(long long rows, int nvec) { return rows * (long long)nvec < (1ll << 31); }
+
 // Threads per row for `vpt` vectors per thread: a multiple of the wave size,
 // at most 1024; rows per work-group so that small rows still fill 256 threads.
 struct RowShape {
@@ -67,26 +85,6 @@ inline RowShape row_shape(int nvec, int vpt, int max_tpr) {
     if (rpb < 1) rpb = 1;
     return {tpr, rpb};
 }
-
-#define MEP_VPL_SWITCH(vpl, FN, ...)         \
-    switch (vpl) {                           \
-        case 1: FN<1>(__VA_ARGS__); break;   \
-        case 2: FN<2>(__VA_ARGS__); break;   \
-        case 3: FN<3>(__VA_ARGS__); break;   \
-        case 4: FN<4>(__VA_ARGS__); break;   \
-        case 5: FN<5>(__VA_ARGS__); break;   \
-        case 6: FN<6>(__VA_ARGS__); break;   \
-        case 7: FN<7>(__VA_ARGS__); break;   \
-        case 8: FN<8>(__VA_ARGS__); break;   \
-        case 9: FN<9>(__VA_ARGS__); break;   \
-        case 10: FN<10>(__VA_ARGS__); break; \
-        case 11: FN<11>(__VA_ARGS__); break; \
-        case 12: FN<12>(__VA_ARGS__); break; \
-        case 13: FN<13>(__VA_ARGS__); break; \
-        case 14: FN<14>(__VA_ARGS__); break; \
-        case 15: FN<15>(__VA_ARGS__); break; \
-        default: FN<16>(__VA_ARGS__); break; \
-    }
 
 }  // namespace rows
 }  // namespace mep

@@ -216,7 +216,8 @@ int mep_remap_prune(int BS, int K, int E, int F, int world_size,
  *   [n_recv] int32 in [0, n_recv); recv_grouped [n_recv,H] bf16.
  * At least one of the two must run, unless T == 0 and n_recv == 0 (then
  * the call does nothing and may pass NULL buffers). Sizes: T >= 0, n_recv >= 0,
- * 1 <= K <= 64, 8 <= H <= 65536 with H % 8 == 0.
+ * 1 <= K <= 64, 8 <= H <= 65536 with H % 8 == 0, T*K < 2^31 and
+ * T*(H/8) < 2^31 (x below 32 GiB).
  * Errors: MEP_ERR_NULLPTR, MEP_ERR_PARAM (neither phase requested),
  *   MEP_ERR_SHAPE, MEP_ERR_HIP.
  */
@@ -241,7 +242,8 @@ int mep_dispatch(int T, int K, int H,
  *   (a row < n_y; a negative or out-of-range entry skips the route);
  *   scores [T*K] fp32; out_bf16 [T,H] bf16
  *   and out_f32 [T,H] fp32, either may be NULL but not both.
- * Sizes: T >= 0, 1 <= K <= 64, 8 <= H <= 65536, H % 8 == 0. With T == 0
+ * Sizes: T >= 0, 1 <= K <= 64, 8 <= H <= 65536, H % 8 == 0, T*K < 2^31,
+ * T*(H/8) < 2^31. With T == 0
  * the call does nothing (buffers may be NULL).
  * Errors: MEP_ERR_NULLPTR, MEP_ERR_SHAPE, MEP_ERR_HIP.
  */

@@ -173,3 +173,28 @@ def test_combine_add_rmsnorm_validation(B):
     assert f(4, 2, 64, 16, 4, 16, 16, 16, 16, 1e-6, None, None, None, None) == B.MEP_ERR_NULLPTR
     assert f(4, 2, 64, None, 4, 16, 16, 16, 16, 1e-6, None, 16, None, None) == B.MEP_ERR_NULLPTR
     assert f(4, 2, 64, 16, 4, 16, 16, 8, 16, 1e-6, None, 16, None, None) == B.MEP_ERR_SHAPE
+
+
+def test_flat_index_limit(B):
+    # the flat row kernels index T*(H/8) vectors with 31 bits
+    T, H = 1 << 20, 65536
+    assert B.mep_dispatch(T, 2, H, 16, 16, 16, 0, None, None, None, None) == B.MEP_ERR_SHAPE
+    assert B.mep_combine(T, 2, H, 16, 4, 16, 16, 16, None, None) == B.MEP_ERR_SHAPE
+    assert B.mep_dispatch_to_peers(T, 2, H, 2, 8, 16, 16, 16, 16, None) == B.MEP_ERR_SHAPE
+
+
+def test_row_division_by_multiply_is_exact():
+    # The row kernels find row = n // d as (n * m) >> (32 + s) with
+    # s = ceil(log2 d), m = ceil(2^(32+s) / d), for n < 2^31. Check the
+    # identity (and that n * m fits in 64 bits) at every quotient boundary
+    # for every row width up to 8192 vectors.
+    for d in range(1, 8193):
+        s = (d - 1).bit_length()
+        m = -(-(1 << (32 + s)) // d)
+        assert m < (1 << 33)
+        qmax = ((1 << 31) - 1) // d
+        for q in {0, 1, 2, qmax // 3, qmax // 2, qmax - 1, qmax}:
+            for n in (q * d - 1, q * d, q * d + d - 1):
+                if 0 <= n < (1 << 31):
+                    assert n * m < (1 << 64)
+                    assert (n * m) >> (32 + s) == n // d, (d, n)
