@@ -250,8 +250,8 @@ def fused_norm(torch, cba, d, pout, y_ret, scores, steps, flush=None):
 def main():
     ap = argparse.ArgumentParser()
     ap.add_argument("--gpus", type=int, default=1)
-    ap.add_argument("--steps", type=int, default=50)
-    ap.add_argument("--warmup", type=int, default=5)
+    ap.add_argument("--steps", type=int, default=100)
+    ap.add_argument("--warmup", type=int, default=10)
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--no-skew-sweep", action="store_true",
                     help="skip the imbalance sweep (R=8 E=384 S=8192 K=8 H=7168)")

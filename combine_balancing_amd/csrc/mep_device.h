@@ -161,9 +161,14 @@ __device__ __forceinline__ int upper_bound(const int* a, int n, int x) {
     return lo;
 }
 
+// Native 4 x int vector: arrays of it stay in registers, where arrays of
+// HIP's int4 struct can be left on the stack (scratch memory).
+typedef int i32x4 __attribute__((ext_vector_type(4)));
+
 // dst[i] = src[i] for i in [0, n), the block's threads striding by NT. The
 // loads of up to U strides are issued together before any store, so the
 // copy costs one memory round trip per U strides instead of one per stride.
+// T must be a scalar or a native vector type (i32x4, not int4).
 template <int NT, int U, typename T>
 __device__ __forceinline__ void stage(T* __restrict__ dst, const T* __restrict__ src, int n) {
     for (int base = 0; base < n; base += NT * U) {

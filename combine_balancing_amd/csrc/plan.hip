@@ -548,7 +548,7 @@ __global__ __launch_bounds__(kRouteThreads) void plan_routes(PlanDims d, PlanWs 
     }
     for (int i = tid; i < kRouteWaves * E; i += kRouteThreads) s_cnt[i] = 0;
     stage<kRouteThreads, 2>(s_ps, w.pstart, PM);
-    stage<kRouteThreads, 2>(s_prec, w.prec, PM);
+    stage<kRouteThreads, 2>((i32x4*)s_prec, (const i32x4*)w.prec, PM);
     stage<kRouteThreads, 1>(s_bkt, w.bucket, kBuckets);
     if (staged) stage<kRouteThreads, kStageIds / kRouteThreads>(s_ids, ids + f0, len);
     lds_barrier();
