@@ -62,7 +62,7 @@ __global__ __launch_bounds__(kMaxTpr) void group_rows(const u32x4* __restrict__ 
                                                       const int* __restrict__ recv_pos,
                                                       u32x4* __restrict__ out, int n, int nvec,
                                                       int tpr, int rpb) {
-    const int r = threadIdx.x / tpr;
+    const int r = row_in_group(tpr);
     const int tid = threadIdx.x - r * tpr;
     const int t = blockIdx.x * rpb + r;
     if (t >= n) return;

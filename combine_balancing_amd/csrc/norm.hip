@@ -10,12 +10,15 @@
 //   rstd    = 1 / sqrt(sum(x^2) / H + eps)                 (fp32)
 //   y       = (x * rstd) * gamma, rounded to bf16; x_out = bf16(x)
 //
-// One work-group per token (several tokens per group for short rows). Each
-// thread keeps NV vectors (8 values each) of its token's row in registers
-// from the K-way sum through the normalisation, so the row is read once and
-// written once; the sum of squares is reduced across the work-group through
-// LDS. HBM-bound like the plain combine: K rows plus the residual read, two
-// rows written.
+// One work-group per token (several tokens per group for short rows), up to
+// 1024 threads, each keeping NV <= 2 vectors (8 values each) of its token's
+// row in registers from the K-way sum through the normalisation, so the row
+// is read once and written once; the sum of squares is reduced across the
+// work-group through LDS. HBM-bound like the plain combine: K rows plus the
+// residual read, two rows written. (Measured on MI355X at H = 7168: 896
+// threads x 1 vector and 256 x 4 move the same bytes in about the same time;
+// what matters is that the row index is wave-uniform, so a token's
+// positions and scores come through scalar loads.)
 #include <algorithm>
 
 #include "rows.h"
@@ -25,8 +28,8 @@ namespace {
 
 using namespace rows;
 
-constexpr int kNormThreads = 256;
-constexpr int kNormMaxNv = 8;  // H <= 8 * 256 * 8 = 16384
+constexpr int kNormThreads = 1024;
+constexpr int kNormMaxNv = 2;  // H <= 2 * 1024 * 8 = 16384
 
 __device__ __forceinline__ float wave_sum(float v) {
 #pragma unroll
@@ -59,7 +62,7 @@ __global__ __launch_bounds__(kNormThreads) void combine_norm_rows(
     u32x4* __restrict__ y_out, float* __restrict__ rstd_out, int T, int K, int nvec, int tpr,
     int rpb) {
     __shared__ float s_red[kNormThreads / kWave];
-    const int r = threadIdx.x / tpr;
+    const int r = row_in_group(tpr);
     const int tid = threadIdx.x - r * tpr;
     const int t_raw = blockIdx.x * rpb + r;
     const bool live = t_raw < T;
@@ -176,13 +179,7 @@ void launch_norm(hipStream_t s, int nv, dim3 g, dim3 b, const u32x4* y, int n_y,
         break;
     switch (nv) {
         MEP_NORM_CASE(1)
-        MEP_NORM_CASE(2)
-        MEP_NORM_CASE(3)
-        MEP_NORM_CASE(4)
-        MEP_NORM_CASE(5)
-        MEP_NORM_CASE(6)
-        MEP_NORM_CASE(7)
-        default: MEP_NORM_CASE(8)
+        default: MEP_NORM_CASE(2)
     }
 #undef MEP_NORM_CASE
 }

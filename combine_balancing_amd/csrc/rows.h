@@ -77,6 +77,14 @@ struct RowShape {
     int tpr, rpb;
 };
 
+// Row of this thread within its work-group. tpr is a multiple of the wave
+// size, so a wave lies inside one row and the row is wave-uniform: reading
+// it from the first lane makes the row's index, position and score loads
+// scalar (and the row base an SGPR pair).
+__device__ __forceinline__ int row_in_group(int tpr) {
+    return __builtin_amdgcn_readfirstlane((int)(threadIdx.x / (unsigned)tpr));
+}
+
 inline RowShape row_shape(int nvec, int vpt, int max_tpr) {
     int tpr = (nvec + vpt - 1) / vpt;
     tpr = (tpr + kWave - 1) / kWave * kWave;

@@ -2,10 +2,10 @@
 
 x_out is compared bit for bit (the same fp32 operations in the same order as
 the oracle). rstd and y depend on the sum of squares, which the kernel
-reduces in fp32 as a tree (at most 64 sequential terms per thread, then 6
-wave levels and at most 3 cross-wave adds), while the oracle sums in fp64.
+reduces in fp32 as a tree (at most 16 sequential terms per thread, then 6
+wave levels and at most 15 cross-wave adds), while the oracle sums in fp64.
 All terms are non-negative, so the sum's relative error is at most
-(64 + 6 + 3) * 2^-24 < 4.4e-6. The division by H, the eps add, sqrt and the
+(16 + 6 + 15) * 2^-24 < 2.3e-6. The division by H, the eps add, sqrt and the
 reciprocal add a few ulps, so rstd is within 1e-5 relative (a bound with
 room). y in fp32 adds two more roundings, and the final bf16 rounding adds
 at most half a bf16 ulp (2^-8 of |y|), so |y - y_exact| <= |y_exact| *
