@@ -64,6 +64,8 @@ def _load():
     lib.oracle_combine_add_rmsnorm.argtypes = [I, I, I, P, I, P, P, P, P, ctypes.c_double,
                                                P, P, P, P]
     lib.oracle_combine_add_rmsnorm.restype = I
+    lib.oracle_dispatch_quant.argtypes = [I, I, I, P, P, I, P, P, I, I, P]
+    lib.oracle_dispatch_quant.restype = I
     lib.oracle_bf16_from_float.argtypes = [P, P, ctypes.c_int64]
     lib.oracle_bf16_from_float.restype = None
     lib.oracle_float_from_fp16.argtypes = [P, P, ctypes.c_int64]
@@ -270,6 +272,34 @@ def combine_add_rmsnorm(y_ret, send_pos, scores, residual, gamma, eps, n_y=None)
                                           _p(out["rstd"]), _p(out["y"])),
            "oracle_combine_add_rmsnorm")
     return out
+
+
+def quant_msg_bytes(H):
+    """Message row size of the int8 dispatch: Align512(Align32(H) + 4)."""
+    return ((H + 31) // 32 * 32 + 4 + 511) // 512 * 512
+
+
+def dispatch_quant(x, send_pos, K, smooth=None, route_expert=None, n_rows=None, msg_bytes=None,
+                   msgs=None):
+    """int8 pack (oracle_dispatch_quant). Returns the message rows
+    [n_rows, msg_bytes] uint8 (bytes the oracle does not write stay as given,
+    zero for a fresh buffer)."""
+    lib = _load()
+    x = _c(x, np.uint16)
+    T, H = x.shape
+    sp = _c(send_pos, np.int32).reshape(-1)
+    if sp.size != T * K:
+        raise ValueError("send_pos must hold T*K entries")
+    n_rows = T * K if n_rows is None else n_rows
+    msg_bytes = quant_msg_bytes(H) if msg_bytes is None else msg_bytes
+    if msgs is None:
+        msgs = np.zeros((n_rows, msg_bytes), np.uint8)
+    sm = None if smooth is None else _c(smooth, np.float32)
+    E = 0 if sm is None else sm.shape[0]
+    re = None if route_expert is None else _c(route_expert, np.int32).reshape(-1)
+    _check(lib.oracle_dispatch_quant(T, K, H, _p(x), _p(sm), E, _p(re), _p(sp), n_rows, msg_bytes,
+                                     _p(msgs)), "oracle_dispatch_quant")
+    return msgs
 
 
 def bf16_from_float(a):

@@ -504,6 +504,67 @@ int oracle_combine_add_rmsnorm(int T, int K, int H, const uint16_t* y_ret, int n
     return OR_OK;
 }
 
+/*
+ * oracle_dispatch_quant: the pack with int8 dynamic quantization of each
+ * routed row ([DispSetup] interface description: token data may be
+ * quantized before it is sent; parameter notes: dynamic quantization may
+ * take optional per-expert smoothing scales; message size
+ * Align512(Align32(H) + 4): H int8 values, padding to a multiple of 32, one
+ * 4-byte scale). The pages give no formula; the reading taken is symmetric
+ * per-route int8 quantization in fp32:
+ *   v[h]  = float(x[t,h])                            (no smoothing), or
+ *   v[h]  = fl(float(x[t,h]) * smooth[e,h])          e = route_expert[t*K+k]
+ *   amax  = max over h of |v[h]|
+ *   s     = fl(amax / 127)
+ *   q[h]  = rint(fl(v[h] / s)) clamped to [-127, 127] (ties to even);
+ *           q = 0 everywhere when s == 0
+ * written to message row send_pos[t*K+k]: bytes [0, H) hold q, bytes
+ * [Align32(H), Align32(H)+4) hold s (fp32, little endian). Other bytes of
+ * the row are not written. Routes with send_pos outside [0, n_rows) are
+ * skipped.
+ */
+int oracle_dispatch_quant(int T, int K, int H, const uint16_t* x, const float* smooth, int E,
+                          const int32_t* route_expert, const int32_t* send_pos, int n_rows,
+                          int msg_bytes, uint8_t* msgs) {
+    const int64_t hq = ((int64_t)H + 31) / 32 * 32;
+    if (T < 0 || K < 1 || H < 1 || n_rows < 0 || msg_bytes < hq + 4) return OR_ERR_ARG;
+    if (smooth && (!route_expert || E < 1)) return OR_ERR_ARG;
+    float* v = (float*)malloc(sizeof(float) * (size_t)H);
+    if (!v) return OR_ERR_ALLOC;
+    for (int64_t t = 0; t < T; t++)
+        for (int k = 0; k < K; k++) {
+            const int32_t row = send_pos[t * K + k];
+            if (row < 0 || row >= n_rows) continue;
+            int32_t e = smooth ? route_expert[t * K + k] : 0;
+            if (smooth && (e < 0 || e >= E)) {
+                free(v);
+                return OR_ERR_ARG;
+            }
+            float amax = 0.0f;
+            for (int64_t h = 0; h < H; h++) {
+                float a = bf16_to_float(x[t * H + h]);
+                if (smooth) a = a * smooth[(int64_t)e * H + h];
+                v[h] = a;
+                const float m = fabsf(a);
+                if (m > amax) amax = m;
+            }
+            const float sc = amax / 127.0f;
+            uint8_t* out = msgs + (int64_t)row * msg_bytes;
+            for (int64_t h = 0; h < H; h++) {
+                float q = 0.0f;
+                if (sc > 0.0f) {
+                    q = rintf(v[h] / sc);
+                    if (q > 127.0f) q = 127.0f;
+                    if (q < -127.0f) q = -127.0f;
+                }
+                out[h] = (uint8_t)(int8_t)q;
+            }
+            memcpy(out + hq, &sc, 4);
+        }
+    free(v);
+    return OR_OK;
+}
+
 /* Exposed for pinning the conversions in tests. */
 void oracle_bf16_from_float(const float* in, uint16_t* out, int64_t n) {
     for (int64_t i = 0; i < n; i++) out[i] = float_to_bf16_rne(in[i]);
