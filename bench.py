@@ -247,6 +247,31 @@ def fused_norm(torch, cba, d, pout, y_ret, scores, steps, flush=None):
             "outputs": "y bf16 [S,H], x bf16 [S,H], rstd fp32 [S]; eps 1e-6"}
 
 
+def int8_dispatch(torch, cba, d, pout, steps, flush=None):
+    """The pack with int8 dynamic quantization at the same workload (rank 0's
+    send map): Align512(Align32(H)+4)-byte messages instead of bf16 rows."""
+    S, K, H, C = d["S"], d["K"], d["H"], d["C"]
+    x = _dev(torch, d["x"])
+    mb = cba.quant_msg_bytes(H)
+    msgs = torch.empty(C, mb, dtype=torch.uint8, device="cuda")
+    stream = torch.cuda.current_stream()
+    t = []
+    for it in range(steps + 3):
+        if flush is not None:
+            flush.fill_(it & 0xFF)
+        ev = [torch.cuda.Event(enable_timing=True) for _ in range(2)]
+        ev[0].record(stream)
+        cba.dispatch_quant(K, x, pout["send_pos"], send_msgs=msgs)
+        ev[1].record(stream)
+        torch.cuda.synchronize()
+        if it >= 3:
+            t.append(ev[0].elapsed_time(ev[1]) * 1e3)
+    us = float(np.mean(t))
+    nb = S * H * 2 + C * (H + 4) + C * 4
+    return {"us": round(us, 2), "GBs": round(nb / (us * 1e-6) / 1e9, 1), "algorithmic_bytes": nb,
+            "msg_bytes": mb, "bytes_sent_vs_bf16": round(C * mb / (C * H * 2), 4)}
+
+
 def main():
     ap = argparse.ArgumentParser()
     ap.add_argument("--gpus", type=int, default=1)
@@ -398,6 +423,8 @@ def main():
     }
     res["combine_add_rmsnorm"] = fused_norm(torch, cba, d, pout, y_ret, scores,
                                             steps=max(5, min(args.steps, 20)), flush=flush)
+    res["int8_dispatch"] = int8_dispatch(torch, cba, d, pout, steps=max(5, min(args.steps, 20)),
+                                         flush=flush)
     if not args.no_zero_copy:
         res["zero_copy"] = zero_copy(torch, cba, d, pout, steps=max(5, min(args.steps, 20)),
                                      flush=flush)

@@ -59,6 +59,10 @@ def lib():
     L.mep_ungroup.restype = I
     L.mep_combine_add_rmsnorm.argtypes = [I, I, I, P, I, P, P, P, P, ctypes.c_float, P, P, P, P]
     L.mep_combine_add_rmsnorm.restype = I
+    L.mep_quant_msg_bytes.argtypes = [I]
+    L.mep_quant_msg_bytes.restype = Z
+    L.mep_dispatch_quant.argtypes = [I, I, I, P, P, I, P, P, I, I, P, P]
+    L.mep_dispatch_quant.restype = I
     _lib = L
     return L
 
@@ -128,3 +132,13 @@ def mep_combine_add_rmsnorm(T, K, H, y_ret, n_y, send_pos, scores, residual, gam
                             y_out, rstd_out, stream) -> int:
     return lib().mep_combine_add_rmsnorm(T, K, H, y_ret, n_y, send_pos, scores, residual, gamma,
                                          eps, x_out, y_out, rstd_out, stream)
+
+
+def mep_quant_msg_bytes(H) -> int:
+    return lib().mep_quant_msg_bytes(H)
+
+
+def mep_dispatch_quant(T, K, H, x, smooth, E, route_expert, send_pos, n_rows, msg_bytes,
+                       send_msgs, stream) -> int:
+    return lib().mep_dispatch_quant(T, K, H, x, smooth, E, route_expert, send_pos, n_rows,
+                                    msg_bytes, send_msgs, stream)

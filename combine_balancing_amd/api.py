@@ -293,3 +293,28 @@ def combine_add_rmsnorm(y_ret, send_pos, scores, residual, gamma, eps=1e-6, x_ou
         _opt(rstd_out, "rstd_out", torch.float32, T), _stream_handle(stream))
     B.check("mep_combine_add_rmsnorm", rc)
     return y_out, x_out, rstd_out
+
+
+def quant_msg_bytes(H):
+    """Bytes of one int8 token message (Align512(Align32(H) + 4))."""
+    return B.mep_quant_msg_bytes(H)
+
+
+def dispatch_quant(K, x, send_pos, send_msgs=None, smooth=None, route_expert=None, n_rows=None,
+                   stream=None):
+    """mep_dispatch_quant. x [T,H] bf16; send_pos [T*K]; smooth [E,H] fp32
+    and route_expert [T*K] (optional, together). Returns send_msgs
+    [n_rows, msg_bytes] uint8 (allocated if not given)."""
+    T, H = x.shape
+    if send_msgs is None:
+        n_rows = T * K if n_rows is None else n_rows
+        send_msgs = torch.zeros(n_rows, quant_msg_bytes(H), dtype=torch.uint8, device=x.device)
+    n_rows, msg_bytes = send_msgs.shape
+    E = 0 if smooth is None else smooth.shape[0]
+    rc = B.mep_dispatch_quant(
+        T, K, H, _need(x, "x", _BF16_LIKE), _opt(smooth, "smooth", torch.float32),
+        E, _opt(route_expert, "route_expert", torch.int32, T * K),
+        _need(send_pos, "send_pos", torch.int32, T * K), n_rows, msg_bytes,
+        _need(send_msgs, "send_msgs", torch.uint8), _stream_handle(stream))
+    B.check("mep_dispatch_quant", rc)
+    return send_msgs

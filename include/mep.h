@@ -336,6 +336,47 @@ int mep_combine_add_rmsnorm(int T, int K, int H, const uint16_t* y_ret, int n_y,
                             uint16_t* x_out, uint16_t* y_out, float* rstd_out,
                             void* stream);
 
+/* -------------------------------------------------------- int8 dispatch */
+
+/*
+ * mep_quant_msg_bytes - size of one int8 token message: Align512(Align32(H)
+ * + 4) bytes ("aclnnMoeDistributeDispatchSetup" op doc, parameter notes:
+ * message size in the quantized case). Host only; 0 for H < 1.
+ */
+size_t mep_quant_msg_bytes(int H);
+
+/*
+ * mep_dispatch_quant - the pack with dynamic int8 quantization of every
+ * routed row ("aclnnMoeDistributeDispatchSetup" op doc, interface
+ * description: token data may be quantized before sending; parameter notes:
+ * optional smoothing scales for dynamic quantization; the message layout).
+ * The pages give no formula; this computes, per route (t,k) with
+ * 0 <= send_pos[t*K+k] < n_rows:
+ *   v[h] = float(x[t,h]), or fl(float(x[t,h]) * smooth[e*H + h]) with
+ *          e = route_expert[t*K+k] when smooth is given
+ *   s    = fl(max_h |v[h]| / 127)          (fp32, correctly rounded)
+ *   q[h] = rint(fl(v[h] / s)), ties to even, clamped to [-127, 127];
+ *          q = 0 when s == 0
+ * and writes message row p = send_pos[t*K+k] of send_msgs: int8 q[0..H) in
+ * bytes [0, H), s (fp32) at byte Align32(H). Other bytes of the row are not
+ * written. With smoothing, a route whose expert id is outside [0, E) is
+ * skipped.
+ *   x [T,H] bf16; smooth [E,H] fp32 or NULL; route_expert [T*K] int32
+ *   (required with smooth); send_pos [T*K] int32 (this rank's send map);
+ *   send_msgs [n_rows, msg_bytes] bytes, msg_bytes >= Align32(H) + 4 and a
+ *   multiple of 16 (mep_quant_msg_bytes(H) is the pages' size).
+ * The received messages are grouped with mep_dispatch's grouping as rows of
+ * msg_bytes / 2 bf16-sized units (the grouping copies bytes).
+ * Sizes: T >= 0, 1 <= K <= 64, 8 <= H <= 16384, H % 8 == 0, T*K < 2^31;
+ * T == 0 or n_rows == 0 does nothing. x, send_msgs and smooth 16-byte
+ * aligned; values of x (and smooth) finite.
+ * Errors: MEP_ERR_NULLPTR, MEP_ERR_PARAM (smooth without route_expert or
+ * E < 1), MEP_ERR_SHAPE, MEP_ERR_HIP.
+ */
+int mep_dispatch_quant(int T, int K, int H, const uint16_t* x, const float* smooth, int E,
+                       const int32_t* route_expert, const int32_t* send_pos, int n_rows,
+                       int msg_bytes, uint8_t* send_msgs, void* stream);
+
 #ifdef __cplusplus
 }
 #endif

@@ -520,8 +520,8 @@ int oracle_combine_add_rmsnorm(int T, int K, int H, const uint16_t* y_ret, int n
  *           q = 0 everywhere when s == 0
  * written to message row send_pos[t*K+k]: bytes [0, H) hold q, bytes
  * [Align32(H), Align32(H)+4) hold s (fp32, little endian). Other bytes of
- * the row are not written. Routes with send_pos outside [0, n_rows) are
- * skipped.
+ * the row are not written. Routes with send_pos outside [0, n_rows), or
+ * (with smoothing) an expert id outside [0, E), are skipped.
  */
 int oracle_dispatch_quant(int T, int K, int H, const uint16_t* x, const float* smooth, int E,
                           const int32_t* route_expert, const int32_t* send_pos, int n_rows,
@@ -536,10 +536,7 @@ int oracle_dispatch_quant(int T, int K, int H, const uint16_t* x, const float* s
             const int32_t row = send_pos[t * K + k];
             if (row < 0 || row >= n_rows) continue;
             int32_t e = smooth ? route_expert[t * K + k] : 0;
-            if (smooth && (e < 0 || e >= E)) {
-                free(v);
-                return OR_ERR_ARG;
-            }
+            if (smooth && (e < 0 || e >= E)) continue; /* no such expert: skipped */
             float amax = 0.0f;
             for (int64_t h = 0; h < H; h++) {
                 float a = bf16_to_float(x[t * H + h]);

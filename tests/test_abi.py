@@ -35,7 +35,7 @@ def test_header_declares_the_four_entry_points():
     for n in ("mep_plan", "mep_remap_prune", "mep_dispatch", "mep_combine",
               "mep_plan_workspace_size", "mep_status_str", "mep_version",
               "mep_dispatch_to_peers", "mep_combine_from_peers", "mep_ungroup",
-              "mep_combine_add_rmsnorm"):
+              "mep_combine_add_rmsnorm", "mep_quant_msg_bytes", "mep_dispatch_quant"):
         assert n in names
 
 
@@ -198,3 +198,18 @@ def test_row_division_by_multiply_is_exact():
                 if 0 <= n < (1 << 31):
                     assert n * m < (1 << 64)
                     assert (n * m) >> (32 + s) == n // d, (d, n)
+
+
+def test_dispatch_quant_validation(B):
+    assert B.mep_quant_msg_bytes(7168) == 7680
+    assert B.mep_quant_msg_bytes(100) == 512
+    assert B.mep_quant_msg_bytes(0) == 0
+    f = B.mep_dispatch_quant
+    assert f(0, 2, 64, None, None, 0, None, None, 0, 512, None, None) == B.MEP_OK
+    assert f(4, 2, 64, 16, None, 0, None, 16, 8, 512, None, None) == B.MEP_ERR_NULLPTR
+    assert f(4, 2, 64, 16, None, 0, None, 16, 8, 64, 16, None) == B.MEP_ERR_SHAPE     # < H+4
+    assert f(4, 2, 64, 16, None, 0, None, 16, 8, 520, 16, None) == B.MEP_ERR_SHAPE    # % 16
+    assert f(4, 2, 16392, 16, None, 0, None, 16, 8, 16896, 16, None) == B.MEP_ERR_SHAPE
+    assert f(4, 2, 64, 16, 16, 3, None, 16, 8, 512, 16, None) == B.MEP_ERR_PARAM     # no experts
+    assert f(4, 2, 64, 16, 16, 0, 16, 16, 8, 512, 16, None) == B.MEP_ERR_PARAM       # E < 1
+    assert f(4, 2, 64, 8, None, 0, None, 16, 8, 512, 16, None) == B.MEP_ERR_SHAPE    # unaligned x

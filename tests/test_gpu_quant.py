@@ -1,0 +1,103 @@
+"""GPU parity of mep_dispatch_quant (int8 dispatch) against the oracle.
+
+Both sides start from the same byte fill, so whole message buffers are
+compared bit for bit: the codes and scales written, and the bytes neither
+side writes. The quantization decision (rint of an fp32 quotient) is taken
+in fp32 on both sides.
+"""
+import numpy as np
+import pytest
+
+import synth
+from gpu_util import dev, host, note, require_gpu
+
+pytestmark = pytest.mark.gpu
+
+FILL = 0x5A
+
+
+def _run(orc, x, sp, K, smooth=None, ex=None, n_rows=None):
+    torch = require_gpu()
+    import combine_balancing_amd as cba
+    T, H = x.shape
+    n_rows = T * K if n_rows is None else n_rows
+    mb = orc.quant_msg_bytes(H)
+    assert cba.quant_msg_bytes(H) == mb
+    ref = np.full((n_rows, mb), FILL, np.uint8)
+    orc.dispatch_quant(x, sp, K, smooth=smooth, route_expert=ex, n_rows=n_rows, msgs=ref)
+    msgs = torch.full((n_rows, mb), FILL, dtype=torch.uint8, device="cuda")
+    cba.dispatch_quant(K, dev(x), dev(sp), send_msgs=msgs,
+                       smooth=None if smooth is None else dev(smooth),
+                       route_expert=None if ex is None else dev(ex))
+    torch.cuda.synchronize()
+    got = host(msgs)
+    if not np.array_equal(got, ref):
+        bad = np.argwhere(got != ref)
+        raise AssertionError(f"{len(bad)} bytes differ, first at {bad[:4].tolist()}")
+    return got
+
+
+CASES = [(1, 1, 8), (5, 3, 24), (64, 8, 128), (37, 4, 1032), (19, 6, 5120), (40, 8, 7168),
+         (7, 2, 16384), (130, 1, 256), (9, 16, 2048)]
+
+
+@pytest.mark.parametrize("T,K,H", CASES)
+def test_quant_shapes(orc, T, K, H):
+    note(f"dispatch_quant T={T} K={K} H={H}")
+    rng = np.random.default_rng(T * 7 + K * 131 + H)
+    x = synth.bf16_normal(rng, (T, H))
+    sp = rng.permutation(T * K).astype(np.int32)
+    sp[rng.random(T * K) < 0.1] = -1
+    _run(orc, x, sp, K)
+
+
+@pytest.mark.parametrize("T,K,H", [(33, 4, 512), (21, 8, 7168), (5, 2, 16384)])
+def test_quant_smoothing(orc, T, K, H):
+    note(f"dispatch_quant smoothing T={T} K={K} H={H}")
+    rng = np.random.default_rng(T + K + H)
+    E = 6
+    x = synth.bf16_normal(rng, (T, H))
+    sm = (rng.random((E, H), dtype=np.float32) * 2.0 + 0.1).astype(np.float32)
+    ex = rng.integers(0, E, T * K).astype(np.int32)
+    ex[::5] = E  # no such expert: skipped on both sides
+    sp = rng.permutation(T * K).astype(np.int32)
+    _run(orc, x, sp, K, smooth=sm, ex=ex)
+
+
+def test_quant_rounding_edges(orc):
+    # ties to even on the GPU (s = 1 exactly), a zero row, a tiny row
+    note("dispatch_quant rounding edges")
+    row = np.array([127.0, 2.5, 3.5, -2.5, -0.5, 1.5, -127.0, 0.0], np.float32)
+    x = np.zeros((3, 8), np.uint16)
+    x[0] = (row.view(np.uint32) >> 16).astype(np.uint16)
+    x[2] = (np.full(8, 1e-30, np.float32).view(np.uint32) >> 16).astype(np.uint16)
+    got = _run(orc, x, np.array([0, 1, 2], np.int32), 1)
+    assert list(got[0, :8].view(np.int8)) == [127, 2, 4, -2, 0, 2, -127, 0]
+    assert np.all(got[1, :8] == 0)
+
+
+def test_quant_headline_shape_and_grouping(orc):
+    # S=4096 K=8 H=7168 on rank 0's planned send map: every message byte;
+    # then the receive grouping of message rows (a byte copy) vs the oracle's
+    torch = require_gpu()
+    import combine_balancing_amd as cba
+    note("dispatch_quant dsv3")
+    d = synth.make_plan_inputs("dsv3", stand_ins=False)
+    R, E, S, K, H, C = d["R"], d["E"], d["S"], d["K"], d["H"], d["C"]
+    p = orc.plan(d["topk_ids"], R, E, S, K, m=0)
+    msgs = _run(orc, d["x"], p["send_pos"], K)
+    note("group int8 messages dsv3")
+    raw = msgs.view(np.uint16)  # rows of msg_bytes / 2 units
+    _, grouped = cba.dispatch(K, recv_raw=dev(raw), recv_pos=dev(p["recv_pos"]))
+    torch.cuda.synchronize()
+    assert np.array_equal(host(grouped), orc.group(raw, p["recv_pos"]))
+
+
+def test_quant_empty():
+    torch = require_gpu()
+    import combine_balancing_amd as cba
+    x = torch.zeros(0, 64, dtype=torch.bfloat16, device="cuda")
+    sp = torch.zeros(0, dtype=torch.int32, device="cuda")
+    m = cba.dispatch_quant(4, x, sp)
+    torch.cuda.synchronize()
+    assert m.shape[0] == 0
