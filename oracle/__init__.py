@@ -66,6 +66,8 @@ def _load():
     lib.oracle_combine_add_rmsnorm.restype = I
     lib.oracle_dispatch_quant.argtypes = [I, I, I, P, P, I, P, P, I, I, P]
     lib.oracle_dispatch_quant.restype = I
+    lib.oracle_group_quant.argtypes = [I, I, I, P, I, P, P, P]
+    lib.oracle_group_quant.restype = I
     lib.oracle_bf16_from_float.argtypes = [P, P, ctypes.c_int64]
     lib.oracle_bf16_from_float.restype = None
     lib.oracle_float_from_fp16.argtypes = [P, P, ctypes.c_int64]
@@ -300,6 +302,20 @@ def dispatch_quant(x, send_pos, K, smooth=None, route_expert=None, n_rows=None, 
     _check(lib.oracle_dispatch_quant(T, K, H, _p(x), _p(sm), E, _p(re), _p(sp), n_rows, msg_bytes,
                                      _p(msgs)), "oracle_dispatch_quant")
     return msgs
+
+
+def group_quant(msgs, recv_pos, H):
+    """int8 messages [n_msgs, msg_bytes] -> (x_q [n,H] int8 as uint8, scales [n] fp32)
+    (oracle_group_quant)."""
+    lib = _load()
+    m = _c(msgs, np.uint8)
+    n_msgs, mb = m.shape
+    rp = _c(recv_pos, np.int32).reshape(-1)
+    xq = np.zeros((rp.size, H), np.uint8)
+    sc = np.zeros(rp.size, np.float32)
+    _check(lib.oracle_group_quant(rp.size, H, mb, _p(rp), n_msgs, _p(m), _p(xq), _p(sc)),
+           "oracle_group_quant")
+    return xq, sc
 
 
 def bf16_from_float(a):

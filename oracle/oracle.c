@@ -562,6 +562,28 @@ int oracle_dispatch_quant(int T, int K, int H, const uint16_t* x, const float* s
     return OR_OK;
 }
 
+/*
+ * oracle_group_quant: receive-side grouping of int8 messages into the
+ * expert-side layout ([DispSetup] call example: the dispatch returns the
+ * received tokens as an int8 matrix plus one fp32 dynamic scale per token):
+ *   x_q[t, 0:H] = msgs[recv_pos[t], 0:H]
+ *   scales[t]   = the fp32 at byte Align32(H) of msgs[recv_pos[t]]
+ * for t in [0, n); entries outside [0, n_msgs) leave row t untouched.
+ */
+int oracle_group_quant(int n, int H, int msg_bytes, const int32_t* recv_pos, int n_msgs,
+                       const uint8_t* msgs, uint8_t* x_q, float* scales) {
+    const int64_t hq = ((int64_t)H + 31) / 32 * 32;
+    if (n < 0 || H < 1 || n_msgs < 0 || msg_bytes < hq + 4) return OR_ERR_ARG;
+    for (int64_t t = 0; t < n; t++) {
+        const int32_t from = recv_pos[t];
+        if (from < 0 || from >= n_msgs) continue;
+        const uint8_t* m = msgs + (int64_t)from * msg_bytes;
+        memcpy(x_q + t * H, m, (size_t)H);
+        memcpy(scales + t, m + hq, 4);
+    }
+    return OR_OK;
+}
+
 /* Exposed for pinning the conversions in tests. */
 void oracle_bf16_from_float(const float* in, uint16_t* out, int64_t n) {
     for (int64_t i = 0; i < n; i++) out[i] = float_to_bf16_rne(in[i]);

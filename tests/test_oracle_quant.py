@@ -133,3 +133,25 @@ def test_token_copies_identical_and_skips(orc):
         rows = [sp[t * K + k] for k in range(K) if sp[t * K + k] >= 0]
         for r in rows[1:]:
             assert np.array_equal(msgs[r, :H], msgs[rows[0], :H])
+
+
+def test_group_quant_is_grouping_then_split(orc):
+    # the receive-side split equals the (pinned) row grouping of whole
+    # messages followed by reading the code bytes and the scale field
+    rng = np.random.default_rng(6)
+    T, K, H = 30, 4, 200
+    x = synth.bf16_normal(rng, (T, H))
+    sp = rng.permutation(T * K).astype(np.int32)
+    msgs = orc.dispatch_quant(x, sp, K)
+    rp = rng.permutation(T * K).astype(np.int32)
+    xq, sc = orc.group_quant(msgs, rp, H)
+    g = orc.group(msgs.view(np.uint16), rp).view(np.uint8)
+    assert np.array_equal(xq, g[:, :H])
+    assert np.array_equal(sc, _s(g, H))
+    # dequantized rows stay within half a step of the token rows they came from
+    tok = np.empty(T * K, np.int64)
+    tok[sp] = np.arange(T * K) // K
+    for t in range(T * K):
+        v = _f32(x[tok[rp[t]]]).astype(np.float64)
+        err = np.abs(xq[t].view(np.int8) * np.float64(sc[t]) - v)
+        assert np.all(err <= (0.5 + 127 * 2.0 ** -24) * sc[t] + 1e-30)
