@@ -255,21 +255,31 @@ def int8_dispatch(torch, cba, d, pout, steps, flush=None):
     mb = cba.quant_msg_bytes(H)
     msgs = torch.empty(C, mb, dtype=torch.uint8, device="cuda")
     stream = torch.cuda.current_stream()
-    t = []
+    xq = torch.empty(C, H, dtype=torch.int8, device="cuda")
+    sc = torch.empty(C, dtype=torch.float32, device="cuda")
+    t = {"pack": [], "group": []}
     for it in range(steps + 3):
         if flush is not None:
             flush.fill_(it & 0xFF)
-        ev = [torch.cuda.Event(enable_timing=True) for _ in range(2)]
+        ev = [torch.cuda.Event(enable_timing=True) for _ in range(3)]
         ev[0].record(stream)
         cba.dispatch_quant(K, x, pout["send_pos"], send_msgs=msgs)
         ev[1].record(stream)
+        # receive side on the same rows (stand-in for the arrival buffer)
+        cba.group_quant(msgs, pout["recv_pos"], H, x_q=xq, scales=sc)
+        ev[2].record(stream)
         torch.cuda.synchronize()
         if it >= 3:
-            t.append(ev[0].elapsed_time(ev[1]) * 1e3)
-    us = float(np.mean(t))
-    nb = S * H * 2 + C * (H + 4) + C * 4
-    return {"us": round(us, 2), "GBs": round(nb / (us * 1e-6) / 1e9, 1), "algorithmic_bytes": nb,
-            "msg_bytes": mb, "bytes_sent_vs_bf16": round(C * mb / (C * H * 2), 4)}
+            t["pack"].append(ev[0].elapsed_time(ev[1]) * 1e3)
+            t["group"].append(ev[1].elapsed_time(ev[2]) * 1e3)
+    us = {k: float(np.mean(v)) for k, v in t.items()}
+    nb = {"pack": S * H * 2 + C * (H + 4) + C * 4, "group": 2 * C * (H + 4) + C * 4}
+    return {"pack_us": round(us["pack"], 2),
+            "pack_GBs": round(nb["pack"] / (us["pack"] * 1e-6) / 1e9, 1),
+            "group_us": round(us["group"], 2),
+            "group_GBs": round(nb["group"] / (us["group"] * 1e-6) / 1e9, 1),
+            "algorithmic_bytes": nb, "msg_bytes": mb,
+            "bytes_sent_vs_bf16": round(C * mb / (C * H * 2), 4)}
 
 
 def main():

@@ -63,6 +63,8 @@ def lib():
     L.mep_quant_msg_bytes.restype = Z
     L.mep_dispatch_quant.argtypes = [I, I, I, P, P, I, P, P, I, I, P, P]
     L.mep_dispatch_quant.restype = I
+    L.mep_group_quant.argtypes = [I, I, I, P, I, P, P, P, P]
+    L.mep_group_quant.restype = I
     _lib = L
     return L
 
@@ -142,3 +144,8 @@ def mep_dispatch_quant(T, K, H, x, smooth, E, route_expert, send_pos, n_rows, ms
                        send_msgs, stream) -> int:
     return lib().mep_dispatch_quant(T, K, H, x, smooth, E, route_expert, send_pos, n_rows,
                                     msg_bytes, send_msgs, stream)
+
+
+def mep_group_quant(n, H, msg_bytes, recv_pos, n_msgs, recv_msgs, x_q, scales, stream) -> int:
+    return lib().mep_group_quant(n, H, msg_bytes, recv_pos, n_msgs, recv_msgs, x_q, scales,
+                                 stream)

@@ -318,3 +318,21 @@ def dispatch_quant(K, x, send_pos, send_msgs=None, smooth=None, route_expert=Non
         _need(send_msgs, "send_msgs", torch.uint8), _stream_handle(stream))
     B.check("mep_dispatch_quant", rc)
     return send_msgs
+
+
+def group_quant(recv_msgs, recv_pos, H, x_q=None, scales=None, stream=None):
+    """mep_group_quant. recv_msgs [n_msgs, msg_bytes] uint8 in arrival order,
+    recv_pos [n]. Returns (x_q [n, H] int8, scales [n] fp32)."""
+    n_msgs, msg_bytes = recv_msgs.shape
+    n = recv_pos.numel()
+    dev = recv_msgs.device
+    if x_q is None:
+        x_q = torch.empty(n, H, dtype=torch.int8, device=dev)
+    if scales is None:
+        scales = torch.empty(n, dtype=torch.float32, device=dev)
+    rc = B.mep_group_quant(n, H, msg_bytes, _need(recv_pos, "recv_pos", torch.int32, n), n_msgs,
+                           _need(recv_msgs, "recv_msgs", torch.uint8),
+                           _need(x_q, "x_q", (torch.int8, torch.uint8), n * H),
+                           _need(scales, "scales", torch.float32, n), _stream_handle(stream))
+    B.check("mep_group_quant", rc)
+    return x_q, scales

@@ -14,12 +14,17 @@
 // Align32(H); other bytes of the row are not written.
 //
 // One work-group per token (several per group for short rows), as the fused
-// norm: each thread holds NV <= 2 vectors (8 values) of the row, the row's
-// amax is reduced by a wave shuffle tree and across waves through LDS, and
-// each thread writes 8 code bytes per vector (a 512-byte contiguous segment
-// per wave) to each of the token's K message rows. Without smoothing one
+// norm: each thread holds up to 2 units of 1 or 2 adjacent 16-byte vectors
+// (8 or 16 values) of the row, the row's amax is reduced by a wave shuffle
+// tree and across waves through LDS, and each thread writes its units'
+// codes (8 or 16 bytes each, so a wave writes 512 B or 1 KiB contiguous) to
+// each of the token's K message rows. Without smoothing one
 // reduction serves all K routes; with it, each route has its own.
 // HBM-bound: S*H*2 bytes read, C*(H+4) written.
+//
+// mep_group_quant is the receive side: message rows in arrival order become
+// the expert-side layout, int8 rows [n, H] grouped by instance plus one fp32
+// scale per row.
 #include <algorithm>
 
 #include "rows.h"
@@ -32,7 +37,7 @@ using namespace rows;
 typedef uint32_t u32x2 __attribute__((ext_vector_type(2)));
 
 constexpr int kQuantThreads = 1024;
-constexpr int kQuantMaxNv = 2;  // H <= 2 * 1024 * 8 = 16384
+constexpr int kQuantMaxNv = 2;  // units per thread: H <= 2 * 1024 * 8 = 16384 (W = 1)
 
 __device__ __forceinline__ float wave_max(float v) {
 #pragma unroll
@@ -50,8 +55,9 @@ __device__ __forceinline__ float row_max(float a, float* s_red, int r, int wpr) 
     return m;
 }
 
-__device__ __forceinline__ u32x2 quantize8(const float* v, float s) {
-    u32x2 o = {0u, 0u};
+// 8 fp32 values -> 8 int8 codes packed little-endian into two words
+__device__ __forceinline__ void quantize8(const float* v, float s, uint32_t* o) {
+    o[0] = o[1] = 0u;
     if (s > 0.0f) {
 #pragma unroll
         for (int j = 0; j < 8; ++j) {
@@ -60,14 +66,28 @@ __device__ __forceinline__ u32x2 quantize8(const float* v, float s) {
             o[j >> 2] |= ((uint32_t)(int32_t)q & 0xffu) << (8 * (j & 3));
         }
     }
-    return o;
 }
 
-template <int NV, bool SMOOTH>
+template <int W>
+struct Codes;  // the store type of W vectors' codes (8 bytes per vector)
+template <>
+struct Codes<1> {
+    typedef u32x2 type;
+};
+template <>
+struct Codes<2> {
+    typedef u32x4 type;
+};
+
+// A thread owns NU units of W adjacent 16-byte vectors (W = 2 when the row
+// has an even number of vectors: 16 values -> one 16-byte code store).
+template <int W, int NU, bool SMOOTH>
 __global__ __launch_bounds__(kQuantThreads) void quant_pack_rows(
     const u32x4* __restrict__ x, const float* __restrict__ smooth, int E,
     const int* __restrict__ route_expert, const int* __restrict__ send_pos, int n_rows,
     uint8_t* __restrict__ msgs, int msg_bytes, int hq, int T, int K, int nvec, int tpr, int rpb) {
+    typedef typename Codes<W>::type CT;
+    constexpr int NV = W * NU;
     __shared__ float s_red[2][kQuantThreads / kWave];
     const int r = row_in_group(tpr);
     const int tid = threadIdx.x - r * tpr;
@@ -75,40 +95,54 @@ __global__ __launch_bounds__(kQuantThreads) void quant_pack_rows(
     const bool live = t_raw < T;
     const int t = live ? t_raw : T - 1;  // rows past T load a real row, store nothing
     const int wpr = tpr / kWave;
+    const int nunits = nvec / W;
+
+    // vector index of slot (unit i, part w); units past the row are clamped
+    // for loads and skipped for stores
+    auto vec_of = [&](int i, int w) { return min(i * tpr + tid, nunits - 1) * W + w; };
+    auto unit_ok = [&](int i) { return i * tpr + tid < nunits; };
 
     float v[NV][8];
 #pragma unroll
-    for (int i = 0; i < NV; ++i) {
-        const u32x4 w = __builtin_nontemporal_load(x + (size_t)t * nvec + min(i * tpr + tid, nvec - 1));
+    for (int i = 0; i < NU; ++i)
 #pragma unroll
-        for (int j = 0; j < 4; ++j) {
-            v[i][2 * j] = __uint_as_float(w[j] << 16);
-            v[i][2 * j + 1] = __uint_as_float(w[j] & 0xffff0000u);
+        for (int w = 0; w < W; ++w) {
+            const u32x4 q = __builtin_nontemporal_load(x + (size_t)t * nvec + vec_of(i, w));
+#pragma unroll
+            for (int j = 0; j < 4; ++j) {
+                v[i * W + w][2 * j] = __uint_as_float(q[j] << 16);
+                v[i * W + w][2 * j + 1] = __uint_as_float(q[j] & 0xffff0000u);
+            }
         }
-    }
 
     if constexpr (!SMOOTH) {
         float a = 0.0f;
 #pragma unroll
-        for (int i = 0; i < NV; ++i)
-            if (i * tpr + tid < nvec)
+        for (int i = 0; i < NU; ++i)
+            if (unit_ok(i))
 #pragma unroll
-                for (int j = 0; j < 8; ++j) a = fmaxf(a, fabsf(v[i][j]));
+                for (int w = 0; w < W; ++w)
+#pragma unroll
+                    for (int j = 0; j < 8; ++j) a = fmaxf(a, fabsf(v[i * W + w][j]));
         const float s = row_max(a, s_red[0], r, wpr) / 127.0f;
-        u32x2 q[NV];
+        CT q[NU];
 #pragma unroll
-        for (int i = 0; i < NV; ++i) q[i] = quantize8(v[i], s);
+        for (int i = 0; i < NU; ++i) {
+            uint32_t o[2 * W];
+#pragma unroll
+            for (int w = 0; w < W; ++w) quantize8(v[i * W + w], s, o + 2 * w);
+#pragma unroll
+            for (int j = 0; j < 2 * W; ++j) q[i][j] = o[j];
+        }
         if (!live) return;
         for (int k = 0; k < K; ++k) {
             const int p = send_pos[(size_t)t * K + k];
             if ((unsigned)p >= (unsigned)n_rows) continue;
-            uint8_t* row = msgs + (size_t)p * msg_bytes;
+            CT* row = (CT*)(msgs + (size_t)p * msg_bytes);
 #pragma unroll
-            for (int i = 0; i < NV; ++i) {
-                const int vi = i * tpr + tid;
-                if (vi < nvec) __builtin_nontemporal_store(q[i], (u32x2*)(row + (size_t)vi * 8));
-            }
-            if (tid == 0) __builtin_nontemporal_store(s, (float*)(row + hq));
+            for (int i = 0; i < NU; ++i)
+                if (unit_ok(i)) __builtin_nontemporal_store(q[i], row + i * tpr + tid);
+            if (tid == 0) __builtin_nontemporal_store(s, (float*)((uint8_t*)row + hq));
         }
     } else {
         for (int k = 0; k < K; ++k) {
@@ -116,36 +150,63 @@ __global__ __launch_bounds__(kQuantThreads) void quant_pack_rows(
             const int e = route_expert[(size_t)t * K + k];
             const bool use = (unsigned)p < (unsigned)n_rows && (unsigned)e < (unsigned)E;
             const float* sm = smooth + (size_t)(use ? e : 0) * (nvec * 8);
-            float w[NV][8];
+            float wv[NV][8];
             float a = 0.0f;
 #pragma unroll
-            for (int i = 0; i < NV; ++i) {
-                const int vi = min(i * tpr + tid, nvec - 1);
-                const f32x4 s0 = *(const f32x4*)(sm + (size_t)vi * 8);
-                const f32x4 s1 = *(const f32x4*)(sm + (size_t)vi * 8 + 4);
+            for (int i = 0; i < NU; ++i)
 #pragma unroll
-                for (int j = 0; j < 4; ++j) {
-                    w[i][j] = v[i][j] * s0[j];
-                    w[i][4 + j] = v[i][4 + j] * s1[j];
+                for (int w = 0; w < W; ++w) {
+                    const int vi = vec_of(i, w);
+                    const f32x4 s0 = *(const f32x4*)(sm + (size_t)vi * 8);
+                    const f32x4 s1 = *(const f32x4*)(sm + (size_t)vi * 8 + 4);
+#pragma unroll
+                    for (int j = 0; j < 4; ++j) {
+                        wv[i * W + w][j] = v[i * W + w][j] * s0[j];
+                        wv[i * W + w][4 + j] = v[i * W + w][4 + j] * s1[j];
+                    }
+                    if (unit_ok(i))
+#pragma unroll
+                        for (int j = 0; j < 8; ++j) a = fmaxf(a, fabsf(wv[i * W + w][j]));
                 }
-                if (i * tpr + tid < nvec)
-#pragma unroll
-                    for (int j = 0; j < 8; ++j) a = fmaxf(a, fabsf(w[i][j]));
-            }
             // one reduction per route; alternating LDS slots make one
             // barrier per route enough
             const float s = row_max(a, s_red[k & 1], r, wpr) / 127.0f;
             if (!live || !use) continue;
-            uint8_t* row = msgs + (size_t)p * msg_bytes;
+            CT* row = (CT*)(msgs + (size_t)p * msg_bytes);
 #pragma unroll
-            for (int i = 0; i < NV; ++i) {
-                const int vi = i * tpr + tid;
-                if (vi < nvec)
-                    __builtin_nontemporal_store(quantize8(w[i], s), (u32x2*)(row + (size_t)vi * 8));
+            for (int i = 0; i < NU; ++i) {
+                if (!unit_ok(i)) continue;
+                uint32_t o[2 * W];
+#pragma unroll
+                for (int w = 0; w < W; ++w) quantize8(wv[i * W + w], s, o + 2 * w);
+                CT c;
+#pragma unroll
+                for (int j = 0; j < 2 * W; ++j) c[j] = o[j];
+                __builtin_nontemporal_store(c, row + i * tpr + tid);
             }
-            if (tid == 0) __builtin_nontemporal_store(s, (float*)(row + hq));
+            if (tid == 0) __builtin_nontemporal_store(s, (float*)((uint8_t*)row + hq));
         }
     }
+}
+
+// x_q[t] = codes of message recv_pos[t], scales[t] = its scale. One thread
+// per (row, unit) in 256-thread work-groups, the unit being 16 bytes when
+// rows of H bytes stay 16-byte aligned (H % 16 == 0) and 8 bytes otherwise;
+// the thread of unit 0 also copies the scale.
+template <typename U>
+__global__ __launch_bounds__(kFlatThreads) void quant_group_flat(
+    const uint8_t* __restrict__ msgs, int msg_bytes, int hq, int n_msgs,
+    const int* __restrict__ recv_pos, U* __restrict__ x_q, float* __restrict__ scales,
+    uint32_t total, FastDiv rowdiv) {
+    const uint32_t i = blockIdx.x * kFlatThreads + threadIdx.x;
+    if (i >= total) return;
+    const uint32_t t = fast_div(i, rowdiv);
+    const uint32_t u = i - t * rowdiv.d;
+    const int from = recv_pos[t];
+    if ((unsigned)from >= (unsigned)n_msgs) return;
+    const uint8_t* m = msgs + (size_t)from * msg_bytes;
+    __builtin_nontemporal_store(__builtin_nontemporal_load((const U*)m + u), x_q + i);
+    if (u == 0) scales[t] = *(const float*)(m + hq);
 }
 
 }  // namespace
@@ -174,22 +235,60 @@ extern "C" int mep_dispatch_quant(int T, int K, int H, const uint16_t* x, const 
     if (!aligned16(x) || !aligned16(send_msgs) || (smooth && !aligned16(smooth)))
         return MEP_ERR_SHAPE;
     const int nvec = H / 8;
-    const int nv = std::min(kQuantMaxNv, std::max(1, (nvec + kQuantThreads - 1) / kQuantThreads));
-    const RowShape rsh = row_shape(nvec, nv, kQuantThreads);
+    const int W = (nvec % 2) == 0 ? 2 : 1;  // 16 values per thread unit when possible
+    const int nunits = nvec / W;
+    const int nu = std::min(kQuantMaxNv, std::max(1, (nunits + kQuantThreads - 1) / kQuantThreads));
+    const RowShape rsh = row_shape(nunits, nu, kQuantThreads);
     const dim3 g((T + rsh.rpb - 1) / rsh.rpb), b(rsh.tpr * rsh.rpb);
     hipStream_t s = (hipStream_t)stream;
     const u32x4* xv = (const u32x4*)x;
     const int* re = (const int*)route_expert;
     const int* sp = (const int*)send_pos;
-#define MEP_QUANT_LAUNCH(N, SM)                                                                   \
-    hipLaunchKernelGGL((quant_pack_rows<N, SM>), g, b, 0, s, xv, smooth, E, re, sp, n_rows,      \
+#define MEP_QUANT_LAUNCH(WW, N, SM)                                                               \
+    hipLaunchKernelGGL((quant_pack_rows<WW, N, SM>), g, b, 0, s, xv, smooth, E, re, sp, n_rows,  \
                        send_msgs, msg_bytes, hq, T, K, nvec, rsh.tpr, rsh.rpb)
-    if (smooth) {
-        if (nv == 1) MEP_QUANT_LAUNCH(1, true); else MEP_QUANT_LAUNCH(2, true);
+    if (W == 2) {
+        if (smooth) {
+            if (nu == 1) MEP_QUANT_LAUNCH(2, 1, true); else MEP_QUANT_LAUNCH(2, 2, true);
+        } else {
+            if (nu == 1) MEP_QUANT_LAUNCH(2, 1, false); else MEP_QUANT_LAUNCH(2, 2, false);
+        }
     } else {
-        if (nv == 1) MEP_QUANT_LAUNCH(1, false); else MEP_QUANT_LAUNCH(2, false);
+        if (smooth) {
+            if (nu == 1) MEP_QUANT_LAUNCH(1, 1, true); else MEP_QUANT_LAUNCH(1, 2, true);
+        } else {
+            if (nu == 1) MEP_QUANT_LAUNCH(1, 1, false); else MEP_QUANT_LAUNCH(1, 2, false);
+        }
     }
 #undef MEP_QUANT_LAUNCH
+    MEP_LAUNCH_CHECK();
+    return MEP_OK;
+}
+
+extern "C" int mep_group_quant(int n, int H, int msg_bytes, const int32_t* recv_pos, int n_msgs,
+                               const uint8_t* recv_msgs, uint8_t* x_q, float* scales,
+                               void* stream) {
+    const int hq = (H + 31) / 32 * 32;
+    if (n < 0 || H < 8 || H > 65536 || (H % 8) != 0 || n_msgs < 0 || msg_bytes < hq + 4 ||
+        (msg_bytes % 16) != 0 || (long long)n * (H / 8) >= (1ll << 31))
+        return MEP_ERR_SHAPE;
+    if (n == 0) return MEP_OK;
+    if (!recv_pos || !x_q || !scales || (n_msgs > 0 && !recv_msgs)) return MEP_ERR_NULLPTR;
+    if ((recv_msgs && !aligned16(recv_msgs)) || ((uintptr_t)x_q & 7u) || ((uintptr_t)scales & 3u))
+        return MEP_ERR_SHAPE;
+    const bool wide = (H % 16) == 0 && aligned16(x_q);
+    const int unit = wide ? 16 : 8;
+    const uint32_t total = (uint32_t)n * (uint32_t)(H / unit);
+    const dim3 g((total + kFlatThreads - 1) / kFlatThreads), b(kFlatThreads);
+    const FastDiv dv = make_fastdiv((uint32_t)(H / unit));
+    if (wide)
+        hipLaunchKernelGGL(quant_group_flat<u32x4>, g, b, 0, (hipStream_t)stream, recv_msgs,
+                           msg_bytes, hq, n_msgs, (const int*)recv_pos, (u32x4*)x_q, scales,
+                           total, dv);
+    else
+        hipLaunchKernelGGL(quant_group_flat<u32x2>, g, b, 0, (hipStream_t)stream, recv_msgs,
+                           msg_bytes, hq, n_msgs, (const int*)recv_pos, (u32x2*)x_q, scales,
+                           total, dv);
     MEP_LAUNCH_CHECK();
     return MEP_OK;
 }

@@ -377,6 +377,25 @@ int mep_dispatch_quant(int T, int K, int H, const uint16_t* x, const float* smoo
                        const int32_t* route_expert, const int32_t* send_pos, int n_rows,
                        int msg_bytes, uint8_t* send_msgs, void* stream);
 
+/*
+ * mep_group_quant - receive side of the int8 dispatch: the arrival buffer
+ * of messages becomes the expert-side layout, int8 rows grouped by expert
+ * instance plus one fp32 scale per row ("aclnnMoeDistributeDispatchSetup"
+ * call example: received tokens come back as an int8 matrix and a vector of
+ * dynamic scales):
+ *   x_q[t, 0:H] = bytes [0, H) of recv_msgs[recv_pos[t]]
+ *   scales[t]   = fp32 at byte Align32(H) of recv_msgs[recv_pos[t]]
+ * for t in [0, n); an entry of recv_pos outside [0, n_msgs) leaves row t
+ * untouched.
+ *   recv_msgs [n_msgs, msg_bytes] (16-byte aligned, msg_bytes as in
+ *   mep_dispatch_quant); recv_pos [n] int32 (mep_plan's recv_pos);
+ *   x_q [n, H] int8 (8-byte aligned); scales [n] fp32.
+ * Sizes: n >= 0 (0 does nothing), 8 <= H <= 65536, H % 8 == 0,
+ * n*(H/8) < 2^31. Errors: MEP_ERR_NULLPTR, MEP_ERR_SHAPE, MEP_ERR_HIP.
+ */
+int mep_group_quant(int n, int H, int msg_bytes, const int32_t* recv_pos, int n_msgs,
+                    const uint8_t* recv_msgs, uint8_t* x_q, float* scales, void* stream);
+
 #ifdef __cplusplus
 }
 #endif

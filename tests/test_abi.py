@@ -35,7 +35,8 @@ def test_header_declares_the_four_entry_points():
     for n in ("mep_plan", "mep_remap_prune", "mep_dispatch", "mep_combine",
               "mep_plan_workspace_size", "mep_status_str", "mep_version",
               "mep_dispatch_to_peers", "mep_combine_from_peers", "mep_ungroup",
-              "mep_combine_add_rmsnorm", "mep_quant_msg_bytes", "mep_dispatch_quant"):
+              "mep_combine_add_rmsnorm", "mep_quant_msg_bytes", "mep_dispatch_quant",
+              "mep_group_quant"):
         assert n in names
 
 
@@ -213,3 +214,12 @@ def test_dispatch_quant_validation(B):
     assert f(4, 2, 64, 16, 16, 3, None, 16, 8, 512, 16, None) == B.MEP_ERR_PARAM     # no experts
     assert f(4, 2, 64, 16, 16, 0, 16, 16, 8, 512, 16, None) == B.MEP_ERR_PARAM       # E < 1
     assert f(4, 2, 64, 8, None, 0, None, 16, 8, 512, 16, None) == B.MEP_ERR_SHAPE    # unaligned x
+
+
+def test_group_quant_validation(B):
+    f = B.mep_group_quant
+    assert f(0, 64, 512, None, 0, None, None, None, None) == B.MEP_OK
+    assert f(4, 64, 512, 16, 4, 16, None, 16, None) == B.MEP_ERR_NULLPTR
+    assert f(4, 64, 64, 16, 4, 16, 16, 16, None) == B.MEP_ERR_SHAPE      # msg too small
+    assert f(4, 60, 512, 16, 4, 16, 16, 16, None) == B.MEP_ERR_SHAPE     # H % 8
+    assert f(4, 64, 512, 16, 4, 16, 12, 16, None) == B.MEP_ERR_SHAPE     # x_q not 8-aligned

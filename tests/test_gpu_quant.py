@@ -101,3 +101,45 @@ def test_quant_empty():
     m = cba.dispatch_quant(4, x, sp)
     torch.cuda.synchronize()
     assert m.shape[0] == 0
+
+
+@pytest.mark.parametrize("n,H,n_msgs", [(1, 8, 1), (37, 136, 40), (300, 2048, 320), (64, 7168, 64)])
+def test_group_quant_shapes(orc, n, H, n_msgs):
+    torch = require_gpu()
+    import combine_balancing_amd as cba
+    note(f"group_quant n={n} H={H}")
+    rng = np.random.default_rng(n + H)
+    x = synth.bf16_normal(rng, (n_msgs, H))
+    msgs = orc.dispatch_quant(x, np.arange(n_msgs, dtype=np.int32), 1)
+    rp = rng.integers(0, n_msgs, n).astype(np.int32)
+    rp[::9] = -1  # leaves the row untouched
+    xq = torch.full((n, H), 7, dtype=torch.int8, device="cuda")
+    sc = torch.full((n,), 3.0, dtype=torch.float32, device="cuda")
+    cba.group_quant(dev(msgs), dev(rp), H, x_q=xq, scales=sc)
+    torch.cuda.synchronize()
+    rxq = np.full((n, H), 7, np.uint8)
+    rsc = np.full(n, 3.0, np.float32)
+    gx, gs = orc.group_quant(msgs, rp, H)
+    ok = rp >= 0
+    rxq[ok], rsc[ok] = gx[ok], gs[ok]
+    assert np.array_equal(host(xq).view(np.uint8), rxq)
+    assert np.array_equal(host(sc), rsc)
+
+
+def test_int8_path_headline(orc):
+    # dsv3 rank 0: quantized pack -> (alltoallv stand-in: rank 0's own
+    # messages as the arrival buffer) -> receive-side split, vs the oracle
+    torch = require_gpu()
+    import combine_balancing_amd as cba
+    note("int8 path dsv3")
+    d = synth.make_plan_inputs("dsv3", stand_ins=False)
+    R, E, S, K, H = d["R"], d["E"], d["S"], d["K"], d["H"]
+    p = orc.plan(d["topk_ids"], R, E, S, K, m=0)
+    sp, rp = dev(p["send_pos"]), dev(p["recv_pos"])
+    msgs = cba.dispatch_quant(K, dev(d["x"]), sp)
+    xq, sc = cba.group_quant(msgs, rp, H)
+    torch.cuda.synchronize()
+    ref_m = orc.dispatch_quant(d["x"], p["send_pos"], K)
+    gx, gs = orc.group_quant(ref_m, p["recv_pos"], H)
+    assert np.array_equal(host(xq).view(np.uint8), gx)
+    assert np.array_equal(host(sc), gs)
