@@ -68,6 +68,8 @@ def _load():
     lib.oracle_dispatch_quant.restype = I
     lib.oracle_group_quant.argtypes = [I, I, I, P, I, P, P, P]
     lib.oracle_group_quant.restype = I
+    lib.oracle_weight_rows.argtypes = [I, I, I, P, P, P]
+    lib.oracle_weight_rows.restype = I
     lib.oracle_bf16_from_float.argtypes = [P, P, ctypes.c_int64]
     lib.oracle_bf16_from_float.restype = None
     lib.oracle_float_from_fp16.argtypes = [P, P, ctypes.c_int64]
@@ -316,6 +318,16 @@ def group_quant(msgs, recv_pos, H):
     _check(lib.oracle_group_quant(rp.size, H, mb, _p(rp), n_msgs, _p(m), _p(xq), _p(sc)),
            "oracle_group_quant")
     return xq, sc
+
+
+def weight_rows(plan, R, E, B):
+    """Weight row per instance [R, E] under B prefetch slots (oracle_weight_rows)."""
+    lib = _load()
+    ic = _c(plan["inst_count"], np.int32).reshape(-1)
+    ie = _c(plan["inst_expert"], np.int32).reshape(-1)
+    out = np.zeros((R, E), np.int32)
+    _check(lib.oracle_weight_rows(R, E, B, _p(ic), _p(ie), _p(out)), "oracle_weight_rows")
+    return out
 
 
 def bf16_from_float(a):

@@ -584,6 +584,41 @@ int oracle_group_quant(int n, int H, int msg_bytes, const int32_t* recv_pos, int
     return OR_OK;
 }
 
+/*
+ * oracle_weight_rows: the weight row each planned instance's expert GEMM
+ * reads, under a cap of B prefetch slots per rank ([MoonEP-TD] memory
+ * contract: the group GEMM's weights are one [E+B, H, H'] tensor, rows
+ * 0..E-1 the experts of all ranks, rows E..E+B-1 local prefetch slots;
+ * B = E/R for training, a smaller B (3-4) for inference, with instances
+ * beyond the slots served from the home rank). Reading: walk rank u's
+ * instances in local order; an instance whose expert is native to u
+ * (home(e) == u) reads row e; the j-th non-native (redundant) instance reads
+ * prefetch row E + j while j < B, else row e (the home rank's copy).
+ * Entries past inst_count[u] are -1.
+ */
+int oracle_weight_rows(int R, int E, int B, const int32_t* inst_count,
+                       const int32_t* inst_expert, int32_t* wrow) {
+    if (R < 1 || E < 1 || B < 0) return OR_ERR_ARG;
+    for (int u = 0; u < R; u++) {
+        int j = 0;
+        for (int i = 0; i < E; i++) {
+            int32_t* out = wrow + (int64_t)u * E + i;
+            if (i >= inst_count[u]) {
+                *out = -1;
+                continue;
+            }
+            const int e = inst_expert[(int64_t)u * E + i];
+            if (home_rank(e, R, E) == u) {
+                *out = e;
+            } else {
+                *out = j < B ? E + j : e;
+                j++;
+            }
+        }
+    }
+    return OR_OK;
+}
+
 /* Exposed for pinning the conversions in tests. */
 void oracle_bf16_from_float(const float* in, uint16_t* out, int64_t n) {
     for (int64_t i = 0; i < n; i++) out[i] = float_to_bf16_rne(in[i]);
