@@ -65,6 +65,8 @@ def lib():
     L.mep_dispatch_quant.restype = I
     L.mep_group_quant.argtypes = [I, I, I, P, I, P, P, P, P]
     L.mep_group_quant.restype = I
+    L.mep_plan_weight_rows.argtypes = [I, I, I, P, P, P, P]
+    L.mep_plan_weight_rows.restype = I
     _lib = L
     return L
 
@@ -149,3 +151,7 @@ def mep_dispatch_quant(T, K, H, x, smooth, E, route_expert, send_pos, n_rows, ms
 def mep_group_quant(n, H, msg_bytes, recv_pos, n_msgs, recv_msgs, x_q, scales, stream) -> int:
     return lib().mep_group_quant(n, H, msg_bytes, recv_pos, n_msgs, recv_msgs, x_q, scales,
                                  stream)
+
+
+def mep_plan_weight_rows(R, E, B, inst_count, inst_expert, inst_wrow, stream) -> int:
+    return lib().mep_plan_weight_rows(R, E, B, inst_count, inst_expert, inst_wrow, stream)

@@ -336,3 +336,17 @@ def group_quant(recv_msgs, recv_pos, H, x_q=None, scales=None, stream=None):
                            _need(scales, "scales", torch.float32, n), _stream_handle(stream))
     B.check("mep_group_quant", rc)
     return x_q, scales
+
+
+def plan_weight_rows(plan_out, R, E, prefetch_slots, inst_wrow=None, stream=None):
+    """mep_plan_weight_rows on mep_plan's outputs with B = prefetch_slots.
+    Returns inst_wrow [R, E]."""
+    ic, ie = plan_out["inst_count"], plan_out["inst_expert"]
+    if inst_wrow is None:
+        inst_wrow = torch.empty(R, E, dtype=torch.int32, device=ic.device)
+    rc = B.mep_plan_weight_rows(R, E, prefetch_slots, _need(ic, "inst_count", torch.int32, R),
+                                _need(ie, "inst_expert", torch.int32, R * E),
+                                _need(inst_wrow, "inst_wrow", torch.int32, R * E),
+                                _stream_handle(stream))
+    B.check("mep_plan_weight_rows", rc)
+    return inst_wrow

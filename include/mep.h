@@ -336,6 +336,26 @@ int mep_combine_add_rmsnorm(int T, int K, int H, const uint16_t* y_ret, int n_y,
                             uint16_t* x_out, uint16_t* y_out, float* rstd_out,
                             void* stream);
 
+/*
+ * mep_plan_weight_rows - the weight row each planned instance's expert GEMM
+ * reads under a cap of B prefetch slots per rank ("MoonEP" technical
+ * overview, memory contract: weights are one [E+B, H, H'] tensor, rows
+ * 0..E-1 the experts of all ranks, rows E..E+B-1 a rank's prefetch slots;
+ * B = E/R for training, 3-4 for inference, redundant experts beyond the
+ * slots served from their home rank). For rank u and local index i of
+ * mep_plan's instance tables:
+ *   inst_wrow[u*E+i] = e        for a native instance (home(e) == u)
+ *                    = E + j    for the j-th redundant instance, j < B
+ *                    = e        for the j-th redundant instance, j >= B
+ *                    = -1       for i >= inst_count[u]
+ *   inst_count [R], inst_expert [R*E] from mep_plan (the plan's local
+ *   layout, natives first, is assumed); inst_wrow [R*E] int32 out.
+ * Sizes: 1 <= R, E <= 1024, B >= 0.
+ * Errors: MEP_ERR_NULLPTR, MEP_ERR_PARAM (B < 0), MEP_ERR_SHAPE, MEP_ERR_HIP.
+ */
+int mep_plan_weight_rows(int R, int E, int B, const int32_t* inst_count,
+                         const int32_t* inst_expert, int32_t* inst_wrow, void* stream);
+
 /* -------------------------------------------------------- int8 dispatch */
 
 /*

@@ -36,7 +36,7 @@ def test_header_declares_the_four_entry_points():
               "mep_plan_workspace_size", "mep_status_str", "mep_version",
               "mep_dispatch_to_peers", "mep_combine_from_peers", "mep_ungroup",
               "mep_combine_add_rmsnorm", "mep_quant_msg_bytes", "mep_dispatch_quant",
-              "mep_group_quant"):
+              "mep_group_quant", "mep_plan_weight_rows"):
         assert n in names
 
 
@@ -223,3 +223,11 @@ def test_group_quant_validation(B):
     assert f(4, 64, 64, 16, 4, 16, 16, 16, None) == B.MEP_ERR_SHAPE      # msg too small
     assert f(4, 60, 512, 16, 4, 16, 16, 16, None) == B.MEP_ERR_SHAPE     # H % 8
     assert f(4, 64, 512, 16, 4, 16, 12, 16, None) == B.MEP_ERR_SHAPE     # x_q not 8-aligned
+
+
+def test_plan_weight_rows_validation(B):
+    f = B.mep_plan_weight_rows
+    assert f(0, 8, 2, 16, 16, 16, None) == B.MEP_ERR_SHAPE
+    assert f(4, 2000, 2, 16, 16, 16, None) == B.MEP_ERR_SHAPE
+    assert f(4, 8, -1, 16, 16, 16, None) == B.MEP_ERR_PARAM
+    assert f(4, 8, 2, None, 16, 16, None) == B.MEP_ERR_NULLPTR

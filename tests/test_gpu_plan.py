@@ -138,3 +138,20 @@ def test_plan_skew_sweep(orc, target):
         got = _gpu_plan(d["topk_ids"], R, E, S, K, m)
         ref = orc.plan(d["topk_ids"], R, E, S, K, m=m)
         _assert_same(ref, got, f"sweep {target} m={m}")
+
+
+@pytest.mark.parametrize("name", ["tiny", "small", "dsv3", "large_skew"])
+def test_plan_weight_rows(orc, name):
+    # the prefetch-slot table for B = 0, 3 (inference) and E/R (training),
+    # from the GPU plan, against the oracle's on the oracle plan
+    torch = require_gpu()
+    import combine_balancing_amd as cba
+    d = synth.make_routing(name)
+    R, E, S, K = d["R"], d["E"], d["S"], d["K"]
+    note(f"plan weight rows {name}")
+    p = cba.plan(dev(d["topk_ids"].reshape(-1)), R, E, S, K, my_rank=0, with_routes=False)
+    ref = orc.plan(d["topk_ids"], R, E, S, K, m=0)
+    for slots in (0, 3, max(1, E // R)):
+        w = cba.plan_weight_rows(p, R, E, slots)
+        torch.cuda.synchronize()
+        assert np.array_equal(host(w), orc.weight_rows(ref, R, E, slots)), slots
