@@ -70,6 +70,8 @@ def _load():
     lib.oracle_group_quant.restype = I
     lib.oracle_weight_rows.argtypes = [I, I, I, P, P, P]
     lib.oracle_weight_rows.restype = I
+    lib.oracle_plan_dedup.argtypes = [I, I, I, I, P, P, P, P, P, P]
+    lib.oracle_plan_dedup.restype = I
     lib.oracle_bf16_from_float.argtypes = [P, P, ctypes.c_int64]
     lib.oracle_bf16_from_float.restype = None
     lib.oracle_float_from_fp16.argtypes = [P, P, ctypes.c_int64]
@@ -327,6 +329,22 @@ def weight_rows(plan, R, E, B):
     ie = _c(plan["inst_expert"], np.int32).reshape(-1)
     out = np.zeros((R, E), np.int32)
     _check(lib.oracle_weight_rows(R, E, B, _p(ic), _p(ie), _p(out)), "oracle_weight_rows")
+    return out
+
+
+def plan_dedup(plan, R, S, K, m):
+    """Per-destination dedup maps of rank m from the global plan
+    (oracle_plan_dedup): dpack_pos [S*K], dsend_count [R], drecv_pos [S*K],
+    drecv_count [R]."""
+    lib = _load()
+    C = S * K
+    rd = _c(plan["route_dest"], np.int32).reshape(-1)
+    rs = _c(plan["route_slot"], np.int32).reshape(-1)
+    out = dict(dpack_pos=np.zeros(C, np.int32), dsend_count=np.zeros(R, np.int32),
+               drecv_pos=np.zeros(C, np.int32), drecv_count=np.zeros(R, np.int32))
+    _check(lib.oracle_plan_dedup(R, S, K, m, _p(rd), _p(rs), _p(out["dpack_pos"]),
+                                 _p(out["dsend_count"]), _p(out["drecv_pos"]),
+                                 _p(out["drecv_count"])), "oracle_plan_dedup")
     return out
 
 

@@ -619,6 +619,92 @@ int oracle_weight_rows(int R, int E, int B, const int32_t* inst_count,
     return OR_OK;
 }
 
+/*
+ * oracle_plan_dedup: per-destination token dedup of rank m's dispatch
+ * ("MoonEP API完全参考", §5.2 communication performance: a check of the
+ * dedup encoding of sent tokens is named there, nothing more). Reading: a token with several routes to one destination rank is
+ * sent there once; the receiver fans the row out to each of the token's
+ * grouped slots on that rank. From the global plan's route maps:
+ *   D(g)             = { route_dest[g*K + k] : k < K } for global token
+ *                      g = src*S + t
+ *   send buffer of m : one row per (t, d) with d in D(m*S + t), ordered by
+ *                      (d ascending, t ascending); dsend_count[d] = rows
+ *                      for d
+ *   dpack_pos[t*K+k] = that row for the first k of t with destination d,
+ *                      -1 for t's later routes to the same d
+ *   arrival on m     : sources ascending, each source's rows to m in token
+ *                      order; drecv_count[src] = rows from src
+ *   drecv_pos[slot]  = arrival row of the token whose route occupies
+ *                      grouped slot `slot` on m
+ * Pack with dpack_pos, exchange the segments, group with drecv_pos: the
+ * grouped buffer equals the one of the plan's own maps.
+ */
+int oracle_plan_dedup(int R, int S, int K, int m, const int32_t* route_dest,
+                      const int32_t* route_slot, int32_t* dpack_pos, int32_t* dsend_count,
+                      int32_t* drecv_pos, int32_t* drecv_count) {
+    if (R < 1 || S < 1 || K < 1 || m < 0 || m >= R) return OR_ERR_ARG;
+    const int64_t C = (int64_t)S * K;
+    /* sender side: count per destination, then rows in (d, t) order */
+    for (int d = 0; d < R; d++) dsend_count[d] = 0;
+    for (int64_t t = 0; t < S; t++)
+        for (int k = 0; k < K; k++) {
+            const int32_t d = route_dest[((int64_t)m * S + t) * K + k];
+            int first = 1;
+            for (int k2 = 0; k2 < k; k2++)
+                if (route_dest[((int64_t)m * S + t) * K + k2] == d) first = 0;
+            if (first && d >= 0 && d < R) dsend_count[d]++;
+        }
+    int64_t* base = (int64_t*)malloc(sizeof(int64_t) * (size_t)R);
+    int64_t* next = (int64_t*)malloc(sizeof(int64_t) * (size_t)R);
+    int64_t* arr = (int64_t*)malloc(sizeof(int64_t) * (size_t)R * S);
+    if (!base || !next || !arr) {
+        free(base);
+        free(next);
+        free(arr);
+        return OR_ERR_ALLOC;
+    }
+    int64_t run = 0;
+    for (int d = 0; d < R; d++) {
+        base[d] = run;
+        next[d] = 0;
+        run += dsend_count[d];
+    }
+    for (int64_t t = 0; t < S; t++)
+        for (int k = 0; k < K; k++) {
+            const int32_t d = route_dest[((int64_t)m * S + t) * K + k];
+            int first = 1;
+            for (int k2 = 0; k2 < k; k2++)
+                if (route_dest[((int64_t)m * S + t) * K + k2] == d) first = 0;
+            if (first && d >= 0 && d < R) dpack_pos[t * K + k] = (int32_t)(base[d] + next[d]++);
+            else dpack_pos[t * K + k] = -1;
+        }
+    /* receiver side: arrival row of every global token that reaches m */
+    run = 0;
+    for (int src = 0; src < R; src++) {
+        int64_t cnt = 0;
+        for (int64_t t = 0; t < S; t++) {
+            const int64_t g = (int64_t)src * S + t;
+            int reaches = 0;
+            for (int k = 0; k < K; k++)
+                if (route_dest[g * K + k] == m) reaches = 1;
+            arr[g] = reaches ? run + cnt : -1;
+            cnt += reaches;
+        }
+        drecv_count[src] = (int32_t)cnt;
+        run += cnt;
+    }
+    for (int64_t s2 = 0; s2 < C; s2++) drecv_pos[s2] = -1;
+    for (int64_t f = 0; f < (int64_t)R * C; f++)
+        if (route_dest[f] == m) {
+            const int32_t sl = route_slot[f];
+            if (sl >= 0 && sl < C) drecv_pos[sl] = (int32_t)arr[f / K];
+        }
+    free(base);
+    free(next);
+    free(arr);
+    return OR_OK;
+}
+
 /* Exposed for pinning the conversions in tests. */
 void oracle_bf16_from_float(const float* in, uint16_t* out, int64_t n) {
     for (int64_t i = 0; i < n; i++) out[i] = float_to_bf16_rne(in[i]);
