@@ -282,6 +282,52 @@ def int8_dispatch(torch, cba, d, pout, steps, flush=None):
             "bytes_sent_vs_bf16": round(C * mb / (C * H * 2), 4)}
 
 
+def dedup_dispatch(torch, cba, d, pout, steps, flush=None):
+    """Per-destination dedup at the same workload: the dedup maps from the
+    plan, the pack of one row per (token, destination), and the grouping
+    that fans the arrival rows out to the C grouped slots (the arrival
+    buffer here is a stand-in of the dedup arrival count's rows)."""
+    R, S, K, H, C = d["R"], d["S"], d["K"], d["H"], d["C"]
+    x = _dev(torch, d["x"])
+    ws = torch.empty(cba.lib().mep_plan_dedup_workspace_size(R, S, K), dtype=torch.uint8,
+                     device="cuda")
+    q = cba.plan_dedup(pout, R, S, K, 0, workspace=ws)
+    torch.cuda.synchronize()
+    n_send = int(q["dsend_count"].sum().item())
+    n_arr = int(q["drecv_count"].sum().item())
+    send = torch.empty(n_send, H, dtype=torch.bfloat16, device="cuda")
+    g = torch.Generator(device="cuda")
+    g.manual_seed(13)
+    raw = torch.randn(n_arr, H, device="cuda", generator=g).to(torch.bfloat16)
+    grouped = torch.empty(C, H, dtype=torch.bfloat16, device="cuda")
+    stream = torch.cuda.current_stream()
+    t = {"maps": [], "pack": [], "group": []}
+    for it in range(steps + 3):
+        if flush is not None:
+            flush.fill_(it & 0xFF)
+        ev = [torch.cuda.Event(enable_timing=True) for _ in range(4)]
+        ev[0].record(stream)
+        cba.plan_dedup(pout, R, S, K, 0, workspace=ws, out=q)
+        ev[1].record(stream)
+        cba.dispatch(K, x=x, send_pos=q["dpack_pos"], send_buf=send)
+        ev[2].record(stream)
+        cba.dispatch(K, recv_raw=raw, recv_pos=q["drecv_pos"], recv_grouped=grouped)
+        ev[3].record(stream)
+        torch.cuda.synchronize()
+        if it >= 3:
+            for j, k in enumerate(("maps", "pack", "group")):
+                t[k].append(ev[j].elapsed_time(ev[j + 1]) * 1e3)
+    us = {k: float(np.mean(v)) for k, v in t.items()}
+    row = H * 2
+    nb = {"pack": S * row + n_send * row + C * 4, "group": n_arr * row + C * row + C * 4}
+    return {"maps_us": round(us["maps"], 2), "pack_us": round(us["pack"], 2),
+            "pack_GBs": round(nb["pack"] / (us["pack"] * 1e-6) / 1e9, 1),
+            "group_us": round(us["group"], 2),
+            "group_GBs": round(nb["group"] / (us["group"] * 1e-6) / 1e9, 1),
+            "rows_sent": n_send, "rows_arrived": n_arr, "rows_sent_vs_plain": round(n_send / C, 4),
+            "algorithmic_bytes": nb}
+
+
 def main():
     ap = argparse.ArgumentParser()
     ap.add_argument("--gpus", type=int, default=1)
@@ -435,6 +481,8 @@ def main():
                                             steps=max(5, min(args.steps, 20)), flush=flush)
     res["int8_dispatch"] = int8_dispatch(torch, cba, d, pout, steps=max(5, min(args.steps, 20)),
                                          flush=flush)
+    res["dedup_dispatch"] = dedup_dispatch(torch, cba, d, pout,
+                                           steps=max(5, min(args.steps, 20)), flush=flush)
     if not args.no_zero_copy:
         res["zero_copy"] = zero_copy(torch, cba, d, pout, steps=max(5, min(args.steps, 20)),
                                      flush=flush)

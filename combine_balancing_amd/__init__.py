@@ -8,5 +8,5 @@ been built (``python -m combine_balancing_amd.build``).
 """
 from .api import (combine, combine_add_rmsnorm, combine_from_peers, dispatch,  # noqa: F401
                   dispatch_quant, dispatch_to_peers, group_quant, peer_table, plan, plan_outputs,
-                  plan_weight_rows, plan_workspace, quant_msg_bytes, remap_prune, ungroup)
+                  plan_dedup, plan_weight_rows, plan_workspace, quant_msg_bytes, remap_prune, ungroup)
 from ._binding import MepError, lib  # noqa: F401

@@ -67,6 +67,10 @@ def lib():
     L.mep_group_quant.restype = I
     L.mep_plan_weight_rows.argtypes = [I, I, I, P, P, P, P]
     L.mep_plan_weight_rows.restype = I
+    L.mep_plan_dedup_workspace_size.argtypes = [I, I, I]
+    L.mep_plan_dedup_workspace_size.restype = Z
+    L.mep_plan_dedup.argtypes = [I, I, I, I, P, P, P, Z, P, P, P, P, P]
+    L.mep_plan_dedup.restype = I
     _lib = L
     return L
 
@@ -155,3 +159,14 @@ def mep_group_quant(n, H, msg_bytes, recv_pos, n_msgs, recv_msgs, x_q, scales, s
 
 def mep_plan_weight_rows(R, E, B, inst_count, inst_expert, inst_wrow, stream) -> int:
     return lib().mep_plan_weight_rows(R, E, B, inst_count, inst_expert, inst_wrow, stream)
+
+
+def mep_plan_dedup_workspace_size(R, S, K) -> int:
+    return lib().mep_plan_dedup_workspace_size(R, S, K)
+
+
+def mep_plan_dedup(R, S, K, my_rank, route_dest, route_slot, workspace, workspace_bytes,
+                   dpack_pos, dsend_count, drecv_pos, drecv_count, stream) -> int:
+    return lib().mep_plan_dedup(R, S, K, my_rank, route_dest, route_slot, workspace,
+                                workspace_bytes, dpack_pos, dsend_count, drecv_pos, drecv_count,
+                                stream)

@@ -156,16 +156,21 @@ def dispatch(K, x=None, send_pos=None, send_buf=None, recv_raw=None, recv_pos=No
         T, H = x.shape
         if send_buf is None:
             send_buf = torch.zeros(T * K, H, dtype=x.dtype, device=x.device)
-        if send_buf.dim() != 2 or send_buf.shape[1] != H or send_buf.shape[0] < T * K:
-            raise ValueError("send_buf must be [>= T*K, H]")
+        # the send buffer holds every row send_pos names: T*K rows for the
+        # plan's map, fewer for a dedup map
+        if send_buf.dim() != 2 or send_buf.shape[1] != H:
+            raise ValueError("send_buf must be [rows, H]")
     n = 0
     if recv_raw is not None:
-        n, H2 = recv_raw.shape
+        n_raw, H2 = recv_raw.shape
         if x is not None and H2 != H:
             raise ValueError("x and recv_raw disagree on H")
         H = H2
+        # grouped rows: one per recv_pos entry (the arrival buffer may be
+        # shorter when a dedup map fans rows out)
+        n = recv_pos.numel() if recv_pos is not None else n_raw
         if recv_grouped is None:
-            recv_grouped = torch.empty_like(recv_raw)
+            recv_grouped = torch.empty(n, H, dtype=recv_raw.dtype, device=recv_raw.device)
     rc = B.mep_dispatch(
         T, K, H, _opt(x, "x", _BF16_LIKE),
         _opt(send_pos, "send_pos", torch.int32, T * K if x is not None else None),
@@ -350,3 +355,31 @@ def plan_weight_rows(plan_out, R, E, prefetch_slots, inst_wrow=None, stream=None
                                 _stream_handle(stream))
     B.check("mep_plan_weight_rows", rc)
     return inst_wrow
+
+
+def plan_dedup(plan_out, R, S, K, my_rank, workspace=None, out=None, stream=None):
+    """mep_plan_dedup on mep_plan's route maps. Returns dict(dpack_pos,
+    dsend_count, drecv_pos, drecv_count)."""
+    rd, rs = plan_out["route_dest"], plan_out["route_slot"]
+    if rd is None or rs is None:
+        raise ValueError("the plan must carry route_dest and route_slot")
+    dev = rd.device
+    C = S * K
+    if workspace is None:
+        n = B.mep_plan_dedup_workspace_size(R, S, K)
+        if n == 0:
+            raise ValueError(f"unsupported dedup sizes R={R} S={S} K={K}")
+        workspace = torch.empty(n, dtype=torch.uint8, device=dev)
+    if out is None:
+        i32 = dict(dtype=torch.int32, device=dev)
+        out = dict(dpack_pos=torch.empty(C, **i32), dsend_count=torch.empty(R, **i32),
+                   drecv_pos=torch.empty(C, **i32), drecv_count=torch.empty(R, **i32))
+    rc = B.mep_plan_dedup(
+        R, S, K, my_rank, _need(rd, "route_dest", torch.int32, R * C),
+        _need(rs, "route_slot", torch.int32, R * C), _need(workspace, "workspace", torch.uint8),
+        workspace.numel(), _need(out["dpack_pos"], "dpack_pos", torch.int32, C),
+        _need(out["dsend_count"], "dsend_count", torch.int32, R),
+        _need(out["drecv_pos"], "drecv_pos", torch.int32, C),
+        _need(out["drecv_count"], "drecv_count", torch.int32, R), _stream_handle(stream))
+    B.check("mep_plan_dedup", rc)
+    return out

@@ -1,0 +1,314 @@
+// Per-destination token dedup of this rank's dispatch.
+//
+// Method ("MoonEP API完全参考", §5.2 communication performance, which names a
+// dedup encoding of sent tokens): a token with several routes to one
+// destination rank is sent there once, and the receiver fans the row out to
+// each of the token's grouped slots. From the global plan's route maps:
+//   D(g)         destinations of global token g = src*S + t
+//   Q[g][d]      number of global tokens g' < g with d in D(g')
+// this rank m's send buffer holds one row per (t, d), d in D(m*S+t), in
+// (d, t) order:
+//   dpack_pos[t*K+k] = segbase[d] + Q[m*S+t][d] - Q[m*S][d] for the first
+//                      route of t to d (-1 for t's later routes to d)
+//   dsend_count[d]   = Q[(m+1)*S][d] - Q[m*S][d]
+// and its arrival buffer holds the rows reaching m, sources ascending, each
+// in token order, which is global token order, so
+//   drecv_pos[slot]  = Q[g][m] for the route of g occupying slot on m
+//   drecv_count[src] = Q[(src+1)*S][m] - Q[src*S][m].
+//
+// Three launches (latency-bound, like the plan):
+//   dedup_count  one 1024-thread work-group per chunk of 1024 tokens (chunks
+//                never straddle a source): each token's destination bit
+//                mask, then per-destination counts by wave ballots
+//   dedup_scan   one work-group: per destination, exclusive scan of the
+//                chunk counts (16 threads per destination, DPP-free: a
+//                16-lane shuffle scan), plus the send/receive counts and
+//                segment bases of rank m
+//   dedup_maps   per chunk: the token's routes loaded once (destinations
+//                and slots together), Q of every token for its destinations
+//                from the chunk base, the wave bases and the token's rank in
+//                its wave's ballot (kept in LDS); writes the three maps
+// R <= 64 (a token's destinations fit one 64-bit mask).
+#include "mep_device.h"
+
+namespace mep {
+namespace {
+
+constexpr int kDedupThreads = 1024;
+constexpr int kDedupChunk = kDedupThreads;  // tokens per chunk
+constexpr int kDedupWaves = kDedupThreads / kWave;
+constexpr int kDedupMaxR = 64;
+
+struct DedupDims {
+    int R, S, K, m, cps, nchunks;
+};
+
+struct DedupWs {
+    int* cnt;        // [nchunks][R]
+    int* base;       // [nchunks][R] exclusive over chunks
+    int* segbase;    // [R]: rank m's send segment bases
+    int* q0;         // [R]: Q[m*S][d]
+};
+
+// Calls f(k, d) for each route k of global token g with destination d. A
+// token's K destinations are contiguous: with K % 4 == 0 they are read as
+// 16-byte vectors (a lane's routes in K/4 loads, not K), else 8 scalar loads
+// at a time; either way the loads of a batch are in flight together.
+template <typename F>
+__device__ __forceinline__ void for_routes(const int* __restrict__ route_dest, size_t g, int K,
+                                           F f) {
+    if ((K & 3) == 0) {
+        const i32x4* p = (const i32x4*)(route_dest + g * K);
+        for (int k0 = 0; k0 < K; k0 += 16) {
+            i32x4 v[4];
+#pragma unroll
+            for (int j = 0; j < 4; ++j)
+                if (k0 + 4 * j < K) v[j] = p[k0 / 4 + j];
+#pragma unroll
+            for (int j = 0; j < 4; ++j)
+                if (k0 + 4 * j < K)
+#pragma unroll
+                    for (int i = 0; i < 4; ++i) f(k0 + 4 * j + i, v[j][i]);
+        }
+        return;
+    }
+    for (int k0 = 0; k0 < K; k0 += 8) {
+        int d[8];
+#pragma unroll
+        for (int j = 0; j < 8; ++j) d[j] = k0 + j < K ? route_dest[g * K + k0 + j] : -1;
+#pragma unroll
+        for (int j = 0; j < 8; ++j)
+            if (k0 + j < K) f(k0 + j, d[j]);
+    }
+}
+
+__device__ __forceinline__ uint64_t token_mask(const int* __restrict__ route_dest, size_t g, int K,
+                                               int R) {
+    uint64_t mk = 0;
+    for_routes(route_dest, g, K, [&](int, int d) {
+        if ((unsigned)d < (unsigned)R) mk |= 1ull << d;
+    });
+    return mk;
+}
+
+__device__ __forceinline__ uint64_t ballot64(bool p) { return __ballot(p); }
+
+__global__ __launch_bounds__(kDedupThreads) void dedup_count(DedupDims dd, DedupWs w,
+                                                             const int* __restrict__ route_dest) {
+    __shared__ int s_cnt[kDedupWaves][kDedupMaxR];
+    const int c = blockIdx.x;
+    const int src = c / dd.cps, sub = c - src * dd.cps;
+    const int t = sub * kDedupChunk + threadIdx.x;
+    const bool valid = t < dd.S;
+    const size_t g = (size_t)src * dd.S + (valid ? t : 0);
+    const uint64_t mk = valid ? token_mask(route_dest, g, dd.K, dd.R) : 0ull;
+    const int wave = threadIdx.x / kWave;
+    for (int d = 0; d < dd.R; ++d) {
+        const uint64_t b = ballot64((mk >> d) & 1ull);
+        if (lane_id() == 0) s_cnt[wave][d] = __popcll(b);
+    }
+    lds_barrier();
+    for (int d = threadIdx.x; d < dd.R; d += kDedupThreads) {
+        int run = 0;
+        for (int v = 0; v < kDedupWaves; ++v) run += s_cnt[v][d];
+        w.cnt[(size_t)c * dd.R + d] = run;
+    }
+}
+
+// 16 threads per destination, destinations in groups of 64 (16 * 64 = 1024)
+__global__ __launch_bounds__(kDedupThreads) void dedup_scan(DedupDims dd, DedupWs w,
+                                                            int* __restrict__ dsend_count,
+                                                            int* __restrict__ drecv_count) {
+    __shared__ int s_q0[kDedupMaxR], s_q1[kDedupMaxR];
+    const int d = threadIdx.x >> 4;  // 0..63
+    const int part = threadIdx.x & 15;
+    const int per = (dd.nchunks + 15) / 16;
+    const int c0 = min(part * per, dd.nchunks), c1 = min(c0 + per, dd.nchunks);
+    int sum = 0;
+    if (d < dd.R)
+        for (int c = c0; c < c1; ++c) sum += w.cnt[(size_t)c * dd.R + d];
+    // exclusive scan of the 16 part sums of this destination (16 adjacent lanes)
+    int incl = sum;
+#pragma unroll
+    for (int o = 1; o < 16; o <<= 1) {
+        const int y = __shfl_up(incl, o, 16);
+        if (part >= o) incl += y;
+    }
+    int run = incl - sum;
+    if (d < dd.R) {
+        for (int c = c0; c < c1; ++c) {
+            w.base[(size_t)c * dd.R + d] = run;
+            run += w.cnt[(size_t)c * dd.R + d];
+        }
+    }
+    // the bases just stored (global memory) are read back below by other
+    // threads of this work-group: a full barrier, which waits for the stores
+    __syncthreads();
+    // rank m's counts: Q at the source boundaries
+    if (threadIdx.x < dd.R) {
+        const int dst = threadIdx.x;
+        const int cm0 = dd.m * dd.cps, cm1 = cm0 + dd.cps;
+        s_q0[dst] = w.base[(size_t)cm0 * dd.R + dst];
+        s_q1[dst] = cm1 < dd.nchunks ? w.base[(size_t)cm1 * dd.R + dst]
+                                     : w.base[(size_t)(dd.nchunks - 1) * dd.R + dst] +
+                                           w.cnt[(size_t)(dd.nchunks - 1) * dd.R + dst];
+    }
+    lds_barrier();
+    if (threadIdx.x == 0) {
+        int acc = 0;
+        for (int dst = 0; dst < dd.R; ++dst) {
+            const int n = s_q1[dst] - s_q0[dst];
+            w.segbase[dst] = acc;
+            w.q0[dst] = s_q0[dst];
+            dsend_count[dst] = n;
+            acc += n;
+        }
+    }
+    // tokens of each source reaching m
+    for (int src = threadIdx.x; src < dd.R; src += kDedupThreads) {
+        int n = 0;
+        for (int c = src * dd.cps; c < (src + 1) * dd.cps; ++c) n += w.cnt[(size_t)c * dd.R + dd.m];
+        drecv_count[src] = n;
+    }
+}
+
+__global__ __launch_bounds__(kDedupThreads) void dedup_maps(DedupDims dd, DedupWs w,
+                                                            const int* __restrict__ route_dest,
+                                                            const int* __restrict__ route_slot,
+                                                            int* __restrict__ dpack_pos,
+                                                            int* __restrict__ drecv_pos) {
+    __shared__ uint64_t s_bal[kDedupWaves][kDedupMaxR];
+    __shared__ int s_wbase[kDedupWaves][kDedupMaxR];
+    __shared__ int s_cbase[kDedupMaxR];
+    __shared__ int s_seg[kDedupMaxR];  // segbase - q0: send row = s_seg[d] + Q
+    const int c = blockIdx.x;
+    const int src = c / dd.cps, sub = c - src * dd.cps;
+    const int t = sub * kDedupChunk + threadIdx.x;
+    const bool valid = t < dd.S;
+    const size_t g = (size_t)src * dd.S + (valid ? t : 0);
+    // the token's first kRegRoutes destinations are loaded up front and
+    // reused for every map
+    constexpr int kRegRoutes = 16;
+    int rd[kRegRoutes];
+#pragma unroll
+    for (int k = 0; k < kRegRoutes; ++k) rd[k] = -1;
+    uint64_t mk = 0;
+    if (valid)
+        for_routes(route_dest, g, dd.K, [&](int k, int d) {
+            if (k < kRegRoutes) rd[k] = d;
+            if ((unsigned)d < (unsigned)dd.R) mk |= 1ull << d;
+        });
+    const int wave = threadIdx.x / kWave;
+    for (int d = 0; d < dd.R; ++d) {
+        const uint64_t b = ballot64((mk >> d) & 1ull);
+        if (lane_id() == 0) s_bal[wave][d] = b;
+    }
+    if (threadIdx.x < dd.R) {
+        s_cbase[threadIdx.x] = w.base[(size_t)c * dd.R + threadIdx.x];
+        s_seg[threadIdx.x] = w.segbase[threadIdx.x] - w.q0[threadIdx.x];
+    }
+    lds_barrier();
+    for (int d = threadIdx.x; d < dd.R; d += kDedupThreads) {
+        int run = 0;
+        for (int v = 0; v < kDedupWaves; ++v) {
+            s_wbase[v][d] = run;
+            run += __popcll(s_bal[v][d]);
+        }
+    }
+    lds_barrier();
+    if (!valid) return;
+    const uint64_t below = (1ull << lane_id()) - 1ull;
+    auto q_of = [&](int d) {
+        return s_cbase[d] + s_wbase[wave][d] + __popcll(s_bal[wave][d] & below);
+    };
+    const bool reaches_m = (mk >> dd.m) & 1ull;
+    if (src != dd.m && !reaches_m) return;
+    const int row_m = reaches_m ? q_of(dd.m) : 0;
+    const int C = dd.S * dd.K;
+    uint64_t seen = 0;
+    auto visit = [&](int k, int d) {
+        if (src == dd.m) {
+            int p = -1;
+            if ((unsigned)d < (unsigned)dd.R && !((seen >> d) & 1ull)) {
+                seen |= 1ull << d;
+                p = s_seg[d] + q_of(d);
+            }
+            dpack_pos[(size_t)t * dd.K + k] = p;
+        }
+        if (d == dd.m) {
+            const int sl = route_slot[g * dd.K + k];
+            if ((unsigned)sl < (unsigned)C) drecv_pos[sl] = row_m;
+        }
+    };
+#pragma unroll
+    for (int k = 0; k < kRegRoutes; ++k)
+        if (k < dd.K) visit(k, rd[k]);
+    for (int k = kRegRoutes; k < dd.K; ++k) visit(k, route_dest[g * dd.K + k]);
+}
+
+bool dedup_dims(int R, int S, int K, int m, DedupDims* d) {
+    if (R < 1 || R > kDedupMaxR || S < 1 || K < 1 || m < 0 || m >= R) return false;
+    if ((long long)R * S * K > (1ll << 30)) return false;
+    d->R = R;
+    d->S = S;
+    d->K = K;
+    d->m = m;
+    d->cps = (S + kDedupChunk - 1) / kDedupChunk;
+    d->nchunks = R * d->cps;
+    return true;
+}
+
+size_t ws_bytes(const DedupDims& d, size_t* off_cnt, size_t* off_base, size_t* off_seg,
+                size_t* off_q0) {
+    auto up = [](size_t b) { return (b + 255) & ~size_t(255); };
+    size_t at = 0;
+    *off_cnt = at;
+    at += up((size_t)d.nchunks * d.R * sizeof(int));
+    *off_base = at;
+    at += up((size_t)d.nchunks * d.R * sizeof(int));
+    *off_seg = at;
+    at += up((size_t)d.R * sizeof(int));
+    *off_q0 = at;
+    at += up((size_t)d.R * sizeof(int));
+    return at;
+}
+
+}  // namespace
+}  // namespace mep
+
+using namespace mep;
+
+extern "C" size_t mep_plan_dedup_workspace_size(int R, int S, int K) {
+    DedupDims d;
+    if (!dedup_dims(R, S, K, 0, &d)) return 0;
+    size_t a, b, c, e;
+    return ws_bytes(d, &a, &b, &c, &e);
+}
+
+extern "C" int mep_plan_dedup(int R, int S, int K, int my_rank, const int32_t* route_dest,
+                              const int32_t* route_slot, void* workspace, size_t workspace_bytes,
+                              int32_t* dpack_pos, int32_t* dsend_count, int32_t* drecv_pos,
+                              int32_t* drecv_count, void* stream) {
+    DedupDims d;
+    if (my_rank < 0 || my_rank >= R) return MEP_ERR_PARAM;
+    if (!dedup_dims(R, S, K, my_rank, &d)) return MEP_ERR_SHAPE;
+    if (!route_dest || !route_slot || !workspace || !dpack_pos || !dsend_count || !drecv_pos ||
+        !drecv_count)
+        return MEP_ERR_NULLPTR;
+    size_t oc, ob, os, oq;
+    if (workspace_bytes < ws_bytes(d, &oc, &ob, &os, &oq)) return MEP_ERR_PARAM;
+    if ((uintptr_t)workspace & 255u) return MEP_ERR_SHAPE;
+    char* base = (char*)workspace;
+    DedupWs w{(int*)(base + oc), (int*)(base + ob), (int*)(base + os), (int*)(base + oq)};
+    hipStream_t s = (hipStream_t)stream;
+    const int* rd = (const int*)route_dest;
+    hipLaunchKernelGGL(dedup_count, dim3(d.nchunks), dim3(kDedupThreads), 0, s, d, w, rd);
+    MEP_LAUNCH_CHECK();
+    hipLaunchKernelGGL(dedup_scan, dim3(1), dim3(kDedupThreads), 0, s, d, w, (int*)dsend_count,
+                       (int*)drecv_count);
+    MEP_LAUNCH_CHECK();
+    hipLaunchKernelGGL(dedup_maps, dim3(d.nchunks), dim3(kDedupThreads), 0, s, d, w, rd,
+                       (const int*)route_slot, (int*)dpack_pos, (int*)drecv_pos);
+    MEP_LAUNCH_CHECK();
+    return MEP_OK;
+}

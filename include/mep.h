@@ -208,12 +208,17 @@ int mep_remap_prune(int BS, int K, int E, int F, int world_size,
  * Pack (runs when x != NULL):
  *   send_buf[send_pos[t*K+k], :] = x[t, :] for every send_pos >= 0.
  *   x [T,H] bf16; send_pos [T*K] int32 (a row index < T*K, or negative to
- *   skip the route); send_buf [T*K, H] bf16 (rows not named by send_pos
- *   are left untouched).
+ *   skip the route); send_buf [n_send, H] bf16 holding every row send_pos
+ *   names (n_send = T*K for the plan's map, the dedup send count for
+ *   mep_plan_dedup's dpack_pos); rows not named are left untouched.
  * Group (runs when recv_raw != NULL):
  *   recv_grouped[t, :] = recv_raw[recv_pos[t], :] for t in [0, n_recv).
- *   recv_raw [n_recv,H] bf16 in arrival (source-major) order; recv_pos
- *   [n_recv] int32 in [0, n_recv); recv_grouped [n_recv,H] bf16.
+ *   recv_raw [n_raw,H] bf16 in arrival (source-major) order; recv_pos
+ *   [n_recv] int32; recv_grouped [n_recv,H] bf16. With the plan's own
+ *   recv_pos, n_raw = n_recv; with mep_plan_dedup's drecv_pos the arrival
+ *   buffer is shorter (n_raw = the dedup arrival count) and rows fan out.
+ *   Entries outside [0, n_recv) skip the row; entries in range must be
+ *   below n_raw (the caller's maps guarantee it).
  * At least one of the two must run, unless T == 0 and n_recv == 0 (then
  * the call does nothing and may pass NULL buffers). Sizes: T >= 0, n_recv >= 0,
  * 1 <= K <= 64, 8 <= H <= 65536 with H % 8 == 0, T*K < 2^31 and
@@ -355,6 +360,42 @@ int mep_combine_add_rmsnorm(int T, int K, int H, const uint16_t* y_ret, int n_y,
  */
 int mep_plan_weight_rows(int R, int E, int B, const int32_t* inst_count,
                          const int32_t* inst_expert, int32_t* inst_wrow, void* stream);
+
+/*
+ * mep_plan_dedup_workspace_size - device workspace bytes mep_plan_dedup
+ * needs for (R, S, K); 0 if unsupported. Host only.
+ */
+size_t mep_plan_dedup_workspace_size(int R, int S, int K);
+
+/*
+ * mep_plan_dedup - per-destination token dedup of rank my_rank's dispatch
+ * ("MoonEP API完全参考", §5.2 communication performance, which names a dedup
+ * encoding of sent tokens; the reading: a token with several routes to one
+ * rank is sent there once and fanned out to its grouped slots on arrival).
+ * From mep_plan's global route maps, with D(g) the destinations of global
+ * token g = src*S + t:
+ *   dpack_pos [S*K]: for the first route (t,k) of t to a destination d, the
+ *     row of (t, d) in the send buffer, ordered by (d, t); -1 for t's later
+ *     routes to d. mep_dispatch's pack with dpack_pos writes each (t, d) row
+ *     once.
+ *   dsend_count [R]: rows for each destination.
+ *   drecv_pos [S*K]: for each grouped slot on my_rank, the arrival row of
+ *     the token whose route occupies it; the arrival buffer holds the rows
+ *     reaching my_rank, sources ascending, each in token order.
+ *     mep_dispatch's grouping with drecv_pos fills recv_grouped exactly as
+ *     the plan's own recv_pos does on the full arrival buffer.
+ *   drecv_count [R]: rows arriving from each source.
+ *   route_dest, route_slot [R*S*K]: mep_plan outputs (a valid plan: every
+ *     slot of my_rank is occupied by exactly one route).
+ *   workspace: mep_plan_dedup_workspace_size bytes, 256-byte aligned.
+ * Sizes: 1 <= R <= 64, S, K >= 1, R*S*K <= 2^30.
+ * Errors: MEP_ERR_NULLPTR, MEP_ERR_PARAM (my_rank outside [0,R), workspace
+ * too small), MEP_ERR_SHAPE, MEP_ERR_HIP.
+ */
+int mep_plan_dedup(int R, int S, int K, int my_rank, const int32_t* route_dest,
+                   const int32_t* route_slot, void* workspace, size_t workspace_bytes,
+                   int32_t* dpack_pos, int32_t* dsend_count, int32_t* drecv_pos,
+                   int32_t* drecv_count, void* stream);
 
 /* -------------------------------------------------------- int8 dispatch */
 

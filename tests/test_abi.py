@@ -36,7 +36,8 @@ def test_header_declares_the_four_entry_points():
               "mep_plan_workspace_size", "mep_status_str", "mep_version",
               "mep_dispatch_to_peers", "mep_combine_from_peers", "mep_ungroup",
               "mep_combine_add_rmsnorm", "mep_quant_msg_bytes", "mep_dispatch_quant",
-              "mep_group_quant", "mep_plan_weight_rows"):
+              "mep_group_quant", "mep_plan_weight_rows", "mep_plan_dedup_workspace_size",
+              "mep_plan_dedup"):
         assert n in names
 
 
@@ -231,3 +232,16 @@ def test_plan_weight_rows_validation(B):
     assert f(4, 2000, 2, 16, 16, 16, None) == B.MEP_ERR_SHAPE
     assert f(4, 8, -1, 16, 16, 16, None) == B.MEP_ERR_PARAM
     assert f(4, 8, 2, None, 16, 16, None) == B.MEP_ERR_NULLPTR
+
+
+def test_plan_dedup_validation(B):
+    assert B.mep_plan_dedup_workspace_size(65, 10, 2) == 0
+    n = B.mep_plan_dedup_workspace_size(8, 4096, 8)
+    assert n > 0 and n % 256 == 0
+    f = B.mep_plan_dedup
+    assert f(8, 16, 2, 8, 16, 16, 256, n, 16, 16, 16, 16, None) == B.MEP_ERR_PARAM   # my_rank
+    assert f(65, 16, 2, 0, 16, 16, 256, n, 16, 16, 16, 16, None) == B.MEP_ERR_SHAPE
+    assert f(8, 16, 2, 0, None, 16, 256, n, 16, 16, 16, 16, None) == B.MEP_ERR_NULLPTR
+    assert f(8, 16, 2, 0, 16, 16, 256, 8, 16, 16, 16, 16, None) == B.MEP_ERR_PARAM   # small ws
+    m = B.mep_plan_dedup_workspace_size(8, 16, 2)
+    assert f(8, 16, 2, 0, 16, 16, 16, m, 16, 16, 16, 16, None) == B.MEP_ERR_SHAPE    # ws align
