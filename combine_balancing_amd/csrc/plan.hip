@@ -49,9 +49,8 @@ namespace {
 #define MEP_PLAN_CHUNK 1024
 #endif
 constexpr int kHistThreads = 256;
-constexpr int kScanThreads = 1024;
+constexpr int kScanThreads = 256;                // plan_scan: 4 experts per work-group
 constexpr int kMaxChunks = MEP_PLAN_MAX_CHUNKS;  // column length of the expert scan
-constexpr int kScanItems = (kMaxChunks + kScanThreads - 1) / kScanThreads;
 constexpr int kBuckets = 1024;
 constexpr size_t kMaxLds = 160 * 1024;  // LDS a gfx950 work-group may allocate  // piece lookup: excess index >> shift -> first piece
 constexpr int kGlobalThreads = 1024;
@@ -132,11 +131,18 @@ __global__ __launch_bounds__(kHistThreads) void plan_hist(PlanDims d, const int*
 }
 
 // ---------------------------------------------------------------- plan_scan
+// One wave per expert: the expert's column of chunk counts (nchunks <=
+// kMaxChunks = 16 per lane) is loaded at once and scanned with a DPP wave
+// scan, so no work-group barrier is needed.
+constexpr int kScanWaves = kScanThreads / kWave;
+constexpr int kScanItems = kMaxChunks / kWave;  // 16
+
 __global__ __launch_bounds__(kScanThreads) void plan_scan(PlanDims d, int* __restrict__ chunk,
                                                           int* __restrict__ cnt) {
-    __shared__ int scratch[kScanThreads / kWave + 1];
-    const int e = blockIdx.x;
-    const int c0 = threadIdx.x * kScanItems;
+    const int e = blockIdx.x * kScanWaves + (int)(threadIdx.x / kWave);
+    if (e >= d.E) return;  // whole waves leave together
+    const int lane = lane_id();
+    const int c0 = lane * kScanItems;
     int v[kScanItems];
     int sum = 0;
 #pragma unroll
@@ -145,15 +151,15 @@ __global__ __launch_bounds__(kScanThreads) void plan_scan(PlanDims d, int* __res
         v[i] = c < d.nchunks ? chunk[c * d.E + e] : 0;
         sum += v[i];
     }
-    int total;
-    int ex = block_exclusive_sum(sum, scratch, &total);
+    const int incl = wave_inclusive_sum(sum);
+    int ex = incl - sum;
 #pragma unroll
     for (int i = 0; i < kScanItems; ++i) {
         const int c = c0 + i;
         if (c < d.nchunks) chunk[c * d.E + e] = ex;
         ex += v[i];
     }
-    if (threadIdx.x == 0) cnt[e] = total;
+    if (lane == kWave - 1) cnt[e] = incl;
 }
 
 // -------------------------------------------------------------- plan_global
@@ -780,7 +786,8 @@ extern "C" int mep_plan(int R, int E, int S, int K, int my_rank, const int32_t* 
     hipLaunchKernelGGL(plan_hist, dim3(d.nchunks), dim3(kHistThreads), d.E * sizeof(int), s, d,
                        (const int*)topk_ids, w.chunk);
     MEP_LAUNCH_CHECK();
-    hipLaunchKernelGGL(plan_scan, dim3(d.E), dim3(kScanThreads), 0, s, d, w.chunk, w.cnt);
+    hipLaunchKernelGGL(plan_scan, dim3((d.E + kScanWaves - 1) / kScanWaves), dim3(kScanThreads), 0,
+                       s, d, w.chunk, w.cnt);
     MEP_LAUNCH_CHECK();
     hipLaunchKernelGGL(plan_global, dim3(1), dim3(kGlobalThreads), glds, s, d, w, o);
     MEP_LAUNCH_CHECK();
