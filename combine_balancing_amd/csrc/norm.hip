@@ -49,7 +49,7 @@ __device__ __forceinline__ u32x4 pack_bf16(const float* a) {
     u32x4 o;
 #pragma unroll
     for (int j = 0; j < 4; ++j)
-        o[j] = float_to_bf16_bits(a[2 * j]) | (float_to_bf16_bits(a[2 * j + 1]) << 16);
+        o[j] = bf16x2_bits(a[2 * j], a[2 * j + 1]);
     return o;
 }
 

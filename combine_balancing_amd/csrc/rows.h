@@ -29,7 +29,7 @@ __device__ __forceinline__ void store_out(const float* acc, u32x4* __restrict__ 
         u32x4 o;
 #pragma unroll
         for (int j = 0; j < 4; ++j)
-            o[j] = float_to_bf16_bits(acc[2 * j]) | (float_to_bf16_bits(acc[2 * j + 1]) << 16);
+            o[j] = bf16x2_bits(acc[2 * j], acc[2 * j + 1]);
         __builtin_nontemporal_store(o, out_bf16 + at);
     }
     if (out_f32) {
