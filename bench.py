@@ -328,6 +328,56 @@ def dedup_dispatch(torch, cba, d, pout, steps, flush=None):
             "algorithmic_bytes": nb}
 
 
+def large_skew(torch, cba, synth, steps, flush=None):
+    """The large plan with extreme skew (R=64, E=256, S=8192, K=8, H=7168):
+    the global plan over all 4,194,304 routes, then rank 0's pack, grouping
+    and combine (seeded stand-ins for the received rows and the returned
+    expert outputs)."""
+    d = synth.make_plan_inputs("large_skew")
+    R, E, S, K, H, C = d["R"], d["E"], d["S"], d["K"], d["H"], d["C"]
+    ids = _dev(torch, d["topk_ids"].reshape(-1))
+    x, recv_raw, y_ret = _dev(torch, d["x"]), _dev(torch, d["recv_raw"]), _dev(torch, d["y_ret"])
+    scores = _dev(torch, d["scores"][0])
+    ws = cba.plan_workspace(R, E, S, K)
+    pout = cba.plan_outputs(R, E, S, K)
+    send_buf = torch.empty(C, H, dtype=torch.int16, device="cuda")
+    grouped = torch.empty(C, H, dtype=torch.int16, device="cuda")
+    out = torch.empty(S, H, dtype=torch.bfloat16, device="cuda")
+    stream = torch.cuda.current_stream()
+    names = ["plan", "pack", "group", "combine"]
+    t = {n: [] for n in names}
+    for it in range(steps + 3):
+        if flush is not None:
+            flush.fill_(it & 0xFF)
+        ev = [torch.cuda.Event(enable_timing=True) for _ in range(5)]
+        ev[0].record(stream)
+        cba.plan(ids, R, E, S, K, my_rank=0, workspace=ws, out=pout)
+        ev[1].record(stream)
+        cba.dispatch(K, x=x, send_pos=pout["send_pos"], send_buf=send_buf)
+        ev[2].record(stream)
+        cba.dispatch(K, recv_raw=recv_raw, recv_pos=pout["recv_pos"], recv_grouped=grouped)
+        ev[3].record(stream)
+        cba.combine(y_ret, pout["send_pos"], scores, out_bf16=out)
+        ev[4].record(stream)
+        torch.cuda.synchronize()
+        if it >= 3:
+            for j, n in enumerate(names):
+                t[n].append(ev[j].elapsed_time(ev[j + 1]) * 1e3)
+    us = {n: float(np.mean(v)) for n, v in t.items()}
+    b = algorithmic_bytes(S, K, H)
+    dc = us["pack"] + us["group"] + us["combine"]
+    loads = pout["rank_load"].cpu().numpy()
+    n_inst = int(pout["inst_gid_base"][-1].item())
+    return {"workload": f"R={R} E={E} S={S} K={K} H={H} bf16, rank 0",
+            "plan_us": round(us["plan"], 2),
+            "routes_per_s_plan": round(R * C / (us["plan"] * 1e-6), 1),
+            "kernel_us_mean": {n: round(v, 2) for n, v in us.items()},
+            "dispatch_combine_us": round(dc, 2),
+            "dispatch_combine_GBs": round((b["pack"] + b["group"] + b["combine"]) / (dc * 1e-6) / 1e9, 1),
+            "maxvio_native": round(float(loads.max()) / C - 1.0, 3),
+            "redundant_instances": n_inst - E}
+
+
 def main():
     ap = argparse.ArgumentParser()
     ap.add_argument("--gpus", type=int, default=1)
@@ -338,6 +388,8 @@ def main():
                     help="skip the imbalance sweep (R=8 E=384 S=8192 K=8 H=7168)")
     ap.add_argument("--no-flush", action="store_true",
                     help="do not write a 1 GiB buffer before each step (caches stay warm)")
+    ap.add_argument("--no-large-skew", action="store_true",
+                    help="skip the R=64 S=8192 large-plan leg")
     ap.add_argument("--no-zero-copy", action="store_true",
                     help="skip the zero-copy push/pull timing")
     ap.add_argument("--copy-calibration", action="store_true",
@@ -486,6 +538,9 @@ def main():
     if not args.no_zero_copy:
         res["zero_copy"] = zero_copy(torch, cba, d, pout, steps=max(5, min(args.steps, 20)),
                                      flush=flush)
+    if not args.no_large_skew:
+        res["large_skew"] = large_skew(torch, cba, synth, steps=max(5, min(args.steps, 20)),
+                                       flush=flush)
     if not args.no_skew_sweep:
         res["skew_sweep"] = skew_sweep(torch, cba, synth, steps=max(5, min(args.steps, 20)),
                                        flush=flush)
