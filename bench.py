@@ -28,6 +28,9 @@ sys.path.insert(0, ROOT)
 import numpy as np  # noqa: E402
 
 HBM_PEAK_GBS = 8000.0
+# extra measurements after the headline step, in the order they run
+LEGS = ("combine_add_rmsnorm", "int8_dispatch", "dedup_dispatch", "zero_copy", "large_skew",
+        "skew_sweep")
 WORKLOAD = "dsv3"
 TRAFFIC_FILE = os.path.join(ROOT, "profiles", "traffic_dsv3.json")
 # sources the row-moving kernels are compiled from: the stored counter
@@ -384,14 +387,14 @@ def main():
     ap.add_argument("--steps", type=int, default=100)
     ap.add_argument("--warmup", type=int, default=10)
     ap.add_argument("--no-cpu-baseline", action="store_true")
-    ap.add_argument("--no-skew-sweep", action="store_true",
-                    help="skip the imbalance sweep (R=8 E=384 S=8192 K=8 H=7168)")
     ap.add_argument("--no-flush", action="store_true",
                     help="do not write a 1 GiB buffer before each step (caches stay warm)")
-    ap.add_argument("--no-large-skew", action="store_true",
-                    help="skip the R=64 S=8192 large-plan leg")
-    ap.add_argument("--no-zero-copy", action="store_true",
-                    help="skip the zero-copy push/pull timing")
+    ap.add_argument("--legs", default=",".join(LEGS),
+                    help="comma-separated extra legs after the headline step, from: "
+                         + ", ".join(LEGS) + " ('none' for the headline step alone)")
+    ap.add_argument("--no-skew-sweep", action="store_true", help="drop the skew_sweep leg")
+    ap.add_argument("--no-large-skew", action="store_true", help="drop the large_skew leg")
+    ap.add_argument("--no-zero-copy", action="store_true", help="drop the zero_copy leg")
     ap.add_argument("--copy-calibration", action="store_true",
                     help="after the timed steps, run plain device-to-device copies of "
                          "the group kernel's output size (a known-size reference for "
@@ -529,21 +532,28 @@ def main():
                      "frac": round(group_gbs / HBM_PEAK_GBS, 4),
                      "traffic": _traffic("group_rows")},
     }
-    res["combine_add_rmsnorm"] = fused_norm(torch, cba, d, pout, y_ret, scores,
-                                            steps=max(5, min(args.steps, 20)), flush=flush)
-    res["int8_dispatch"] = int8_dispatch(torch, cba, d, pout, steps=max(5, min(args.steps, 20)),
-                                         flush=flush)
-    res["dedup_dispatch"] = dedup_dispatch(torch, cba, d, pout,
-                                           steps=max(5, min(args.steps, 20)), flush=flush)
-    if not args.no_zero_copy:
-        res["zero_copy"] = zero_copy(torch, cba, d, pout, steps=max(5, min(args.steps, 20)),
-                                     flush=flush)
-    if not args.no_large_skew:
-        res["large_skew"] = large_skew(torch, cba, synth, steps=max(5, min(args.steps, 20)),
-                                       flush=flush)
-    if not args.no_skew_sweep:
-        res["skew_sweep"] = skew_sweep(torch, cba, synth, steps=max(5, min(args.steps, 20)),
-                                       flush=flush)
+    legs = set() if args.legs == "none" else set(args.legs.split(","))
+    unknown = legs - set(LEGS)
+    if unknown:
+        raise SystemExit(f"unknown legs: {sorted(unknown)}")
+    for flag, leg in ((args.no_skew_sweep, "skew_sweep"), (args.no_large_skew, "large_skew"),
+                      (args.no_zero_copy, "zero_copy")):
+        if flag:
+            legs.discard(leg)
+    leg_steps = max(5, min(args.steps, 20))
+    if "combine_add_rmsnorm" in legs:
+        res["combine_add_rmsnorm"] = fused_norm(torch, cba, d, pout, y_ret, scores,
+                                                steps=leg_steps, flush=flush)
+    if "int8_dispatch" in legs:
+        res["int8_dispatch"] = int8_dispatch(torch, cba, d, pout, steps=leg_steps, flush=flush)
+    if "dedup_dispatch" in legs:
+        res["dedup_dispatch"] = dedup_dispatch(torch, cba, d, pout, steps=leg_steps, flush=flush)
+    if "zero_copy" in legs:
+        res["zero_copy"] = zero_copy(torch, cba, d, pout, steps=leg_steps, flush=flush)
+    if "large_skew" in legs:
+        res["large_skew"] = large_skew(torch, cba, synth, steps=leg_steps, flush=flush)
+    if "skew_sweep" in legs:
+        res["skew_sweep"] = skew_sweep(torch, cba, synth, steps=leg_steps, flush=flush)
     if args.copy_calibration:
         nbytes = C * H * 2
         for _ in range(3):
