@@ -29,8 +29,8 @@ import numpy as np  # noqa: E402
 
 HBM_PEAK_GBS = 8000.0
 # extra measurements after the headline step, in the order they run
-LEGS = ("combine_add_rmsnorm", "int8_dispatch", "dedup_dispatch", "zero_copy", "large_skew",
-        "skew_sweep")
+LEGS = ("graph_step", "combine_add_rmsnorm", "int8_dispatch", "dedup_dispatch", "zero_copy",
+        "large_skew", "skew_sweep")
 WORKLOAD = "dsv3"
 TRAFFIC_FILE = os.path.join(ROOT, "profiles", "traffic_dsv3.json")
 # sources the row-moving kernels are compiled from: the stored counter
@@ -381,6 +381,35 @@ def large_skew(torch, cba, synth, steps, flush=None):
             "redundant_instances": n_inst - E}
 
 
+def graph_step(torch, step, steps, flush=None):
+    """The headline step captured once in a HIP graph and replayed (the
+    library only enqueues: no host sync, allocation or memset inside)."""
+    s = torch.cuda.Stream()
+    s.wait_stream(torch.cuda.current_stream())
+    with torch.cuda.stream(s):
+        step()
+    torch.cuda.current_stream().wait_stream(s)
+    torch.cuda.synchronize()
+    g = torch.cuda.CUDAGraph()
+    with torch.cuda.graph(g):
+        step()
+    torch.cuda.synchronize()
+    stream = torch.cuda.current_stream()
+    t = []
+    for it in range(steps + 3):
+        if flush is not None:
+            flush.fill_(it & 0xFF)
+        ev = [torch.cuda.Event(enable_timing=True) for _ in range(2)]
+        ev[0].record(stream)
+        g.replay()
+        ev[1].record(stream)
+        torch.cuda.synchronize()
+        if it >= 3:
+            t.append(ev[0].elapsed_time(ev[1]) * 1e3)
+    return {"step_us": round(float(np.mean(t)), 2), "step_us_median": round(float(np.median(t)), 2),
+            "what": "plan + remap/prune + pack + group + combine, one graph replay"}
+
+
 def main():
     ap = argparse.ArgumentParser()
     ap.add_argument("--gpus", type=int, default=1)
@@ -541,6 +570,8 @@ def main():
         if flag:
             legs.discard(leg)
     leg_steps = max(5, min(args.steps, 20))
+    if "graph_step" in legs:
+        res["graph_step"] = graph_step(torch, step, steps=leg_steps, flush=flush)
     if "combine_add_rmsnorm" in legs:
         res["combine_add_rmsnorm"] = fused_norm(torch, cba, d, pout, y_ret, scores,
                                                 steps=leg_steps, flush=flush)
