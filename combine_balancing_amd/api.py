@@ -213,7 +213,9 @@ def combine(y_ret, send_pos, scores, out_bf16=True, out_f32=False, stream=None):
 
 def peer_table(bufs):
     """Device array of row-buffer addresses (one per rank) for the zero-copy
-    calls. `bufs`: a list of R device tensors, or one [R, C, H] tensor."""
+    calls. `bufs`: a list of R device tensors, or one [R, C, H] tensor.
+    The table holds raw addresses: the caller keeps the buffers alive for as
+    long as the table is used."""
     if isinstance(bufs, torch.Tensor):
         bufs = list(bufs.unbind(0))
     for b in bufs:

@@ -157,3 +157,42 @@ def test_zero_copy_headline_shape(orc):
     rf64 = rf.astype(np.float64)
     mag = np.abs(rf64).max()
     assert np.all(np.abs(host(of)[tok].astype(np.float64) - rf64) <= 1e-6 * mag)
+
+
+@pytest.mark.parametrize("T,K,H,R,C", [(3, 2, 65536, 2, 4), (5, 3, 72, 3, 6), (1, 1, 8, 1, 1)])
+def test_zero_copy_and_ungroup_edges(orc, T, K, H, R, C):
+    # the largest row, ragged vector tails, one rank and one slot; routes
+    # outside [0,R) x [0,C) are skipped
+    torch = require_gpu()
+    import combine_balancing_amd as cba
+    rng = np.random.default_rng(T * 7 + H)
+    x = synth.bf16_normal(rng, (T, H))
+    rd = rng.integers(0, R, T * K).astype(np.int32)
+    rs = rng.integers(0, C, T * K).astype(np.int32)
+    rd[::4] = R  # no such rank
+    # one route per (dest, slot): keep the first writer of each slot
+    seen = set()
+    for f in range(T * K):
+        if (rd[f], rs[f]) in seen:
+            rd[f] = -1
+        seen.add((rd[f], rs[f]))
+    note(f"zero-copy edges T={T} K={K} H={H} R={R} C={C}")
+    grouped = torch.zeros(R, C, H, dtype=torch.bfloat16, device="cuda")
+    cba.dispatch_to_peers(K, dev(x), dev(rd), dev(rs), cba.peer_table(grouped), C)
+    torch.cuda.synchronize()
+    want = orc.push(x, rd, rs, K, R, C)
+    assert np.array_equal(host(grouped), want)
+    y = synth.bf16_normal(rng, (R, C, H))
+    sc = rng.standard_normal((T, K)).astype(np.float32)
+    yd = dev(y).view(torch.bfloat16)  # the peer table holds raw addresses: keep yd alive
+    ob, of = cba.combine_from_peers(cba.peer_table(yd), C, H, dev(rd), dev(rs), dev(sc),
+                                    out_bf16=True, out_f32=True)
+    torch.cuda.synchronize()
+    rb, rf = orc.pull_combine(y, rd, rs, sc)
+    assert np.array_equal(host(ob), rb) and np.array_equal(host(of), rf)
+    n = min(T * K, 16)
+    rows = synth.bf16_normal(rng, (n, H))
+    rp = rng.permutation(n).astype(np.int32)
+    ya = cba.ungroup(dev(rows), dev(rp))
+    torch.cuda.synchronize()
+    assert np.array_equal(host(ya), orc.ungroup(rows, rp))

@@ -150,7 +150,8 @@ def test_eplb_pack_after_remap(orc):
 
 
 @pytest.mark.parametrize("T,K,H", [(1, 1, 8), (5, 3, 8), (37, 4, 136), (64, 8, 1032),
-                                   (130, 2, 4096), (33, 6, 16384), (9, 20, 512), (3, 64, 64)])
+                                   (130, 2, 4096), (33, 6, 16384), (9, 20, 512), (3, 64, 64),
+                                   (3, 2, 65536), (2, 7, 65528)])
 def test_row_kernels_odd_shapes(orc, T, K, H):
     # ragged vector tails (H/8 not a multiple of 64), K beyond the unrolled
     # combine instances, negative and out-of-range entries skipped
