@@ -561,6 +561,30 @@ def main():
                      "frac": round(group_gbs / HBM_PEAK_GBS, 4),
                      "traffic": _traffic("group_rows")},
     }
+    # copy references at the grouping's size, same cold caches: the grouping
+    # kernel with the identity map (a purely sequential copy) and torch's
+    # device-to-device copy
+    ident = torch.arange(C, dtype=torch.int32, device="cuda")
+    refs = {}
+    for name, fn in (("identity_grouping", lambda: cba.dispatch(K, recv_raw=recv_raw, recv_pos=ident,
+                                                                 recv_grouped=grouped)),
+                     ("torch_copy", lambda: grouped.copy_(recv_raw))):
+        ct = []
+        for it in range(max(5, min(args.steps, 20)) + 3):
+            if flush is not None:
+                flush.fill_(it & 0xFF)
+            ev = [torch.cuda.Event(enable_timing=True) for _ in range(2)]
+            ev[0].record(stream)
+            fn()
+            ev[1].record(stream)
+            torch.cuda.synchronize()
+            if it >= 3:
+                ct.append(ev[0].elapsed_time(ev[1]) * 1e3)
+        cus = float(np.mean(ct))
+        refs[name] = {"us": round(cus, 2), "GBs": round(2 * C * H * 2 / (cus * 1e-6) / 1e9, 1)}
+    res["copy_reference"] = dict(bytes=2 * C * H * 2, **refs,
+                                 group_rows_vs_identity=round(
+                                     group_gbs / refs["identity_grouping"]["GBs"], 4))
     legs = set() if args.legs == "none" else set(args.legs.split(","))
     unknown = legs - set(LEGS)
     if unknown:
