@@ -26,7 +26,7 @@ from __future__ import annotations
 
 import numpy as np
 
-CONFIGS = {
+WORKLOADS = {
     "tiny": dict(R=4, E=16, S=64, K=2, H=128, seed=1),
     "small": dict(R=8, E=64, S=1024, K=4, H=2048, seed=2),
     "dsv3": dict(R=8, E=256, S=4096, K=8, H=7168, seed=3),
@@ -35,7 +35,7 @@ CONFIGS = {
                  H=7168, n_active=448, seed=5),
 }
 
-PLAN_CONFIGS = ("tiny", "small", "dsv3", "large_skew")
+PLAN_WORKLOADS = ("tiny", "small", "dsv3", "large_skew")
 
 _ROW_CHUNK = 65536  # router rows drawn per call, bounds peak host memory
 
@@ -121,7 +121,7 @@ def make_routing(name: str, seed: int | None = None):
     Returns dict with topk_ids int32 [R,S,K] and scores fp32 [R,S,K], plus the
     rng positioned after the routing draws (for hidden rows).
     """
-    c = CONFIGS[name]
+    c = WORKLOADS[name]
     rng = np.random.default_rng(c["seed"] if seed is None else seed)
     R, E, S, K = c["R"], c["E"], c["S"], c["K"]
     bias = _bias(name, rng, E)
@@ -161,7 +161,7 @@ def make_plan_inputs(name: str, seed: int | None = None, *, rank: int = 0,
 
 def make_eplb_inputs(seed: int | None = None, *, with_x: bool = True):
     """EPLB remap + prune workload (and the rows it then dispatches)."""
-    c = CONFIGS["eplb"]
+    c = WORKLOADS["eplb"]
     rng = np.random.default_rng(c["seed"] if seed is None else seed)
     E, F, BS, K, H = c["E"], c["F"], c["BS"], c["K"], c["H"]
     ws, ppr = c["world_size"], c["place_per_rank"]
