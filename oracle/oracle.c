@@ -25,6 +25,20 @@
  * that meets the [MoonEP-TD] invariant; the readings are listed with the
  * design notes of this repository.
  *
+ * [DispSetup] "aclnnMoeDistributeDispatchSetup" op doc: quantized token
+ *             messages and their size; the call example's outputs.
+ *
+ * Pins. Every function is checked by the test suite against something other
+ * than itself (the op doc's worked example, closed forms, invariants, brute
+ * force, equivalence with already pinned functions). Parity unpinned, where
+ * the pages print no formula or example and the pins fix the reading taken
+ * rather than the pages: remap with instance counts above one beyond the
+ * hand-derived examples; prune decisions within rounding distance of the
+ * threshold sum; the combine + add + RMSNorm formula
+ * (oracle_combine_add_rmsnorm); the int8 quantization formula
+ * (oracle_dispatch_quant); the prefetch-slot order (oracle_weight_rows);
+ * the dedup orders (oracle_plan_dedup).
+ *
  * Build: gcc -O2 -ffp-contract=off -fPIC -shared (no FMA contraction, so
  * every fp32 multiply and add is rounded on its own).
  */
