@@ -29,8 +29,8 @@ import numpy as np  # noqa: E402
 
 HBM_PEAK_GBS = 8000.0
 # extra measurements after the headline step, in the order they run
-LEGS = ("graph_step", "combine_add_rmsnorm", "int8_dispatch", "dedup_dispatch", "zero_copy",
-        "large_skew", "skew_sweep")
+LEGS = ("copy_reference", "graph_step", "combine_add_rmsnorm", "int8_dispatch",
+        "dedup_dispatch", "zero_copy", "large_skew", "skew_sweep")
 WORKLOAD = "dsv3"
 TRAFFIC_FILE = os.path.join(ROOT, "profiles", "traffic_dsv3.json")
 # sources the row-moving kernels are compiled from: the stored counter
@@ -410,6 +410,34 @@ def graph_step(torch, step, steps, flush=None):
             "what": "plan + remap/prune + pack + group + combine, one graph replay"}
 
 
+def copy_reference(torch, cba, K, recv_raw, grouped, group_gbs, steps, flush=None):
+    """Copy references at the grouping's size, same cold caches: the grouping
+    kernel with the identity map (a purely sequential copy) and torch's
+    device-to-device copy."""
+    C, H = recv_raw.shape
+    stream = torch.cuda.current_stream()
+    ident = torch.arange(C, dtype=torch.int32, device="cuda")
+    refs = {}
+    for name, fn in (("identity_grouping", lambda: cba.dispatch(K, recv_raw=recv_raw, recv_pos=ident,
+                                                                 recv_grouped=grouped)),
+                     ("torch_copy", lambda: grouped.copy_(recv_raw))):
+        ct = []
+        for it in range(steps + 3):
+            if flush is not None:
+                flush.fill_(it & 0xFF)
+            ev = [torch.cuda.Event(enable_timing=True) for _ in range(2)]
+            ev[0].record(stream)
+            fn()
+            ev[1].record(stream)
+            torch.cuda.synchronize()
+            if it >= 3:
+                ct.append(ev[0].elapsed_time(ev[1]) * 1e3)
+        cus = float(np.mean(ct))
+        refs[name] = {"us": round(cus, 2), "GBs": round(2 * C * H * 2 / (cus * 1e-6) / 1e9, 1)}
+    return dict(bytes=2 * C * H * 2, **refs,
+                group_rows_vs_identity=round(group_gbs / refs["identity_grouping"]["GBs"], 4))
+
+
 def main():
     ap = argparse.ArgumentParser()
     ap.add_argument("--gpus", type=int, default=1)
@@ -561,30 +589,6 @@ def main():
                      "frac": round(group_gbs / HBM_PEAK_GBS, 4),
                      "traffic": _traffic("group_rows")},
     }
-    # copy references at the grouping's size, same cold caches: the grouping
-    # kernel with the identity map (a purely sequential copy) and torch's
-    # device-to-device copy
-    ident = torch.arange(C, dtype=torch.int32, device="cuda")
-    refs = {}
-    for name, fn in (("identity_grouping", lambda: cba.dispatch(K, recv_raw=recv_raw, recv_pos=ident,
-                                                                 recv_grouped=grouped)),
-                     ("torch_copy", lambda: grouped.copy_(recv_raw))):
-        ct = []
-        for it in range(max(5, min(args.steps, 20)) + 3):
-            if flush is not None:
-                flush.fill_(it & 0xFF)
-            ev = [torch.cuda.Event(enable_timing=True) for _ in range(2)]
-            ev[0].record(stream)
-            fn()
-            ev[1].record(stream)
-            torch.cuda.synchronize()
-            if it >= 3:
-                ct.append(ev[0].elapsed_time(ev[1]) * 1e3)
-        cus = float(np.mean(ct))
-        refs[name] = {"us": round(cus, 2), "GBs": round(2 * C * H * 2 / (cus * 1e-6) / 1e9, 1)}
-    res["copy_reference"] = dict(bytes=2 * C * H * 2, **refs,
-                                 group_rows_vs_identity=round(
-                                     group_gbs / refs["identity_grouping"]["GBs"], 4))
     legs = set() if args.legs == "none" else set(args.legs.split(","))
     unknown = legs - set(LEGS)
     if unknown:
@@ -594,6 +598,9 @@ def main():
         if flag:
             legs.discard(leg)
     leg_steps = max(5, min(args.steps, 20))
+    if "copy_reference" in legs:
+        res["copy_reference"] = copy_reference(torch, cba, K, recv_raw, grouped, group_gbs,
+                                               steps=leg_steps, flush=flush)
     if "graph_step" in legs:
         res["graph_step"] = graph_step(torch, step, steps=leg_steps, flush=flush)
     if "combine_add_rmsnorm" in legs:
