@@ -245,3 +245,12 @@ def test_plan_dedup_validation(B):
     assert f(8, 16, 2, 0, 16, 16, 256, 8, 16, 16, 16, 16, None) == B.MEP_ERR_PARAM   # small ws
     m = B.mep_plan_dedup_workspace_size(8, 16, 2)
     assert f(8, 16, 2, 0, 16, 16, 16, m, 16, 16, 16, 16, None) == B.MEP_ERR_SHAPE    # ws align
+
+
+def test_c_consumer_builds(B):
+    # the plain C consumer of the ABI compiles and links against the library
+    # and the oracle with gcc (it runs in the GPU suite)
+    import __graft_entry__ as g
+    import oracle
+    oracle.build()
+    assert os.path.exists(g.build_c_abi_check())
