@@ -17,9 +17,9 @@
 // work-group -> XCD assignment does not matter here.
 //
 // Launch shapes (measured on MI355X at H=7168): pack and combine are flat,
-// one thread per (token, vector) in 256-thread work-groups, which keeps the
-// most stores (pack) and row loads (combine) in flight; the grouping copy
-// runs one work-group per row, which reaches the read+write copy ceiling.
+// one thread per (token, vector) in 256-thread work-groups; the grouping
+// copy runs one work-group per row, which reaches the read+write copy
+// ceiling.
 #include <algorithm>
 
 #include "rows.h"
@@ -32,7 +32,14 @@ using namespace rows;
 // ------------------------------------------------------------------- pack
 // send_buf[send_pos[t*K+k]] = x[t] for each k with 0 <= send_pos < nrows.
 // One thread per (token, vector): the token's row is read once and stored to
-// each of its K send rows.
+// each of its K send rows, one store in flight at a time (each waits for the
+// previous one). The K send rows of a token lie in up to K far-apart
+// segments, so the grid writes many streams at once, and fewer outstanding
+// stores measured faster on MI355X (dsv3 shape: 8 back-to-back stores
+// 113 us, one at a time 104 us). Capping residency at two work-groups per
+// CU gained 4 us more at full K but lost 10 us when a third of the
+// positions are skipped (dedup maps) and 40 us in the peer-write variant,
+// so the launch keeps full residency.
 template <int KT>
 __global__ __launch_bounds__(kFlatThreads) void pack_flat(const u32x4* __restrict__ x,
                                                           const int* __restrict__ send_pos,
@@ -43,14 +50,26 @@ __global__ __launch_bounds__(kFlatThreads) void pack_flat(const u32x4* __restric
     if (i >= total) return;
     const uint32_t t = fast_div(i, rowdiv);
     const uint32_t v = i - t * rowdiv.d;
-    const int kk = KT > 0 ? KT : K;
-    const int* sp = send_pos + (size_t)t * kk;
-    const u32x4 w = __builtin_nontemporal_load(x + i);
+    if constexpr (KT > 0) {
+        int p[KT];  // all positions first, so each store waits only for the last
 #pragma unroll
-    for (int k = 0; k < kk; ++k) {
-        const int p = sp[k];
-        if ((unsigned)p < (unsigned)nrows)
-            __builtin_nontemporal_store(w, send_buf + (size_t)p * rowdiv.d + v);
+        for (int k = 0; k < KT; ++k) p[k] = send_pos[(size_t)t * KT + k];
+        const u32x4 w = __builtin_nontemporal_load(x + i);
+#pragma unroll
+        for (int k = 0; k < KT; ++k) {
+            if ((unsigned)p[k] < (unsigned)nrows)
+                __builtin_nontemporal_store(w, send_buf + (size_t)p[k] * rowdiv.d + v);
+            if (k + 1 < KT) __builtin_amdgcn_s_waitcnt(kWaitVmem);
+        }
+    } else {
+        const int* sp = send_pos + (size_t)t * K;
+        const u32x4 w = __builtin_nontemporal_load(x + i);
+        for (int k = 0; k < K; ++k) {
+            const int p = sp[k];
+            if ((unsigned)p < (unsigned)nrows)
+                __builtin_nontemporal_store(w, send_buf + (size_t)p * rowdiv.d + v);
+            __builtin_amdgcn_s_waitcnt(kWaitVmem);
+        }
     }
 }
 
@@ -62,7 +81,7 @@ __global__ __launch_bounds__(kMaxTpr) void group_rows(const u32x4* __restrict__ 
                                                       const int* __restrict__ recv_pos,
                                                       u32x4* __restrict__ out, int n, int nvec,
                                                       int tpr, int rpb) {
-    const int r = row_in_group(tpr);
+    const int r = row_in_group(tpr, rpb);
     const int tid = threadIdx.x - r * tpr;
     const int t = blockIdx.x * rpb + r;
     if (t >= n) return;

@@ -62,7 +62,7 @@ __global__ __launch_bounds__(kNormThreads) void combine_norm_rows(
     u32x4* __restrict__ y_out, float* __restrict__ rstd_out, int T, int K, int nvec, int tpr,
     int rpb) {
     __shared__ float s_red[kNormThreads / kWave];
-    const int r = row_in_group(tpr);
+    const int r = row_in_group(tpr, rpb);
     const int tid = threadIdx.x - r * tpr;
     const int t_raw = blockIdx.x * rpb + r;
     const bool live = t_raw < T;

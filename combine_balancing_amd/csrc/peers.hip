@@ -113,7 +113,7 @@ __global__ __launch_bounds__(kMaxTpr) void ungroup_rows(const u32x4* __restrict_
                                                         const int* __restrict__ pos,
                                                         u32x4* __restrict__ out, int n, int nvec,
                                                         int tpr, int rpb) {
-    const int r = row_in_group(tpr);
+    const int r = row_in_group(tpr, rpb);
     const int tid = threadIdx.x - r * tpr;
     const int t = blockIdx.x * rpb + r;
     if (t >= n) return;

@@ -89,7 +89,7 @@ __global__ __launch_bounds__(kQuantThreads) void quant_pack_rows(
     typedef typename Codes<W>::type CT;
     constexpr int NV = W * NU;
     __shared__ float s_red[2][kQuantThreads / kWave];
-    const int r = row_in_group(tpr);
+    const int r = row_in_group(tpr, rpb);
     const int tid = threadIdx.x - r * tpr;
     const int t_raw = blockIdx.x * rpb + r;
     const bool live = t_raw < T;

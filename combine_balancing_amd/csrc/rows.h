@@ -49,6 +49,11 @@ inline bool aligned16(const void* p) { return ((uintptr_t)p & 15u) == 0; }
 // 896-thread row groups stay near 4.7 TB/s).
 constexpr int kFlatThreads = 256;
 
+// s_waitcnt operand that waits for every outstanding vector memory operation
+// (vmcnt(0)) and leaves the export and LDS/scalar counters alone (gfx9
+// encoding: vmcnt in bits [3:0] and [15:14], expcnt [6:4], lgkmcnt [11:8]).
+constexpr unsigned kWaitVmem = 0x0F70;
+
 // q = n / d for 0 <= n < 2^31 by one 64-bit multiply and a shift, with
 // s = ceil(log2 d) and m = ceil(2^(32+s) / d) < 2^33: the rounding error of m
 // times n stays below 2^(32+s) / d, so the quotient is exact.
@@ -80,16 +85,22 @@ struct RowShape {
 // Row of this thread within its work-group. tpr is a multiple of the wave
 // size, so a wave lies inside one row and the row is wave-uniform: reading
 // it from the first lane makes the row's index, position and score loads
-// scalar (and the row base an SGPR pair).
-__device__ __forceinline__ int row_in_group(int tpr) {
-    return __builtin_amdgcn_readfirstlane((int)(threadIdx.x / (unsigned)tpr));
+// scalar (and the row base an SGPR pair). A work-group holds several rows
+// only when tpr <= 128 (row_shape), and then tpr is 64 or 128, so the row is
+// a shift of the thread index; with one row per group it is 0. No integer
+// division: these work-groups are short-lived, and a division in the
+// prologue (about 25 dependent scalar instructions) measured 2 us slower on
+// a 32768-row grouping copy.
+__device__ __forceinline__ int row_in_group(int tpr, int rpb) {
+    if (rpb == 1) return 0;
+    return __builtin_amdgcn_readfirstlane((int)threadIdx.x) >> __builtin_ctz((unsigned)tpr);
 }
 
 inline RowShape row_shape(int nvec, int vpt, int max_tpr) {
     int tpr = (nvec + vpt - 1) / vpt;
     tpr = (tpr + kWave - 1) / kWave * kWave;
     if (tpr > max_tpr) tpr = max_tpr;
-    int rpb = 256 / tpr;
+    int rpb = 256 / tpr;  // >= 2 only for tpr = 64 or 128 (row_in_group shifts)
     if (rpb < 1) rpb = 1;
     return {tpr, rpb};
 }
