@@ -59,7 +59,7 @@ constexpr int kMinChunk = MEP_PLAN_CHUNK;              // routes per chunk (at l
 constexpr int kRouteWaves = kRouteThreads / kWave;
 constexpr int kMaxR = 1024;
 constexpr int kMaxE = 1024;
-constexpr int kStageIds = 4096;  // chunk sizes up to this keep their ids in LDS
+constexpr int kStageIds = 2048;  // chunk sizes up to this keep their ids in LDS (plan_routes)
 
 enum { SC_NP = 0, SC_EFIRST_M = 1, SC_NAT_M = 2, SC_FP_M = 3, SC_NIM = 4, SC_SHIFT = 5, SC_COUNT = 16 };
 
@@ -509,6 +509,14 @@ __host__ __device__ inline size_t routes_lds_ints(int E, int R, int T) {
            (T <= kStageIds ? T : 0);
 }
 
+// STAGED: the chunk's ids are copied to LDS (chunks of at most kStageIds
+// routes), else both passes read them from global memory (the second time
+// from L2): pass 1 with several loads in flight per lane, pass 2 loading the
+// next step's ids before this step's work. Larger chunks only occur at
+// N > 2M routes, where leaving the ids out of LDS shortened the table-staging
+// prologue and measured 2 us faster on a 4M-route plan. KEY_BITS: width of
+// the expert ids in the wave multi-split (8 ballots when E <= 256).
+template <bool STAGED, int KEY_BITS>
 __global__ __launch_bounds__(kRouteThreads) void plan_routes(PlanDims d, PlanWs w,
                                                              const int* __restrict__ ids,
                                                              PlanOut o) {
@@ -529,7 +537,6 @@ __global__ __launch_bounds__(kRouteThreads) void plan_routes(PlanDims d, PlanWs 
     const int f0 = src * C + sub * d.T;
     const int f1 = min(f0 + d.T, (src + 1) * C);
     const int len = f1 - f0;
-    const bool staged = d.T <= kStageIds;
 
     // one round trip: every table this block reads, and its routes.
     // For a route of expert e at rank rin among the chunk's routes of e:
@@ -556,7 +563,7 @@ __global__ __launch_bounds__(kRouteThreads) void plan_routes(PlanDims d, PlanWs 
     stage<kRouteThreads, 2>(s_ps, w.pstart, PM);
     stage<kRouteThreads, 2>((i32x4*)s_prec, (const i32x4*)w.prec, PM);
     stage<kRouteThreads, 1>(s_bkt, w.bucket, kBuckets);
-    if (staged) stage<kRouteThreads, kStageIds / kRouteThreads>(s_ids, ids + f0, len);
+    if (STAGED) stage<kRouteThreads, kStageIds / kRouteThreads>(s_ids, ids + f0, len);
     lds_barrier();
 
     // this block's slice of the instance tables inst_cu [R][E+1] and
@@ -599,9 +606,21 @@ __global__ __launch_bounds__(kRouteThreads) void plan_routes(PlanDims d, PlanWs 
     int* my_cnt = s_cnt + wave * E;
 
     // pass 1: per-wave expert counts
-    for (int j = a + lane; j < b; j += kWave) {
-        const int e = staged ? s_ids[j] : ids[f0 + j];
-        if ((unsigned)e < (unsigned)E) atomicAdd(&my_cnt[e], 1);
+    if (STAGED) {
+        for (int j = a + lane; j < b; j += kWave) {
+            const int e = s_ids[j];
+            if ((unsigned)e < (unsigned)E) atomicAdd(&my_cnt[e], 1);
+        }
+    } else {
+        constexpr int U = 4;  // global id loads in flight per lane
+        for (int j0 = a + lane; j0 < b; j0 += U * kWave) {
+            int ev[U];
+#pragma unroll
+            for (int u = 0; u < U; ++u) ev[u] = j0 + u * kWave < b ? ids[f0 + j0 + u * kWave] : -1;
+#pragma unroll
+            for (int u = 0; u < U; ++u)
+                if ((unsigned)ev[u] < (unsigned)E) atomicAdd(&my_cnt[ev[u]], 1);
+        }
     }
     lds_barrier();
     for (int e = tid; e < E; e += kRouteThreads) {
@@ -616,14 +635,22 @@ __global__ __launch_bounds__(kRouteThreads) void plan_routes(PlanDims d, PlanWs 
     lds_barrier();
 
     // pass 2: stable rank within the chunk, then placement
+    int e_next = 0;
+    if (!STAGED && a + lane < b) e_next = ids[f0 + a + lane];
     for (int base = a; base < b; base += kWave) {
         const int j = base + lane;
         const int f = f0 + j;
         bool valid = j < b;
-        int e = valid ? (staged ? s_ids[j] : ids[f]) : 0;
+        int e;
+        if (STAGED) {
+            e = valid ? s_ids[j] : 0;
+        } else {
+            e = valid ? e_next : 0;
+            if (j + kWave < b) e_next = ids[f + kWave];  // before this step's stores
+        }
         valid = valid && (unsigned)e < (unsigned)E;
         if (!valid) e = 0;
-        const uint64_t peers = match_peers(e, valid);
+        const uint64_t peers = match_peers<KEY_BITS>(e, valid);
         const int rin = my_cnt[e] + count_below(peers);
         if (valid && is_group_leader(peers)) my_cnt[e] += __popcll(peers);
         const int4 x0 = s_ex0[e];
@@ -724,9 +751,12 @@ bool lds_ready() {
         bool good = hipFuncSetAttribute((const void*)plan_global,
                                         hipFuncAttributeMaxDynamicSharedMemorySize,
                                         lim) == hipSuccess;
-        good = hipFuncSetAttribute((const void*)plan_routes,
-                                   hipFuncAttributeMaxDynamicSharedMemorySize,
-                                   lim) == hipSuccess && good;
+        for (const void* k : {(const void*)plan_routes<true, 8>, (const void*)plan_routes<true, kKeyBits>,
+                              (const void*)plan_routes<false, 8>,
+                              (const void*)plan_routes<false, kKeyBits>})
+            good = hipFuncSetAttribute(k, hipFuncAttributeMaxDynamicSharedMemorySize, lim) ==
+                       hipSuccess &&
+                   good;
         (void)hipGetLastError();
         return good;
     }();
@@ -791,8 +821,16 @@ extern "C" int mep_plan(int R, int E, int S, int K, int my_rank, const int32_t* 
     MEP_LAUNCH_CHECK();
     hipLaunchKernelGGL(plan_global, dim3(1), dim3(kGlobalThreads), glds, s, d, w, o);
     MEP_LAUNCH_CHECK();
-    hipLaunchKernelGGL(plan_routes, dim3(d.nchunks), dim3(kRouteThreads), rlds, s, d, w,
-                       (const int*)topk_ids, o);
+    // expert ids below 256 need 8 ballots in the multi-split, not 10
+    const dim3 rg(d.nchunks), rb(kRouteThreads);
+    const int* ids = (const int*)topk_ids;
+    if (d.T <= kStageIds) {
+        if (d.E <= 256) hipLaunchKernelGGL((plan_routes<true, 8>), rg, rb, rlds, s, d, w, ids, o);
+        else hipLaunchKernelGGL((plan_routes<true, kKeyBits>), rg, rb, rlds, s, d, w, ids, o);
+    } else {
+        if (d.E <= 256) hipLaunchKernelGGL((plan_routes<false, 8>), rg, rb, rlds, s, d, w, ids, o);
+        else hipLaunchKernelGGL((plan_routes<false, kKeyBits>), rg, rb, rlds, s, d, w, ids, o);
+    }
     MEP_LAUNCH_CHECK();
     return MEP_OK;
 }
