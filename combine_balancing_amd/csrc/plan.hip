@@ -11,9 +11,9 @@
 // GPU design (four launches, all deterministic, no host sync):
 //   plan_hist    one block per chunk of T routes (chunks never straddle a
 //                source rank): per-chunk expert histogram in LDS.
-//   plan_scan    one block per expert: exclusive scan of its column over the
-//                chunks, so chunk c knows how many routes of expert e precede
-//                it in (expert, f) order.
+//   plan_scan    one block per 8 experts: exclusive scan of each expert's
+//                column over the chunks, so chunk c knows how many routes of
+//                expert e precede it in (expert, f) order.
 //   plan_global  one block: expert offsets, native loads, surplus/deficit
 //                scans, the redundant instances (the pieces that the ordered
 //                excess list forms against the ordered deficit list, found by
@@ -49,7 +49,6 @@ namespace {
 #define MEP_PLAN_CHUNK 1024
 #endif
 constexpr int kHistThreads = 256;
-constexpr int kScanThreads = 256;                // plan_scan: 4 experts per work-group
 constexpr int kMaxChunks = MEP_PLAN_MAX_CHUNKS;  // column length of the expert scan
 constexpr int kBuckets = 1024;
 constexpr size_t kMaxLds = 160 * 1024;  // LDS a gfx950 work-group may allocate  // piece lookup: excess index >> shift -> first piece
@@ -131,35 +130,62 @@ __global__ __launch_bounds__(kHistThreads) void plan_hist(PlanDims d, const int*
 }
 
 // ---------------------------------------------------------------- plan_scan
-// One wave per expert: the expert's column of chunk counts (nchunks <=
-// kMaxChunks = 16 per lane) is loaded at once and scanned with a DPP wave
-// scan, so no work-group barrier is needed.
-constexpr int kScanWaves = kScanThreads / kWave;
-constexpr int kScanItems = kMaxChunks / kWave;  // 16
+// Exclusive scan of every expert's column of chunk counts. A work-group
+// takes 8 experts (a 32-byte segment of each chunk row) and cuts the column
+// into 128 ranges of at most kScanItems chunks: lane l of wave w holds
+// expert l % 8 over range 8w + l / 8. Each load instruction of a wave then
+// touches eight 32-byte segments, where one wave per expert with
+// lane-strided chunks touched 64 lines per load. Range sums are scanned
+// across the wave's ranges with shuffles and across the 16 waves through
+// LDS. Measured on MI355X (warm): 8 experts per group beat 4, 16 and 32,
+// and the whole plan went from 63 to 56 us on a 1024-chunk plan.
+#ifndef MEP_PLAN_SCAN_EXPERTS
+#define MEP_PLAN_SCAN_EXPERTS 8
+#endif
+constexpr int kScanExperts = MEP_PLAN_SCAN_EXPERTS;
+constexpr int kScanSubs = kWave / kScanExperts;                   // ranges per wave
+constexpr int kScanThreads = 1024;
+constexpr int kScanRanges = (kScanThreads / kWave) * kScanSubs;  // 128
+constexpr int kScanItems = kMaxChunks / kScanRanges;             // 8
+static_assert(kScanItems * kScanRanges == kMaxChunks, "chunk ranges must cover kMaxChunks");
 
 __global__ __launch_bounds__(kScanThreads) void plan_scan(PlanDims d, int* __restrict__ chunk,
                                                           int* __restrict__ cnt) {
-    const int e = blockIdx.x * kScanWaves + (int)(threadIdx.x / kWave);
-    if (e >= d.E) return;  // whole waves leave together
+    __shared__ int s_wave[kScanThreads / kWave][kScanExperts];
+    const int wave = threadIdx.x / kWave;
     const int lane = lane_id();
-    const int c0 = lane * kScanItems;
+    const int el = lane % kScanExperts, sub = lane / kScanExperts;
+    const int e = blockIdx.x * kScanExperts + el;
+    const bool live = e < d.E;
+    const int per = (d.nchunks + kScanRanges - 1) / kScanRanges;  // <= kScanItems
+    const int c0 = (wave * kScanSubs + sub) * per;
     int v[kScanItems];
     int sum = 0;
 #pragma unroll
     for (int i = 0; i < kScanItems; ++i) {
         const int c = c0 + i;
-        v[i] = c < d.nchunks ? chunk[c * d.E + e] : 0;
+        v[i] = live && i < per && c < d.nchunks ? chunk[c * d.E + e] : 0;
         sum += v[i];
     }
-    const int incl = wave_inclusive_sum(sum);
-    int ex = incl - sum;
+    // inclusive sum over this wave's ranges of the same expert (lanes el + 8k)
+    int incl = sum;
+#pragma unroll
+    for (int k = 1; k < kScanSubs; k *= 2) {
+        const int t = __shfl_up(incl, k * kScanExperts);
+        if (sub >= k) incl += t;
+    }
+    if (sub == kScanSubs - 1) s_wave[wave][el] = incl;
+    __syncthreads();
+    int before = 0;
+    for (int w = 0; w < wave; ++w) before += s_wave[w][el];
+    int ex = before + incl - sum;
 #pragma unroll
     for (int i = 0; i < kScanItems; ++i) {
         const int c = c0 + i;
-        if (c < d.nchunks) chunk[c * d.E + e] = ex;
+        if (live && i < per && c < d.nchunks) chunk[c * d.E + e] = ex;
         ex += v[i];
     }
-    if (lane == kWave - 1) cnt[e] = incl;
+    if (live && wave == kScanThreads / kWave - 1 && sub == kScanSubs - 1) cnt[e] = before + incl;
 }
 
 // -------------------------------------------------------------- plan_global
@@ -816,8 +842,8 @@ extern "C" int mep_plan(int R, int E, int S, int K, int my_rank, const int32_t* 
     hipLaunchKernelGGL(plan_hist, dim3(d.nchunks), dim3(kHistThreads), d.E * sizeof(int), s, d,
                        (const int*)topk_ids, w.chunk);
     MEP_LAUNCH_CHECK();
-    hipLaunchKernelGGL(plan_scan, dim3((d.E + kScanWaves - 1) / kScanWaves), dim3(kScanThreads), 0,
-                       s, d, w.chunk, w.cnt);
+    hipLaunchKernelGGL(plan_scan, dim3((d.E + kScanExperts - 1) / kScanExperts),
+                       dim3(kScanThreads), 0, s, d, w.chunk, w.cnt);
     MEP_LAUNCH_CHECK();
     hipLaunchKernelGGL(plan_global, dim3(1), dim3(kGlobalThreads), glds, s, d, w, o);
     MEP_LAUNCH_CHECK();
