@@ -585,6 +585,14 @@ __global__ __launch_bounds__(kRouteThreads) void plan_routes(PlanDims d, PlanWs 
         s_ex0[e] = make_int4(qbase, off - pre, w.nsend[e], h);
         s_ex1[e] = make_int4(w.uex[h] + qbase - C, nrcv, min(eex - rbh, C), rcv);
     }
+    // this block's share of the instance tables (filled after the barrier):
+    // its first rank record joins this round trip
+    const int E1 = E + 1;
+    const int per = (R * E1 + gridDim.x - 1) / gridDim.x;
+    const int lo = min(blockIdx.x * per, R * E1), hi = min(lo + per, R * E1);
+    const int step_u = kRouteThreads / E1, step_i = kRouteThreads - step_u * E1;
+    const int u0 = (lo + tid) / E1, i0 = (lo + tid) - u0 * E1;
+    const int4 ri0 = lo + tid < hi ? w.rinfo[u0] : make_int4(0, 0, 0, 0);
     for (int i = tid; i < kRouteWaves * E; i += kRouteThreads) s_cnt[i] = 0;
     stage<kRouteThreads, 2>(s_ps, w.pstart, PM);
     stage<kRouteThreads, 2>((i32x4*)s_prec, (const i32x4*)w.prec, PM);
@@ -593,16 +601,12 @@ __global__ __launch_bounds__(kRouteThreads) void plan_routes(PlanDims d, PlanWs 
     lds_barrier();
 
     // this block's slice of the instance tables inst_cu [R][E+1] and
-    // inst_expert [R][E]: idx = u*(E+1) + i, walked without divisions
+    // inst_expert [R][E]: idx = u*(E+1) + i, walked without divisions; the
+    // first step's rank record was loaded with the tables above
     {
-        const int E1 = E + 1;
-        const int total = R * E1;
-        const int per = (total + gridDim.x - 1) / gridDim.x;
-        const int lo = min(blockIdx.x * per, total), hi = min(lo + per, total);
-        const int step_u = kRouteThreads / E1, step_i = kRouteThreads - step_u * E1;
-        int u = (lo + tid) / E1, i = (lo + tid) - u * E1;
+        int u = u0, i = i0;
         for (int idx = lo + tid; idx < hi; idx += kRouteThreads) {
-            const int4 ri = w.rinfo[u];  // {first native, natives, pieces, first piece}
+            const int4 ri = idx == lo + tid ? ri0 : w.rinfo[u];
             int cu = C, ie = -1;
             if (i < ri.y) {
                 ie = ri.x + i;
