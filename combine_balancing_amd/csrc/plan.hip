@@ -353,11 +353,11 @@ __global__ __launch_bounds__(kGlobalThreads) void plan_global(PlanDims d, PlanWs
     lds_barrier();
 
     // D. deficit starts that coincide with an expert's excess start
-    int coin = 0;
+    int coin = 0, lb_d = 0;  // lb_d: first excess start >= this deficit start
     if (tid < NU) {
         const int s = g.cdl[tid];
-        const int lb = lower_bound(g.cjs, NS, s);
-        coin = lb < NS && g.cjs[lb] == s;
+        lb_d = lower_bound(g.cjs, NS, s);
+        coin = lb_d < NS && g.cjs[lb_d] == s;
     }
     int NC;
     const int ci = block_exclusive_sum(coin, scratch, &NC);
@@ -374,7 +374,8 @@ __global__ __launch_bounds__(kGlobalThreads) void plan_global(PlanDims d, PlanWs
         const int e = g.cje[tid];
         const int lb = lower_bound(g.cdl, NU, s);
         const int pi = tid + lb - g.coin[lb];
-        const int u = g.cdu[upper_bound(g.cdl, NU, s) - 1];
+        // deficit starts are strictly increasing: upper_bound = lb + (equal)
+        const int u = g.cdu[lb + (lb < NU && g.cdl[lb] == s) - 1];
         const int kp = g.kept[e];
         const int end = min(s + g.cnt[e] - kp, g.dex[u] + (C - g.L[u]));
         g.pst[pi] = s;
@@ -386,7 +387,7 @@ __global__ __launch_bounds__(kGlobalThreads) void plan_global(PlanDims d, PlanWs
     if (tid < NU && !coin) {
         const int s = g.cdl[tid];
         const int u = g.cdu[tid];
-        const int lb = lower_bound(g.cjs, NS, s);
+        const int lb = lb_d;
         const int pi = tid + lb - g.coin[tid];
         const int e = g.cje[lb - 1];
         const int jse = g.js[e];
@@ -398,7 +399,7 @@ __global__ __launch_bounds__(kGlobalThreads) void plan_global(PlanDims d, PlanWs
         g.pn[pi] = end - s;
         g.ppos[pi] = g.eex[e] + kp + (s - jse);
     }
-    if (tid < NU) g.fp[g.cdu[tid]] = tid + lower_bound(g.cjs, NS, g.cdl[tid]) - g.coin[tid];
+    if (tid < NU) g.fp[g.cdu[tid]] = tid + lb_d - g.coin[tid];
     if (tid == 0) g.pst[NP] = totU;
     lds_barrier();
     if (tid < NU) {
