@@ -82,7 +82,12 @@ __device__ __forceinline__ int wave_inclusive_sum(int x) {
 
 // Exclusive block-wide sum. `scratch` holds at least blockDim/64 + 1 ints of
 // LDS. Every thread of the block must call it (it uses lds_barrier). Returns the exclusive prefix;
-// *total receives the block sum.
+// *total receives the block sum. CLOSE = false leaves out the closing
+// barrier that lets the next call reuse `scratch`: the caller then
+// alternates two scratch buffers between consecutive calls (a call's two
+// barriers keep the buffer of the call before it from being rewritten
+// while it is still read).
+template <bool CLOSE = true>
 __device__ __forceinline__ int block_exclusive_sum(int v, int* scratch, int* total) {
     const int lane = threadIdx.x & (kWave - 1);
     const int wave = threadIdx.x / kWave;
@@ -99,12 +104,13 @@ __device__ __forceinline__ int block_exclusive_sum(int v, int* scratch, int* tot
     lds_barrier();
     const int res = inc - v + scratch[wave];
     *total = scratch[nw];
-    lds_barrier();
+    if (CLOSE) lds_barrier();
     return res;
 }
 
 // Two exclusive block-wide sums with one pair of barriers. `scratch` holds
-// at least 2*(blockDim/64 + 1) ints of LDS.
+// at least 2*(blockDim/64 + 1) ints of LDS. CLOSE as for block_exclusive_sum.
+template <bool CLOSE = true>
 __device__ __forceinline__ void block_exclusive_sum2(int a, int b, int* scratch, int* ea, int* eb,
                                                      int* ta, int* tb) {
     const int lane = threadIdx.x & (kWave - 1);
@@ -138,7 +144,7 @@ __device__ __forceinline__ void block_exclusive_sum2(int a, int b, int* scratch,
     *eb = ib - b + sb[wave];
     *ta = sa[nw];
     *tb = sb[nw];
-    lds_barrier();
+    if (CLOSE) lds_barrier();
 }
 
 // Smallest index i in [0, n) with a[i] >= x (n if none).

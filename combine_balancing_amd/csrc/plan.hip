@@ -201,7 +201,7 @@ struct GlobalLds {
 
 __host__ __device__ inline size_t global_lds_ints(int E, int R) {
     return (size_t)8 * E + 1 + (size_t)13 * R + 10 + (size_t)5 * (E + R) + 1 +
-           2 * (kGlobalThreads / kWave + 1);
+           4 * (kGlobalThreads / kWave + 1);
 }
 
 __device__ inline GlobalLds carve_global(int* p, int E, int R) {
@@ -267,7 +267,10 @@ __global__ __launch_bounds__(kGlobalThreads) void plan_global(PlanDims d, PlanWs
     const int E = d.E, R = d.R, C = d.C, m = d.m;
     const int tid = threadIdx.x, NT = blockDim.x;
     const GlobalLds g = carve_global(lds, E, R);
-    int* scratch = g.scratch;
+    // two scan buffers, alternated between the block scans so that a scan
+    // needs no closing barrier
+    int* scr0 = g.scratch;
+    int* scr1 = g.scratch + 2 * (kGlobalThreads / kWave + 1);
 
     // A. one round trip: expert totals and this rank's per-expert offsets
     int c = 0, pm = 0, pm1 = 0;
@@ -277,7 +280,7 @@ __global__ __launch_bounds__(kGlobalThreads) void plan_global(PlanDims d, PlanWs
         pm1 = m + 1 < R ? w.chunk[((m + 1) * d.cps) * E + tid] : -1;
     }
     int total;
-    const int ex = block_exclusive_sum(c, scratch, &total);
+    const int ex = block_exclusive_sum<false>(c, scr0, &total);
     if (tid < E) {
         g.cnt[tid] = c;
         g.eex[tid] = ex;
@@ -311,7 +314,7 @@ __global__ __launch_bounds__(kGlobalThreads) void plan_global(PlanDims d, PlanWs
         o.rank_load[tid] = Lr;
     }
     int uex, dex, totU, totD;
-    block_exclusive_sum2(U, D, scratch, &uex, &dex, &totU, &totD);
+    block_exclusive_sum2<false>(U, D, scr1, &uex, &dex, &totU, &totD);
     if (tid < R) {
         g.uex[tid] = uex;
         g.dex[tid] = dex;
@@ -340,7 +343,7 @@ __global__ __launch_bounds__(kGlobalThreads) void plan_global(PlanDims d, PlanWs
     }
     if (tid < R) under = g.L[tid] < C;
     int si, ui, NS, NU;
-    block_exclusive_sum2(spill, under, scratch, &si, &ui, &NS, &NU);
+    block_exclusive_sum2<false>(spill, under, scr0, &si, &ui, &NS, &NU);
     if (spill) {
         g.cjs[si] = js;
         g.cje[si] = tid;
@@ -360,7 +363,7 @@ __global__ __launch_bounds__(kGlobalThreads) void plan_global(PlanDims d, PlanWs
         coin = lb_d < NS && g.cjs[lb_d] == s;
     }
     int NC;
-    const int ci = block_exclusive_sum(coin, scratch, &NC);
+    const int ci = block_exclusive_sum<false>(coin, scr1, &NC);
     if (tid < NU) g.coin[tid] = ci;
     if (tid == 0) g.coin[NU] = NC;
     lds_barrier();
@@ -416,7 +419,7 @@ __global__ __launch_bounds__(kGlobalThreads) void plan_global(PlanDims d, PlanWs
         o.inst_count[tid] = ic;
     }
     int NI;
-    const int gb = block_exclusive_sum(ic, scratch, &NI);
+    const int gb = block_exclusive_sum<false>(ic, scr0, &NI);
     if (tid < R) {
         g.gid[tid] = gb;
         o.inst_gid_base[tid] = gb;
@@ -445,7 +448,7 @@ __global__ __launch_bounds__(kGlobalThreads) void plan_global(PlanDims d, PlanWs
             sum += clampi(P + n - g.eex[e] - g.prem[e], 0, Hm) - clampi(P - g.eex[e] - g.prem[e], 0, Hm);
         }
         int tot;
-        int run = block_exclusive_sum(sum, scratch, &tot);
+        int run = block_exclusive_sum<false>(sum, scr1, &tot);
         for (int gi = g0; gi < g1; ++gi) {
             const int u = upper_bound(g.gid, R + 1, gi) - 1;
             int e, P, n, pi;
@@ -485,7 +488,7 @@ __global__ __launch_bounds__(kGlobalThreads) void plan_global(PlanDims d, PlanWs
             sum += clampi(P + n - g.eex[e] - pre, 0, Hs) - clampi(P - g.eex[e] - pre, 0, Hs);
         }
         int tot;
-        int run = block_exclusive_sum(sum, scratch, &tot);
+        int run = block_exclusive_sum<false>(sum, scr0, &tot);
         for (int q = q0i; q < q1i; ++q) {
             const int src = q / nim, i = q - src * nim;
             int e, P, n, pi;
