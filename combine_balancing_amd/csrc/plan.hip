@@ -53,6 +53,7 @@ constexpr int kMaxChunks = MEP_PLAN_MAX_CHUNKS;  // column length of the expert 
 constexpr int kBuckets = 1024;
 constexpr size_t kMaxLds = 160 * 1024;  // LDS a gfx950 work-group may allocate  // piece lookup: excess index >> shift -> first piece
 constexpr int kGlobalThreads = 1024;
+constexpr int kItemCache = 4;  // plan_global: per-thread items kept between two passes
 constexpr int kRouteThreads = MEP_PLAN_ROUTE_THREADS;  // work-group of plan_routes
 constexpr int kMinChunk = MEP_PLAN_CHUNK;              // routes per chunk (at least)
 constexpr int kRouteWaves = kRouteThreads / kWave;
@@ -435,42 +436,65 @@ __global__ __launch_bounds__(kGlobalThreads) void plan_global(PlanDims d, PlanWs
         w.rinfo[u] = make_int4(g.ef[u], g.ef[u + 1] - g.ef[u], g.np[u], g.fp[u]);
 
     // H. send bases of this rank: instances in gid order = (dest, slot)
-    //    order; c_m(I) = this rank's routes inside instance I.
+    //    order; c_m(I) = this rank's routes inside instance I. A thread's
+    //    items (at most 3: NI <= 2E + R - 1) keep what the first pass found
+    //    for the second, which would otherwise repeat the dependent LDS
+    //    lookups after the scan's barriers.
     {
         const int ipt = (NI + NT - 1) / NT;
         const int g0 = min(tid * ipt, NI), g1 = min(g0 + ipt, NI);
-        int sum = 0;
-        for (int gi = g0; gi < g1; ++gi) {
+        int hq0[kItemCache], hcm[kItemCache], hpi[kItemCache], he[kItemCache], hfirst[kItemCache];
+        auto counts = [&](int gi, int* q0, int* cm, int* pi_out, int* e_out, int* first) {
             const int u = upper_bound(g.gid, R + 1, gi) - 1;
             int e, P, n, pi;
             inst_of(g, u, gi - g.gid[u], &e, &P, &n, &pi);
             const int Hm = g.prem1[e] - g.prem[e];
-            sum += clampi(P + n - g.eex[e] - g.prem[e], 0, Hm) - clampi(P - g.eex[e] - g.prem[e], 0, Hm);
+            *q0 = clampi(P - g.eex[e] - g.prem[e], 0, Hm);
+            *cm = clampi(P + n - g.eex[e] - g.prem[e], 0, Hm) - *q0;
+            *pi_out = pi;
+            *e_out = e;
+            *first = gi == g.gid[u] ? u : -1;
+        };
+        int sum = 0;
+#pragma unroll
+        for (int k = 0; k < kItemCache; ++k) {
+            hcm[k] = 0;
+            if (g0 + k < g1) counts(g0 + k, &hq0[k], &hcm[k], &hpi[k], &he[k], &hfirst[k]);
+            sum += hcm[k];
+        }
+        for (int gi = g0 + kItemCache; gi < g1; ++gi) {
+            int q0, cm, pi, e, first;
+            counts(gi, &q0, &cm, &pi, &e, &first);
+            sum += cm;
         }
         int tot;
         int run = block_exclusive_sum<false>(sum, scr1, &tot);
-        for (int gi = g0; gi < g1; ++gi) {
-            const int u = upper_bound(g.gid, R + 1, gi) - 1;
-            int e, P, n, pi;
-            inst_of(g, u, gi - g.gid[u], &e, &P, &n, &pi);
-            const int Hm = g.prem1[e] - g.prem[e];
-            const int q0 = clampi(P - g.eex[e] - g.prem[e], 0, Hm);
-            const int cm = clampi(P + n - g.eex[e] - g.prem[e], 0, Hm) - q0;
+        auto place = [&](int q0, int cm, int pi, int e, int first) {
             if (pi < 0) {
                 w.nsend[e] = run - q0;
             } else {
                 const int host = g.phost[pi];
                 w.prec[pi] = make_int4(host, g.L[host] - g.dex[host], run - q0, g.pexp[pi]);
             }
-            if (gi == g.gid[u]) g.sbase[u] = run;
+            if (first >= 0) g.sbase[first] = run;
             run += cm;
+        };
+#pragma unroll
+        for (int k = 0; k < kItemCache; ++k)
+            if (g0 + k < g1) place(hq0[k], hcm[k], hpi[k], he[k], hfirst[k]);
+        for (int gi = g0 + kItemCache; gi < g1; ++gi) {
+            int q0, cm, pi, e, first;
+            counts(gi, &q0, &cm, &pi, &e, &first);
+            place(q0, cm, pi, e, first);
         }
         if (tid == 0) g.sbase[R] = tot;
     }
 
     // I. receive bases of this rank: items (source, local instance i) in
     //    arrival order; recvbase = sources' rows before the item minus the
-    //    item's start rank within its expert.
+    //    item's start rank within its expert. The first kItemCache items of
+    //    a thread keep their counts (two global loads each) for the second
+    //    pass.
     const int ef_m = g.ef[m];
     const int nat_m = g.ef[m + 1] - ef_m;
     const int nim = nat_m + g.np[m];
@@ -478,28 +502,43 @@ __global__ __launch_bounds__(kGlobalThreads) void plan_global(PlanDims d, PlanWs
         const int items = R * nim;
         const int ipt = (items + NT - 1) / NT;
         const int q0i = min(tid * ipt, items), q1i = min(q0i + ipt, items);
-        int sum = 0;
-        for (int q = q0i; q < q1i; ++q) {
+        int rq0[kItemCache], rcs[kItemCache];
+        auto counts = [&](int q, int* q0, int* cs) {
             const int src = q / nim, i = q - src * nim;
             int e, P, n, pi;
             inst_of(g, m, i, &e, &P, &n, &pi);
             const int pre = pre_of(d, w.chunk, g.cnt, src, e);
             const int Hs = pre_of(d, w.chunk, g.cnt, src + 1, e) - pre;
-            sum += clampi(P + n - g.eex[e] - pre, 0, Hs) - clampi(P - g.eex[e] - pre, 0, Hs);
+            *q0 = clampi(P - g.eex[e] - pre, 0, Hs);
+            *cs = clampi(P + n - g.eex[e] - pre, 0, Hs) - *q0;
+        };
+        int sum = 0;
+#pragma unroll
+        for (int k = 0; k < kItemCache; ++k) {
+            rcs[k] = 0;
+            if (q0i + k < q1i) counts(q0i + k, &rq0[k], &rcs[k]);
+            sum += rcs[k];
+        }
+        for (int q = q0i + kItemCache; q < q1i; ++q) {
+            int q0, cs;
+            counts(q, &q0, &cs);
+            sum += cs;
         }
         int tot;
         int run = block_exclusive_sum<false>(sum, scr0, &tot);
-        for (int q = q0i; q < q1i; ++q) {
+        auto place = [&](int q, int q0, int cs) {
             const int src = q / nim, i = q - src * nim;
-            int e, P, n, pi;
-            inst_of(g, m, i, &e, &P, &n, &pi);
-            const int pre = pre_of(d, w.chunk, g.cnt, src, e);
-            const int Hs = pre_of(d, w.chunk, g.cnt, src + 1, e) - pre;
-            const int q0 = clampi(P - g.eex[e] - pre, 0, Hs);
-            const int cs = clampi(P + n - g.eex[e] - pre, 0, Hs) - q0;
             w.recvbase[src * E + i] = run - q0;
             if (i == 0) g.roff[src] = run;
             run += cs;
+        };
+#pragma unroll
+        for (int k = 0; k < kItemCache; ++k)
+            if (q0i + k < q1i) place(q0i + k, rq0[k], rcs[k]);
+        for (int q = q0i + kItemCache; q < q1i; ++q) {
+            int q0, cs;
+            counts(q, &q0, &cs);
+            place(q, q0, cs);
         }
         if (tid == 0) g.roff[R] = tot;
     }
