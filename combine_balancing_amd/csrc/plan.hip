@@ -262,6 +262,16 @@ __device__ __forceinline__ int pre_of(const PlanDims& d, const int* chunk, const
     return src >= d.R ? cnt[e] : chunk[(src * d.cps) * d.E + e];
 }
 
+// Exclusive sum when only the first wave holds values (R <= 64 for the
+// per-rank scans): that wave scans alone, with no barrier; the total goes to
+// that wave, and the caller publishes it through LDS at its next barrier.
+// Call with the whole first wave.
+__device__ __forceinline__ int wave0_exclusive_sum(int v, int* total) {
+    const int inc = wave_inclusive_sum(v);
+    *total = __builtin_amdgcn_readlane(inc, kWave - 1);
+    return inc - v;
+}
+
 // One element per thread in the per-expert and per-rank phases (E, R <= NT).
 __global__ __launch_bounds__(kGlobalThreads) void plan_global(PlanDims d, PlanWs w, PlanOut o) {
     extern __shared__ int lds[];
@@ -304,18 +314,24 @@ __global__ __launch_bounds__(kGlobalThreads) void plan_global(PlanDims d, PlanWs
         g.rb[r] = rb;
         w.rb[r] = rb;
     }
-    lds_barrier();
     int U = 0, D = 0;
     if (tid < R) {
-        const int Lr = g.rb[tid + 1] - g.rb[tid];
+        const int Lr = g.eex[efirst_of(tid + 1, R, E)] - g.eex[efirst_of(tid, R, E)];
         U = max(Lr - C, 0);
         D = max(C - Lr, 0);
         g.L[tid] = Lr;
         w.load[tid] = Lr;
         o.rank_load[tid] = Lr;
     }
-    int uex, dex, totU, totD;
-    block_exclusive_sum2<false>(U, D, scr1, &uex, &dex, &totU, &totD);
+    int uex = 0, dex = 0, totU, totD;
+    if (R <= kWave) {
+        if (tid < kWave) {
+            uex = wave0_exclusive_sum(U, &totU);
+            dex = wave0_exclusive_sum(D, &totD);
+        }
+    } else {
+        block_exclusive_sum2<false>(U, D, scr1, &uex, &dex, &totU, &totD);
+    }
     if (tid < R) {
         g.uex[tid] = uex;
         g.dex[tid] = dex;
@@ -329,6 +345,8 @@ __global__ __launch_bounds__(kGlobalThreads) void plan_global(PlanDims d, PlanWs
         w.dex[R] = totD;
     }
     lds_barrier();
+    totU = g.uex[R];
+    totD = g.dex[R];
 
     // C. rows of each expert kept at home, start of its excess; compacted
     //    lists of spilling experts and under-loaded ranks
@@ -363,11 +381,16 @@ __global__ __launch_bounds__(kGlobalThreads) void plan_global(PlanDims d, PlanWs
         lb_d = lower_bound(g.cjs, NS, s);
         coin = lb_d < NS && g.cjs[lb_d] == s;
     }
-    int NC;
-    const int ci = block_exclusive_sum<false>(coin, scr1, &NC);
+    int NC, ci = 0;  // NU <= R
+    if (R <= kWave) {
+        if (tid < kWave) ci = wave0_exclusive_sum(coin, &NC);
+    } else {
+        ci = block_exclusive_sum<false>(coin, scr1, &NC);
+    }
     if (tid < NU) g.coin[tid] = ci;
     if (tid == 0) g.coin[NU] = NC;
     lds_barrier();
+    NC = g.coin[NU];
     const int NP = NS + NU - NC;
 
     // E. pieces (redundant instances): the excess list [0, totU) cut at every
@@ -419,8 +442,12 @@ __global__ __launch_bounds__(kGlobalThreads) void plan_global(PlanDims d, PlanWs
         ic = g.ef[tid + 1] - g.ef[tid] + g.np[tid];
         o.inst_count[tid] = ic;
     }
-    int NI;
-    const int gb = block_exclusive_sum<false>(ic, scr0, &NI);
+    int NI, gb = 0;
+    if (R <= kWave) {
+        if (tid < kWave) gb = wave0_exclusive_sum(ic, &NI);
+    } else {
+        gb = block_exclusive_sum<false>(ic, scr0, &NI);
+    }
     if (tid < R) {
         g.gid[tid] = gb;
         o.inst_gid_base[tid] = gb;
@@ -430,6 +457,7 @@ __global__ __launch_bounds__(kGlobalThreads) void plan_global(PlanDims d, PlanWs
         o.inst_gid_base[R] = NI;
     }
     lds_barrier();
+    NI = g.gid[R];
 
     // G. per-rank instance layout for the table fill done by plan_routes
     for (int u = tid; u < R; u += NT)
