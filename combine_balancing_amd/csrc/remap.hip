@@ -55,6 +55,11 @@ __device__ __forceinline__ float scale_value(uint32_t raw, int dtype) {
 // multiply-shift reciprocals instead of integer divisions: t = (i*kmag) >> 21
 // for i < 8192 and K <= 16, and t / count = (t*m) >> 20 for t < 512 and
 // count <= 1024, with kmag = ceil(2^21/K) and m = ceil(2^20/count).
+// TAB_STAGED: the table fits the LDS stage (E*F <= kStageTable) and is read
+// from LDS; otherwise from global memory. A compile-time choice keeps the
+// table reads plain LDS loads (a pointer chosen at run time between the two
+// made them generic loads, which wait on both memory counters).
+template <bool TAB_STAGED>
 __global__ __launch_bounds__(kRemapThreads) void remap_prune_kernel(RemapArgs a) {
     // s_tab is dead once the ids are remapped; the send-map counters reuse
     // its space.
@@ -75,7 +80,6 @@ __global__ __launch_bounds__(kRemapThreads) void remap_prune_kernel(RemapArgs a)
     const int n_inst = a.ws * a.ppr;
     const bool pruning = a.scales != nullptr;
     const int tab_n = a.E * a.F;
-    const bool tab_staged = tab_n <= kStageTable;
     const unsigned kmag = ((1u << 21) + a.K - 1) / a.K;
     const int S1 = a.BS + 1;
 
@@ -103,7 +107,7 @@ __global__ __launch_bounds__(kRemapThreads) void remap_prune_kernel(RemapArgs a)
             }
         }
     }
-    if (tab_staged) stage<kRemapThreads, kStageTable / kRemapThreads>(s_tab, a.table, tab_n);
+    if (TAB_STAGED) stage<kRemapThreads, kStageTable / kRemapThreads>(s_tab, a.table, tab_n);
     if (pruning && tid < a.K) s_thr[tid] = a.thr[tid];
     if (tid < a.BS) s_act[tid] = (pruning && a.active) ? (a.active[tid] != 0) : 1;
     if (pruning) {
@@ -115,7 +119,7 @@ __global__ __launch_bounds__(kRemapThreads) void remap_prune_kernel(RemapArgs a)
         }
     }
     lds_barrier();
-    const int* tab = tab_staged ? s_tab : a.table;
+    const int* tab = TAB_STAGED ? s_tab : a.table;
 
     // 2. per expert: the mode-0 column (it depends on the rank and the
     //    expert's count only) or the count's reciprocal for mode 1; per
@@ -184,7 +188,7 @@ __global__ __launch_bounds__(kRemapThreads) void remap_prune_kernel(RemapArgs a)
     if (tid < n_inst)
         for (int v = 0; v < kCountWaves; ++v) tot += s_cnt[v * n_inst + tid];
     int all;
-    const int base = block_exclusive_sum(tot, scratch, &all);
+    const int base = block_exclusive_sum<false>(tot, scratch, &all);  // scratch is not reused
     if (tid < n_inst) {
         s_tot[tid] = tot;
         int run = base;
@@ -243,8 +247,12 @@ extern "C" int mep_remap_prune(int BS, int K, int E, int F, int world_size, int 
     RemapArgs a{BS, K, E, F, world_size, place_per_rank, local_rank_id, balance_mode, scale_dtype,
                 (const int*)expert_ids, (const int*)eplb_table, expert_scales, pruning_threshold,
                 active_mask, (int*)balanced_ids, balanced_mask, (int*)send_pos, (int*)send_count};
-    hipLaunchKernelGGL(remap_prune_kernel, dim3(1), dim3(kRemapThreads), 0, (hipStream_t)stream,
-                       a);
+    if ((long long)E * F <= kStageTable)
+        hipLaunchKernelGGL(remap_prune_kernel<true>, dim3(1), dim3(kRemapThreads), 0,
+                           (hipStream_t)stream, a);
+    else
+        hipLaunchKernelGGL(remap_prune_kernel<false>, dim3(1), dim3(kRemapThreads), 0,
+                           (hipStream_t)stream, a);
     MEP_LAUNCH_CHECK();
     return MEP_OK;
 }
