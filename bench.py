@@ -118,7 +118,10 @@ def cpu_baseline(d, plan_ref, budget_s=10.0):
             "sample": f"{len(passes)} full passes of pack+group+combine, {WORKLOAD} rank 0 "
                       f"({total} algorithmic bytes each), median {dt:.3f} s per pass, "
                       f"{time.perf_counter() - t_start:.1f} s in all",
-            "plan_s": round(plan_s, 4), "host_cpu": cpu_model(),
+            "plan_s": round(plan_s, 4),
+            "routes_per_s_dispatch_combine": round(S * K / dt, 1),
+            "routes_per_s_plan": round(d["R"] * S * K / plan_s, 1),
+            "host_cpu": cpu_model(),
             "host_cpu_count": os.cpu_count()}
 
 
