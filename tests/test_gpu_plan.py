@@ -126,10 +126,10 @@ def test_plan_rejects_bad_arguments():
         cba.plan(ids, 2, 4, 4, 2, my_rank=0, workspace=ws[:16])
 
 
-@pytest.mark.parametrize("target", [0.2, 20.0])
+@pytest.mark.parametrize("target", [0.2, 1.0, 10.0, 20.0])
 def test_plan_skew_sweep(orc, target):
-    # the imbalance sweep's shape (R=8, E=384, S=8192, K=8) at its mildest and
-    # strongest point: every plan output bit-exact
+    # the imbalance sweep's shape (R=8, E=384, S=8192, K=8) at every point the
+    # benchmark times: every plan output bit-exact
     require_gpu()
     d = synth.make_sweep_routing(target)
     R, E, S, K = d["R"], d["E"], d["S"], d["K"]
