@@ -275,8 +275,10 @@ int mep_combine(int T, int K, int H, const uint16_t* y_ret, int n_y,
  *              of other GPUs mapped into this process on a multi-GPU system;
  *              slices of one allocation on one GPU).
  * Run by every rank, this fills each rank's grouped buffer with exactly what
- * pack -> exchange -> group produces. Sizes as mep_dispatch's pack, R, C >= 1;
- * T == 0 does nothing. Errors: MEP_ERR_NULLPTR, MEP_ERR_SHAPE, MEP_ERR_HIP.
+ * pack -> exchange -> group produces. Sizes as mep_dispatch's pack,
+ * 1 <= R <= 1024 (mep_plan's rank limit; the pointer table is staged in
+ * on-chip memory), C >= 1; T == 0 does nothing.
+ * Errors: MEP_ERR_NULLPTR, MEP_ERR_SHAPE, MEP_ERR_HIP.
  */
 int mep_dispatch_to_peers(int T, int K, int H, int R, int C, const uint16_t* x,
                           const int32_t* route_dest, const int32_t* route_slot,
@@ -290,9 +292,9 @@ int mep_dispatch_to_peers(int T, int K, int H, int R, int C, const uint16_t* x,
  *   out[t,h] = sum over k of scores[t*K+k] * peer_bufs[dest][slot, h]
  * with (dest, slot) = (route_dest, route_slot)[t*K+k] of this rank's routes;
  * out-of-range entries are skipped. peer_bufs: DEVICE array of R device
- * pointers to [C,H] bf16 grouped expert outputs. Outputs and errors as
- * mep_combine. With the same values it gives the same bits as mep_combine
- * on the returned rows.
+ * pointers to [C,H] bf16 grouped expert outputs, 1 <= R <= 1024, C >= 1.
+ * Outputs and errors as mep_combine. With the same values it gives the same
+ * bits as mep_combine on the returned rows.
  */
 int mep_combine_from_peers(int T, int K, int H, int R, int C,
                            const uint16_t* const* peer_bufs,

@@ -153,11 +153,13 @@ def test_zero_copy_and_ungroup_validation(B):
     assert P(4, 2, 64, 4, 8, None, 16, 16, 16, None) == B.MEP_ERR_NULLPTR
     assert P(4, 2, 60, 4, 8, 16, 16, 16, 16, None) == B.MEP_ERR_SHAPE
     assert P(4, 2, 64, 0, 8, 16, 16, 16, 16, None) == B.MEP_ERR_SHAPE
+    assert P(4, 2, 64, 1025, 8, 16, 16, 16, 16, None) == B.MEP_ERR_SHAPE   # R > 1024
     assert P(4, 2, 64, 4, 8, 8, 16, 16, 16, None) == B.MEP_ERR_SHAPE      # unaligned x
     Q = B.mep_combine_from_peers
     assert Q(0, 2, 64, 4, 8, None, None, None, None, None, None, None) == B.MEP_OK
     assert Q(4, 2, 64, 4, 8, 16, 16, 16, 16, None, None, None) == B.MEP_ERR_NULLPTR
     assert Q(4, 0, 64, 4, 8, 16, 16, 16, 16, 16, None, None) == B.MEP_ERR_SHAPE
+    assert Q(4, 2, 64, 1025, 8, 16, 16, 16, 16, 16, None, None) == B.MEP_ERR_SHAPE  # R > 1024
     U = B.mep_ungroup
     assert U(0, 64, None, None, None, None) == B.MEP_OK
     assert U(4, 64, None, 16, 16, None) == B.MEP_ERR_NULLPTR
