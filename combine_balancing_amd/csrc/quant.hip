@@ -189,24 +189,58 @@ __global__ __launch_bounds__(kQuantThreads) void quant_pack_rows(
     }
 }
 
-// x_q[t] = codes of message recv_pos[t], scales[t] = its scale. One thread
-// per (row, unit) in 256-thread work-groups, the unit being 16 bytes when
-// rows of H bytes stay 16-byte aligned (H % 16 == 0) and 8 bytes otherwise;
-// the thread of unit 0 also copies the scale.
-template <typename U>
-__global__ __launch_bounds__(kFlatThreads) void quant_group_flat(
+// x_q[t] = codes of message recv_pos[t], scales[t] = its scale. One
+// work-group per row, as the bf16 grouping copy; the unit U is 16 bytes when
+// rows of H bytes stay 16-byte aligned (H % 16 == 0) and 8 bytes otherwise,
+// and thread 0 copies the scale. (A flat launch, one thread per (row, unit),
+// measured 1 us slower at H = 7168.)
+template <typename U, int VPT>
+__global__ __launch_bounds__(kMaxTpr) void quant_group_rows(
     const uint8_t* __restrict__ msgs, int msg_bytes, int hq, int n_msgs,
-    const int* __restrict__ recv_pos, U* __restrict__ x_q, float* __restrict__ scales,
-    uint32_t total, FastDiv rowdiv) {
-    const uint32_t i = blockIdx.x * kFlatThreads + threadIdx.x;
-    if (i >= total) return;
-    const uint32_t t = fast_div(i, rowdiv);
-    const uint32_t u = i - t * rowdiv.d;
+    const int* __restrict__ recv_pos, U* __restrict__ x_q, float* __restrict__ scales, int n,
+    int nunits, int tpr, int rpb) {
+    const int r = row_in_group(tpr, rpb);
+    const int tid = threadIdx.x - r * tpr;
+    const int t = blockIdx.x * rpb + r;
+    if (t >= n) return;
     const int from = recv_pos[t];
     if ((unsigned)from >= (unsigned)n_msgs) return;
     const uint8_t* m = msgs + (size_t)from * msg_bytes;
-    __builtin_nontemporal_store(__builtin_nontemporal_load((const U*)m + u), x_q + i);
-    if (u == 0) scales[t] = *(const float*)(m + hq);
+    const U* src = (const U*)m;
+    U* dst = x_q + (size_t)t * nunits;
+    for (int v0 = 0; v0 < nunits; v0 += tpr * VPT) {
+        U q[VPT];
+#pragma unroll
+        for (int i = 0; i < VPT; ++i) {
+            const int v = v0 + i * tpr + tid;
+            if (v < nunits) q[i] = __builtin_nontemporal_load(src + v);
+        }
+#pragma unroll
+        for (int i = 0; i < VPT; ++i) {
+            const int v = v0 + i * tpr + tid;
+            if (v < nunits) __builtin_nontemporal_store(q[i], dst + v);
+        }
+    }
+    if (tid == 0) scales[t] = *(const float*)(m + hq);
+}
+
+template <typename U>
+void launch_group_quant_rows(hipStream_t s, const uint8_t* msgs, int msg_bytes, int hq,
+                             int n_msgs, const int* rp, U* xq, float* sc, int n, int nunits) {
+    int vpt = 1;
+    while (vpt < 8 && nunits > kMaxTpr * vpt) vpt *= 2;
+    const RowShape rs = row_shape(nunits, vpt, kMaxTpr);
+    const dim3 g((n + rs.rpb - 1) / rs.rpb), b(rs.tpr * rs.rpb);
+#define MEP_QG_LAUNCH(V)                                                                        \
+    hipLaunchKernelGGL((quant_group_rows<U, V>), g, b, 0, s, msgs, msg_bytes, hq, n_msgs, rp, xq, \
+                       sc, n, nunits, rs.tpr, rs.rpb)
+    switch (vpt) {
+        case 1: MEP_QG_LAUNCH(1); break;
+        case 2: MEP_QG_LAUNCH(2); break;
+        case 4: MEP_QG_LAUNCH(4); break;
+        default: MEP_QG_LAUNCH(8); break;
+    }
+#undef MEP_QG_LAUNCH
 }
 
 }  // namespace
@@ -278,17 +312,13 @@ extern "C" int mep_group_quant(int n, int H, int msg_bytes, const int32_t* recv_
         return MEP_ERR_SHAPE;
     const bool wide = (H % 16) == 0 && aligned16(x_q);
     const int unit = wide ? 16 : 8;
-    const uint32_t total = (uint32_t)n * (uint32_t)(H / unit);
-    const dim3 g((total + kFlatThreads - 1) / kFlatThreads), b(kFlatThreads);
-    const FastDiv dv = make_fastdiv((uint32_t)(H / unit));
+    hipStream_t s = (hipStream_t)stream;
     if (wide)
-        hipLaunchKernelGGL(quant_group_flat<u32x4>, g, b, 0, (hipStream_t)stream, recv_msgs,
-                           msg_bytes, hq, n_msgs, (const int*)recv_pos, (u32x4*)x_q, scales,
-                           total, dv);
+        launch_group_quant_rows(s, recv_msgs, msg_bytes, hq, n_msgs, (const int*)recv_pos,
+                                (u32x4*)x_q, scales, n, H / unit);
     else
-        hipLaunchKernelGGL(quant_group_flat<u32x2>, g, b, 0, (hipStream_t)stream, recv_msgs,
-                           msg_bytes, hq, n_msgs, (const int*)recv_pos, (u32x2*)x_q, scales,
-                           total, dv);
+        launch_group_quant_rows(s, recv_msgs, msg_bytes, hq, n_msgs, (const int*)recv_pos,
+                                (u32x2*)x_q, scales, n, H / unit);
     MEP_LAUNCH_CHECK();
     return MEP_OK;
 }
