@@ -74,6 +74,17 @@ __global__ __launch_bounds__(kNormThreads) void combine_norm_rows(
 #pragma unroll
         for (int j = 0; j < 8; ++j) x[i][j] = 0.0f;
 
+    // The residual and gamma vectors are loaded first, with the expert rows:
+    // loaded where they are used, each cost one more round trip after the
+    // rows (the loads wait in issue order).
+    u32x4 rv[NV], gv[NV];
+#pragma unroll
+    for (int i = 0; i < NV; ++i) {
+        const int v = min(i * tpr + tid, nvec - 1);
+        rv[i] = __builtin_nontemporal_load(residual + (size_t)t * nvec + v);
+        gv[i] = gamma[v];
+    }
+
     if constexpr (KT > 0) {
         int pos[KT];
         float sc[KT];
@@ -122,24 +133,14 @@ __global__ __launch_bounds__(kNormThreads) void combine_norm_rows(
 
     // x = a + residual; sum of squares over this thread's real vectors
     float ss = 0.0f;
-    {
-        u32x4 rv[NV];
 #pragma unroll
-        for (int i = 0; i < NV; ++i)
-            rv[i] = __builtin_nontemporal_load(residual + (size_t)t * nvec +
-                                               min(i * tpr + tid, nvec - 1));
+    for (int i = 0; i < NV; ++i) {
+        load_add(x[i], rv[i]);
+        if (i * tpr + tid < nvec) {
 #pragma unroll
-        for (int i = 0; i < NV; ++i) {
-            load_add(x[i], rv[i]);
-            if (i * tpr + tid < nvec) {
-#pragma unroll
-                for (int j = 0; j < 8; ++j) ss = ss + x[i][j] * x[i][j];
-            }
+            for (int j = 0; j < 8; ++j) ss = ss + x[i][j] * x[i][j];
         }
     }
-    u32x4 gv[NV];
-#pragma unroll
-    for (int i = 0; i < NV; ++i) gv[i] = gamma[min(i * tpr + tid, nvec - 1)];
 
     ss = wave_sum(ss);
     const int wpr = tpr / kWave;  // waves per row: each wave lies in one row
