@@ -196,25 +196,14 @@ __device__ __forceinline__ int clampi(int v, int lo, int hi) {
     return v < lo ? lo : (v > hi ? hi : v);
 }
 
-// bf16 bit pattern -> fp32 (exact).
-__device__ __forceinline__ float bf16_bits_to_float(uint32_t b) {
-    return __uint_as_float(b << 16);
-}
-
-// fp32 -> bf16 bits, round to nearest, ties to even; NaN stays a quiet NaN
-// with its sign and top payload bits ((bits >> 16) | 0x40).
-__device__ __forceinline__ uint32_t float_to_bf16_bits(float f) {
-    const uint32_t u = __float_as_uint(f);
-    if ((u & 0x7fffffffu) > 0x7f800000u) return (u >> 16) | 0x0040u;
-    return (u + 0x7fffu + ((u >> 16) & 1u)) >> 16;
-}
-
 typedef __bf16 bf16x2_t __attribute__((ext_vector_type(2)));
 typedef float f32x2_t __attribute__((ext_vector_type(2)));
 
 // Two fp32 -> one word of two bf16 (lo in the low half) with gfx950's
-// v_cvt_pk_bf16_f32. Checked on the MI355X against float_to_bf16_bits over
-// all 2^32 inputs, NaNs included: bit-identical.
+// v_cvt_pk_bf16_f32: round to nearest, ties to even. Checked on the MI355X
+// over all 2^32 inputs against the integer rounding (u + 0x7fff + lsb) >> 16,
+// with a NaN kept quiet with its sign and top payload bits
+// ((u >> 16) | 0x40): bit-identical.
 __device__ __forceinline__ uint32_t bf16x2_bits(float lo, float hi) {
     const f32x2_t v = {lo, hi};
     return __builtin_bit_cast(uint32_t, __builtin_convertvector(v, bf16x2_t));
