@@ -81,12 +81,12 @@ __device__ __forceinline__ int wave_inclusive_sum(int x) {
 }
 
 // Exclusive block-wide sum. `scratch` holds at least blockDim/64 + 1 ints of
-// LDS. Every thread of the block must call it (it uses lds_barrier). Returns the exclusive prefix;
-// *total receives the block sum. CLOSE = false leaves out the closing
-// barrier that lets the next call reuse `scratch`: the caller then
-// alternates two scratch buffers between consecutive calls (a call's two
-// barriers keep the buffer of the call before it from being rewritten
-// while it is still read).
+// LDS. Every thread of the block must call it (it uses lds_barrier). Returns
+// the exclusive prefix; *total receives the block sum. CLOSE = false leaves
+// out the closing barrier that lets the next call reuse `scratch`: the
+// caller then alternates two scratch buffers between consecutive calls (a
+// call's two barriers keep the buffer of the call before it from being
+// rewritten while it is still read).
 template <bool CLOSE = true>
 __device__ __forceinline__ int block_exclusive_sum(int v, int* scratch, int* total) {
     const int lane = threadIdx.x & (kWave - 1);
