@@ -72,6 +72,11 @@ def test_workspace_size(B):
     assert B.mep_plan_workspace_size(8, 2000, 4096, 8) == 0   # E > 1024
     assert B.mep_plan_workspace_size(8, 4, 16, 8) == 0       # K > E
     assert B.mep_plan_workspace_size(2048, 256, 16, 8) == 0  # R > 1024
+    # every rank count up to the limit has a chunking (one chunk per source
+    # at least), from tiny to large route counts
+    for R in (1, 511, 512, 513, 1024):
+        for S, K in ((1, 1), (3, 2), (8192, 8)):
+            assert B.mep_plan_workspace_size(R, 256, S, K) > 0 or R * S * K > (1 << 30)
     assert B.mep_plan_workspace_size(1024, 1024, 1 << 17, 16) == 0  # N > 2^30
 
 
