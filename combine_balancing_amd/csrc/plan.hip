@@ -264,9 +264,14 @@ __device__ __forceinline__ void inst_of(const GlobalLds& g, int u, int i, int* e
 }
 
 // Routes of expert e from source ranks below `src` (src == R: all of them).
+// Both reads are made and one is kept: selecting the pointer instead (LDS
+// counts or global chunk prefixes) compiled to a generic load, which waits
+// on the LDS counter too.
 __device__ __forceinline__ int pre_of(const PlanDims& d, const int* chunk, const int* cnt, int src,
                                       int e) {
-    return src >= d.R ? cnt[e] : chunk[(src * d.cps) * d.E + e];
+    const int from_chunks = chunk[(min(src, d.R - 1) * d.cps) * d.E + e];
+    const int total = cnt[e];
+    return src >= d.R ? total : from_chunks;
 }
 
 // Exclusive sum when only the first wave holds values (R <= 64 for the
