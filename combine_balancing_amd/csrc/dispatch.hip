@@ -33,13 +33,13 @@ using namespace rows;
 // send_buf[send_pos[t*K+k]] = x[t] for each k with 0 <= send_pos < nrows.
 // One thread per (token, vector): the token's row is read once and stored to
 // each of its K send rows, one store in flight at a time (each waits for the
-// previous one). The K send rows of a token lie in up to K far-apart
-// segments, so the grid writes many streams at once, and fewer outstanding
-// stores measured faster on MI355X (dsv3 shape: 8 back-to-back stores
-// 113 us, one at a time 104 us). Capping residency at two work-groups per
-// CU gained 4 us more at full K but lost 10 us when a third of the
-// positions are skipped (dedup maps) and 40 us in the peer-write variant,
-// so the launch keeps full residency.
+// previous one): fewer outstanding stores measured faster on MI355X (dsv3
+// shape: 8 back-to-back stores 113 us, one at a time 104 us). Neither
+// scalar position loads nor prefetching a next item per thread gained
+// anything. Capping residency at two work-groups per CU gained 4 us more
+// at full K but lost 10 us when a third of the positions are skipped (dedup
+// maps) and 40 us in the peer-write variant, so the launch keeps full
+// residency.
 template <int KT>
 __global__ __launch_bounds__(kFlatThreads) void pack_flat(const u32x4* __restrict__ x,
                                                           const int* __restrict__ send_pos,
