@@ -28,20 +28,30 @@ __device__ __forceinline__ int count_below(uint64_t mask) {
 // on every lane and leave the groups unchanged). Call with the whole wave.
 constexpr int kKeyBits = 10;  // keys below 1024: experts and instances
 
+// gfx950's three-input bitwise op, truth table indexed by
+// (bit of a) * 4 + (bit of b) * 2 + (bit of c): 0x90 is a & ~(b ^ c).
+constexpr int kAndXnor = 0x90;
+
 template <int NBITS = kKeyBits>
 __device__ __forceinline__ uint64_t match_peers(int key, bool valid) {
     // Invalid lanes are dropped by the first ballot; the per-bit ballots need
     // not exclude them again.
     // Per bit: lb = 0 or ~0 (the lane's bit, sign-extended), m = ballot of
-    // the bit; lanes agreeing with this lane on the bit are ~(m ^ lb).
+    // the bit; lanes agreeing with this lane on the bit are ~(m ^ lb). Each
+    // half of the mask takes that in one v_bitop3, so a bit costs four
+    // vector instructions (extract, compare, two bitop3) where the plain
+    // expression compiled to about six.
     const uint64_t v = __ballot(valid);
     uint32_t lo = (uint32_t)v, hi = (uint32_t)(v >> 32);
 #pragma unroll
     for (int b = 0; b < NBITS; ++b) {
-        const int lb = (int)((uint32_t)key << (31 - b)) >> 31;
-        const uint64_t m = __ballot(lb != 0);
-        lo &= ~((uint32_t)m ^ (uint32_t)lb);
-        hi &= ~((uint32_t)(m >> 32) ^ (uint32_t)lb);
+        uint32_t lb = (uint32_t)__builtin_amdgcn_sbfe((int)key, b, 1);
+        // opaque, so the ballot compares lb itself (seen through, it is
+        // rebuilt from a shift of the key: one more instruction per bit)
+        asm("" : "+v"(lb));
+        const uint64_t m = __ballot(lb != 0u);
+        lo = __builtin_amdgcn_bitop3_b32(lo, (uint32_t)m, lb, kAndXnor);
+        hi = __builtin_amdgcn_bitop3_b32(hi, (uint32_t)(m >> 32), lb, kAndXnor);
     }
     return ((uint64_t)hi << 32) | lo;
 }

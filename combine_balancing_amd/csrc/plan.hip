@@ -55,8 +55,8 @@ namespace {
 constexpr int kHistThreads = 256;
 constexpr int kMaxChunks = 1024;  // column length of the expert scan (>= the rank limit)
 constexpr int kTargetChunks = MEP_PLAN_TARGET_CHUNKS;
-constexpr int kBuckets = 1024;
-constexpr size_t kMaxLds = 160 * 1024;  // LDS a gfx950 work-group may allocate  // piece lookup: excess index >> shift -> first piece
+constexpr int kBuckets = 1024;  // piece lookup: excess index >> shift -> first piece
+constexpr size_t kMaxLds = 160 * 1024;  // LDS a gfx950 work-group may allocate
 constexpr int kGlobalThreads = 1024;
 constexpr int kItemCache = 4;  // plan_global: per-thread items kept between two passes
 constexpr int kRouteThreads = MEP_PLAN_ROUTE_THREADS;  // work-group of plan_routes
@@ -763,11 +763,18 @@ __global__ __launch_bounds__(kRouteThreads) void plan_routes(PlanDims d, PlanWs 
         }
         valid = valid && (unsigned)e < (unsigned)E;
         if (!valid) e = 0;
-        const uint64_t peers = match_peers<KEY_BITS>(e, valid);
-        const int rin = my_cnt[e] + count_below(peers);
-        if (valid && is_group_leader(peers)) my_cnt[e] += __popcll(peers);
+        // the expert's records are read with its count, in one LDS round
+        // trip (read after the count's update they would wait for it)
         const int4 x0 = s_ex0[e];
         const int4 x1 = s_ex1[e];
+        const uint64_t peers = match_peers<KEY_BITS>(e, valid);
+        const int cnt = my_cnt[e];
+        int rin = cnt + count_below(peers);
+        // rin is formed before the leader's branch: formed after it, the
+        // merge of the two paths made the compiler wait for the count's
+        // update to complete as well
+        asm volatile("" : "+v"(rin));
+        if (valid && is_group_leader(peers)) my_cnt[e] = cnt + __popcll(peers);
         int dest = -1, slot = -1;
         if (valid) {
             const int q = x0.x + rin;
@@ -781,8 +788,15 @@ __global__ __launch_bounds__(kRouteThreads) void plan_routes(PlanDims d, PlanWs 
                 const int jx = x1.x + rin;
                 const int bi = jx >> shift;
                 int pi = s_bkt[bi < 0 ? 0 : min(bi, kBuckets - 1)];
-                while (pi + 1 < NP && s_ps[pi + 1] <= jx) ++pi;
-                const int4 pr = s_prec[pi];
+                // the bucket's first piece and the next piece's start come
+                // in one round trip; a later piece needs further steps
+                int4 pr = s_prec[pi];
+                const int next_start = s_ps[min(pi + 1, PM - 1)];
+                if (pi + 1 < NP && next_start <= jx) {
+                    do ++pi;
+                    while (pi + 1 < NP && s_ps[pi + 1] <= jx);
+                    pr = s_prec[pi];
+                }
                 if ((unsigned)pr.x < (unsigned)R && pi < NP) {
                     dest = pr.x;
                     slot = pr.y + jx;
