@@ -56,13 +56,6 @@ __device__ __forceinline__ uint64_t match_peers(int key, bool valid) {
     return ((uint64_t)hi << 32) | lo;
 }
 
-// True on the highest lane of its peer group.
-__device__ __forceinline__ bool is_group_leader(uint64_t peers) {
-    const int lane = lane_id();
-    const uint64_t above = lane == 63 ? 0ull : (~0ull << (lane + 1));
-    return (peers & above) == 0;
-}
-
 // Work-group barrier for LDS data: waits for this wave's LDS (and scalar)
 // operations, then meets the other waves. Unlike __syncthreads() it does not
 // wait for outstanding global stores, so a phase that writes outputs does

@@ -609,6 +609,13 @@ __global__ __launch_bounds__(kGlobalThreads) void plan_global(PlanDims d, PlanWs
 }
 
 // -------------------------------------------------------------- plan_routes
+// Element i of a route-sized array through a 32-bit byte offset: route
+// indices stay below 2^30, so 4*i fits, and the store can take its base
+// from scalar registers with no 64-bit address arithmetic per lane.
+__device__ __forceinline__ int& at32(int* base, int i) {
+    return *(int*)((char*)base + (uint32_t)i * 4u);
+}
+
 // LDS per work-group: per-wave counters, two packed per-expert tables, the
 // receive bases of this source, piece starts and records, the bucket table
 // and (for chunks up to kStageIds routes) the chunk's ids.
@@ -768,13 +775,15 @@ __global__ __launch_bounds__(kRouteThreads) void plan_routes(PlanDims d, PlanWs 
         const int4 x0 = s_ex0[e];
         const int4 x1 = s_ex1[e];
         const uint64_t peers = match_peers<KEY_BITS>(e, valid);
+        const int below = count_below(peers);
         const int cnt = my_cnt[e];
-        int rin = cnt + count_below(peers);
-        // rin is formed before the leader's branch: formed after it, the
-        // merge of the two paths made the compiler wait for the count's
-        // update to complete as well
+        int rin = cnt + below;
+        // rin is formed before the branch below: formed after it, the merge
+        // of the two paths made the compiler wait for the count's update to
+        // complete as well
         asm volatile("" : "+v"(rin));
-        if (valid && is_group_leader(peers)) my_cnt[e] = cnt + __popcll(peers);
+        // the group's lowest lane moves the count past the whole group
+        if (valid && below == 0) my_cnt[e] = cnt + __popcll(peers);
         int dest = -1, slot = -1;
         if (valid) {
             const int q = x0.x + rin;
@@ -782,8 +791,8 @@ __global__ __launch_bounds__(kRouteThreads) void plan_routes(PlanDims d, PlanWs 
             if (q < C) {
                 dest = x0.w;
                 slot = q;
-                if (src == m) o.send_pos[f - m * C] = x0.z + qs;
-                if (dest == m && (unsigned)slot < (unsigned)C) o.recv_pos[slot] = x1.y + qs;
+                if (src == m) at32(o.send_pos, f - m * C) = x0.z + qs;
+                if (dest == m && (unsigned)slot < (unsigned)C) at32(o.recv_pos, slot) = x1.y + qs;
             } else {
                 const int jx = x1.x + rin;
                 const int bi = jx >> shift;
@@ -800,16 +809,16 @@ __global__ __launch_bounds__(kRouteThreads) void plan_routes(PlanDims d, PlanWs 
                 if ((unsigned)pr.x < (unsigned)R && pi < NP) {
                     dest = pr.x;
                     slot = pr.y + jx;
-                    if (src == m) o.send_pos[f - m * C] = pr.z + qs;
+                    if (src == m) at32(o.send_pos, f - m * C) = pr.z + qs;
                     const int i = nat_m + pi - fp_m;
                     if (dest == m && (unsigned)slot < (unsigned)C && (unsigned)i < (unsigned)E)
-                        o.recv_pos[slot] = s_ex1[i].w + qs;
+                        at32(o.recv_pos, slot) = s_ex1[i].w + qs;
                 }
             }
         }
         if (j < b && o.route_dest) {
-            o.route_dest[f] = dest;
-            o.route_slot[f] = slot;
+            at32(o.route_dest, f) = dest;
+            at32(o.route_slot, f) = slot;
         }
     }
 }

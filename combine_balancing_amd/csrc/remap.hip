@@ -211,8 +211,9 @@ __global__ __launch_bounds__(kRemapThreads) void remap_prune_kernel(RemapArgs a)
         valid = valid && s_keep[i] && (unsigned)inst < (unsigned)n_inst;
         if (!valid) inst = 0;
         const uint64_t peers = match_peers(inst, valid);
-        const int r = my_cnt[inst] + count_below(peers);
-        if (valid && is_group_leader(peers)) my_cnt[inst] += __popcll(peers);
+        const int below = count_below(peers);
+        const int r = my_cnt[inst] + below;
+        if (valid && below == 0) my_cnt[inst] += __popcll(peers);  // the group's lowest lane
         if (i < hi) a.send_pos[i] = valid ? r : -1;
     }
 }
