@@ -197,3 +197,25 @@ def test_rejects_bad_arguments(orc):
         orc.plan(ids, 2, 4, 2, 2, m=2)   # m out of range
     with pytest.raises(orc.OracleError):
         orc.plan(ids + 9, 2, 4, 2, 2)    # id out of range
+
+
+def test_scale_checks_accept_oracle_and_catch_a_swap(orc):
+    # the checks the maximum-size GPU plan test relies on (the plan rule in
+    # vectorised form for every route, the send/arrival permutations), run
+    # here on the oracle's plan of the same skewed routing at a small size;
+    # a planted swap of two routes' slots must fail them
+    import torch
+    from test_gpu_plan_max import check_plan_at_scale, skewed_ids
+    R, E, S, K, m = 8, 256, 2048, 8, 5
+    ids = skewed_ids(R, S, seed=11)
+    p = orc.plan(ids.astype(np.int32), R, E, S, K, m=m)
+    tp = {k: torch.from_numpy(np.ascontiguousarray(v)) for k, v in p.items()}
+    tids = torch.from_numpy(ids.astype(np.int32))
+    L = check_plan_at_scale(tids, R, E, S, K, m, tp)
+    assert int(L.max()) > S * K
+    bad = {k: v.clone() for k, v in tp.items()}
+    f = torch.nonzero(bad["route_dest"].reshape(-1) == m).reshape(-1)[:2]
+    sl = bad["route_slot"].reshape(-1)
+    sl[f[0]], sl[f[1]] = sl[f[1]].clone(), sl[f[0]].clone()
+    with pytest.raises(AssertionError):
+        check_plan_at_scale(tids, R, E, S, K, m, bad)
