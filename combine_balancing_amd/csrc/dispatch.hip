@@ -17,9 +17,9 @@
 // work-group -> XCD assignment does not matter here.
 //
 // Launch shapes (measured on MI355X at H=7168): pack and combine are flat,
-// one thread per (token, vector) in 256-thread work-groups; the grouping
-// copy runs one work-group per row, which reaches the read+write copy
-// ceiling.
+// one thread per (token, vector), pack in 256-thread work-groups and combine
+// in 128-thread ones; the grouping copy runs one work-group per row, which
+// reaches the read+write copy ceiling.
 #include <algorithm>
 
 #include "rows.h"
@@ -110,13 +110,13 @@ __global__ __launch_bounds__(kMaxTpr) void group_rows(const u32x4* __restrict__ 
 // with its K loads in flight together; skipped routes load row 0 and are
 // left out exactly.
 template <int KT>
-__global__ __launch_bounds__(kFlatThreads) void combine_flat(const u32x4* __restrict__ y, int n_y,
+__global__ __launch_bounds__(kCombineThreads) void combine_flat(const u32x4* __restrict__ y, int n_y,
                                                              const int* __restrict__ send_pos,
                                                              const float* __restrict__ scores,
                                                              u32x4* __restrict__ out_bf16,
                                                              f32x4* __restrict__ out_f32,
                                                              uint32_t total, FastDiv rowdiv) {
-    const uint32_t i = blockIdx.x * kFlatThreads + threadIdx.x;
+    const uint32_t i = blockIdx.x * kCombineThreads + threadIdx.x;
     if (i >= total) return;
     const uint32_t t = fast_div(i, rowdiv);
     const uint32_t v = i - t * rowdiv.d;
@@ -142,11 +142,11 @@ __global__ __launch_bounds__(kFlatThreads) void combine_flat(const u32x4* __rest
 
 // Any K up to 64 (and the case with no rows to read): one route at a time,
 // in k order, loading only valid routes.
-__global__ __launch_bounds__(kFlatThreads) void combine_flat_any(
+__global__ __launch_bounds__(kCombineThreads) void combine_flat_any(
     const u32x4* __restrict__ y, int n_y, const int* __restrict__ send_pos,
     const float* __restrict__ scores, u32x4* __restrict__ out_bf16, f32x4* __restrict__ out_f32,
     uint32_t total, int K, FastDiv rowdiv) {
-    const uint32_t i = blockIdx.x * kFlatThreads + threadIdx.x;
+    const uint32_t i = blockIdx.x * kCombineThreads + threadIdx.x;
     if (i >= total) return;
     const uint32_t t = fast_div(i, rowdiv);
     const uint32_t v = i - t * rowdiv.d;
@@ -180,8 +180,8 @@ void launch_group(hipStream_t s, const u32x4* raw, const int* rp, u32x4* out, in
 template <int KT>
 void launch_combine(hipStream_t s, const u32x4* y, int n_y, const int* sp, const float* sc,
                     u32x4* ob, f32x4* of, uint32_t total, FastDiv dv) {
-    hipLaunchKernelGGL(combine_flat<KT>, dim3((total + kFlatThreads - 1) / kFlatThreads),
-                       dim3(kFlatThreads), 0, s, y, n_y, sp, sc, ob, of, total, dv);
+    hipLaunchKernelGGL(combine_flat<KT>, dim3((total + kCombineThreads - 1) / kCombineThreads),
+                       dim3(kCombineThreads), 0, s, y, n_y, sp, sc, ob, of, total, dv);
 }
 
 }  // namespace
@@ -270,8 +270,8 @@ extern "C" int mep_combine(int T, int K, int H, const uint16_t* y_ret, int n_y,
         case 15: launch_combine<15>(s, y, n_y, sp, scores, ob, of, total, dv); break;
         case 16: launch_combine<16>(s, y, n_y, sp, scores, ob, of, total, dv); break;
         default:
-            hipLaunchKernelGGL(combine_flat_any, dim3((total + kFlatThreads - 1) / kFlatThreads),
-                               dim3(kFlatThreads), 0, s, y, n_y, sp, scores, ob, of, total, K, dv);
+            hipLaunchKernelGGL(combine_flat_any, dim3((total + kCombineThreads - 1) / kCombineThreads),
+                               dim3(kCombineThreads), 0, s, y, n_y, sp, scores, ob, of, total, K, dv);
             break;
     }
     MEP_LAUNCH_CHECK();

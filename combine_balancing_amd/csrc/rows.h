@@ -49,6 +49,11 @@ inline bool aligned16(const void* p) { return ((uintptr_t)p & 15u) == 0; }
 // 896-thread row groups stay near 4.7 TB/s).
 constexpr int kFlatThreads = 256;
 
+// The flat combine (K row loads, one store per thread) runs 128-thread
+// work-groups: 90.3 us against 92.6 us at 256 on the dsv3 shape (64: 90.4-91,
+// 512 and 1024: 91-92.5). Pack measured no better below 256 and slower above.
+constexpr int kCombineThreads = 128;
+
 // s_waitcnt operand that waits for every outstanding vector memory operation
 // (vmcnt(0)) and leaves the export and LDS/scalar counters alone (gfx9
 // encoding: vmcnt in bits [3:0] and [15:14], expcnt [6:4], lgkmcnt [11:8]).
