@@ -159,10 +159,12 @@ def test_zero_copy_headline_shape(orc):
     assert np.all(np.abs(host(of)[tok].astype(np.float64) - rf64) <= 1e-6 * mag)
 
 
-@pytest.mark.parametrize("T,K,H,R,C", [(3, 2, 65536, 2, 4), (5, 3, 72, 3, 6), (1, 1, 8, 1, 1)])
+@pytest.mark.parametrize("T,K,H,R,C", [(3, 2, 65536, 2, 4), (5, 3, 72, 3, 6), (1, 1, 8, 1, 1),
+                                       (300, 8, 64, 1024, 4), (50, 20, 136, 1000, 3)])
 def test_zero_copy_and_ungroup_edges(orc, T, K, H, R, C):
-    # the largest row, ragged vector tails, one rank and one slot; routes
-    # outside [0,R) x [0,C) are skipped
+    # the largest row, ragged vector tails, one rank and one slot, the
+    # largest peer table (1024 ranks, staged whole in LDS by the pull) and a
+    # generic-K one; routes outside [0,R) x [0,C) are skipped
     torch = require_gpu()
     import combine_balancing_amd as cba
     rng = np.random.default_rng(T * 7 + H)
