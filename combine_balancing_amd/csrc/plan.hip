@@ -616,6 +616,32 @@ __device__ __forceinline__ int& at32(int* base, int i) {
     return *(int*)((char*)base + (uint32_t)i * 4u);
 }
 
+// plan_routes stages its tables through registers: every load is issued
+// first, at clamped indices and with no branches, and the LDS writes follow
+// once all of them are in flight. Staged table by table, each table's
+// writes waited for its loads before the next table's loads went out: five
+// global round trips in the prologue where one suffices.
+constexpr int kPmRegs = (kMaxE + kMaxR + 1 + kRouteThreads - 1) / kRouteThreads;
+constexpr int kBktRegs = (kBuckets + kRouteThreads - 1) / kRouteThreads;
+constexpr int kIdRegs = (kStageIds + kRouteThreads - 1) / kRouteThreads;
+
+// v[u] = src[min(u * kRouteThreads + tid, n - 1)]; needs 1 <= n.
+template <int U, typename T>
+__device__ __forceinline__ void regs_load(T (&v)[U], const T* __restrict__ src, int n) {
+#pragma unroll
+    for (int u = 0; u < U; ++u) v[u] = src[min(u * kRouteThreads + (int)threadIdx.x, n - 1)];
+}
+
+// dst[i] = v[u] for i = u * kRouteThreads + tid < n.
+template <int U, typename T>
+__device__ __forceinline__ void regs_store(T* dst, const T (&v)[U], int n) {
+#pragma unroll
+    for (int u = 0; u < U; ++u) {
+        const int i = u * kRouteThreads + (int)threadIdx.x;
+        if (i < n) dst[i] = v[u];
+    }
+}
+
 // LDS per work-group: per-wave counters, two packed per-expert tables, the
 // receive bases of this source, piece starts and records, the bucket table
 // and (for chunks up to kStageIds routes) the chunk's ids.
@@ -652,7 +678,23 @@ __global__ __launch_bounds__(kRouteThreads) void plan_routes(PlanDims d, PlanWs 
     const int src = c / d.cps, sub = c - src * d.cps;
     const int f0 = src * C + sub * d.T;
     const int f1 = min(f0 + d.T, (src + 1) * C);
-    const int len = f1 - f0;
+    const int len = f1 - f0;  // >= 1: a source's last chunk holds the rest of its C routes
+
+    // the staged tables' loads go out first (their LDS writes follow below)
+    int ps_r[kPmRegs], bk_r[kBktRegs], id_r[STAGED ? kIdRegs : 1];
+    i32x4 pr_r[kPmRegs];
+    regs_load(ps_r, w.pstart, PM);
+    regs_load(pr_r, (const i32x4*)w.prec, PM);
+    regs_load(bk_r, w.bucket, kBuckets);
+    if constexpr (STAGED) regs_load(id_r, ids + f0, len);
+    // this block's share of the instance tables (filled after the barrier):
+    // its first rank record joins this round trip
+    const int E1 = E + 1;
+    const int per = (R * E1 + gridDim.x - 1) / gridDim.x;
+    const int lo = min(blockIdx.x * per, R * E1), hi = min(lo + per, R * E1);
+    const int step_u = kRouteThreads / E1, step_i = kRouteThreads - step_u * E1;
+    const int u0 = (lo + tid) / E1, i0 = (lo + tid) - u0 * E1;
+    const int4 ri0 = lo + tid < hi ? w.rinfo[u0] : make_int4(0, 0, 0, 0);
 
     // one round trip: every table this block reads, and its routes.
     // For a route of expert e at rank rin among the chunk's routes of e:
@@ -675,19 +717,11 @@ __global__ __launch_bounds__(kRouteThreads) void plan_routes(PlanDims d, PlanWs 
         s_ex0[e] = make_int4(qbase, off - pre, w.nsend[e], h);
         s_ex1[e] = make_int4(w.uex[h] + qbase - C, nrcv, min(eex - rbh, C), rcv);
     }
-    // this block's share of the instance tables (filled after the barrier):
-    // its first rank record joins this round trip
-    const int E1 = E + 1;
-    const int per = (R * E1 + gridDim.x - 1) / gridDim.x;
-    const int lo = min(blockIdx.x * per, R * E1), hi = min(lo + per, R * E1);
-    const int step_u = kRouteThreads / E1, step_i = kRouteThreads - step_u * E1;
-    const int u0 = (lo + tid) / E1, i0 = (lo + tid) - u0 * E1;
-    const int4 ri0 = lo + tid < hi ? w.rinfo[u0] : make_int4(0, 0, 0, 0);
     for (int i = tid; i < kRouteWaves * E; i += kRouteThreads) s_cnt[i] = 0;
-    stage<kRouteThreads, 2>(s_ps, w.pstart, PM);
-    stage<kRouteThreads, 2>((i32x4*)s_prec, (const i32x4*)w.prec, PM);
-    stage<kRouteThreads, 1>(s_bkt, w.bucket, kBuckets);
-    if (STAGED) stage<kRouteThreads, kStageIds / kRouteThreads>(s_ids, ids + f0, len);
+    regs_store(s_ps, ps_r, PM);
+    regs_store((i32x4*)s_prec, pr_r, PM);
+    regs_store(s_bkt, bk_r, kBuckets);
+    if constexpr (STAGED) regs_store(s_ids, id_r, len);
     lds_barrier();
 
     // this block's slice of the instance tables inst_cu [R][E+1] and
