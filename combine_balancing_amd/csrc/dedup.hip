@@ -41,6 +41,7 @@ constexpr int kDedupMaxR = 64;
 
 struct DedupDims {
     int R, S, K, m, cps, nchunks;
+    int vec;  // K % 4 == 0 and both route maps 16-byte aligned: read them as vectors
 };
 
 struct DedupWs {
@@ -51,13 +52,14 @@ struct DedupWs {
 };
 
 // Calls f(k, d) for each route k of global token g with destination d. A
-// token's K destinations are contiguous: with K % 4 == 0 they are read as
-// 16-byte vectors (a lane's routes in K/4 loads, not K), else 8 scalar loads
-// at a time; either way the loads of a batch are in flight together.
+// token's K destinations are contiguous: with vec (K % 4 == 0, aligned maps)
+// they are read as 16-byte vectors (a lane's routes in K/4 loads, not K),
+// else 8 scalar loads at a time; either way the loads of a batch are in
+// flight together.
 template <typename F>
 __device__ __forceinline__ void for_routes(const int* __restrict__ route_dest, size_t g, int K,
-                                           F f) {
-    if ((K & 3) == 0) {
+                                           int vec, F f) {
+    if (vec) {
         const i32x4* p = (const i32x4*)(route_dest + g * K);
         for (int k0 = 0; k0 < K; k0 += 16) {
             i32x4 v[4];
@@ -83,9 +85,9 @@ __device__ __forceinline__ void for_routes(const int* __restrict__ route_dest, s
 }
 
 __device__ __forceinline__ uint64_t token_mask(const int* __restrict__ route_dest, size_t g, int K,
-                                               int R) {
+                                               int vec, int R) {
     uint64_t mk = 0;
-    for_routes(route_dest, g, K, [&](int, int d) {
+    for_routes(route_dest, g, K, vec, [&](int, int d) {
         if ((unsigned)d < (unsigned)R) mk |= 1ull << d;
     });
     return mk;
@@ -101,7 +103,7 @@ __global__ __launch_bounds__(kDedupThreads) void dedup_count(DedupDims dd, Dedup
     const int t = sub * kDedupChunk + threadIdx.x;
     const bool valid = t < dd.S;
     const size_t g = (size_t)src * dd.S + (valid ? t : 0);
-    const uint64_t mk = valid ? token_mask(route_dest, g, dd.K, dd.R) : 0ull;
+    const uint64_t mk = valid ? token_mask(route_dest, g, dd.K, dd.vec, dd.R) : 0ull;
     const int wave = threadIdx.x / kWave;
     for (int d = 0; d < dd.R; ++d) {
         const uint64_t b = ballot64((mk >> d) & 1ull);
@@ -125,8 +127,10 @@ __global__ __launch_bounds__(kDedupThreads) void dedup_scan(DedupDims dd, DedupW
     const int per = (dd.nchunks + 15) / 16;
     const int c0 = min(part * per, dd.nchunks), c1 = min(c0 + per, dd.nchunks);
     int sum = 0;
-    if (d < dd.R)
+    if (d < dd.R) {
+#pragma unroll 8
         for (int c = c0; c < c1; ++c) sum += w.cnt[(size_t)c * dd.R + d];
+    }
     // exclusive scan of the 16 part sums of this destination (16 adjacent lanes)
     int incl = sum;
 #pragma unroll
@@ -167,6 +171,7 @@ __global__ __launch_bounds__(kDedupThreads) void dedup_scan(DedupDims dd, DedupW
     // tokens of each source reaching m
     for (int src = threadIdx.x; src < dd.R; src += kDedupThreads) {
         int n = 0;
+#pragma unroll 8
         for (int c = src * dd.cps; c < (src + 1) * dd.cps; ++c) n += w.cnt[(size_t)c * dd.R + dd.m];
         drecv_count[src] = n;
     }
@@ -194,7 +199,7 @@ __global__ __launch_bounds__(kDedupThreads) void dedup_maps(DedupDims dd, DedupW
     for (int k = 0; k < kRegRoutes; ++k) rd[k] = -1;
     uint64_t mk = 0;
     if (valid)
-        for_routes(route_dest, g, dd.K, [&](int k, int d) {
+        for_routes(route_dest, g, dd.K, dd.vec, [&](int k, int d) {
             if (k < kRegRoutes) rd[k] = d;
             if ((unsigned)d < (unsigned)dd.R) mk |= 1ull << d;
         });
@@ -225,8 +230,29 @@ __global__ __launch_bounds__(kDedupThreads) void dedup_maps(DedupDims dd, DedupW
     if (src != dd.m && !reaches_m) return;
     const int row_m = reaches_m ? q_of(dd.m) : 0;
     const int C = dd.S * dd.K;
+    // the token's slots, loaded together before any map is written: loaded
+    // in the route loop below, each route to m cost a round trip
+    int sl_r[kRegRoutes];
+#pragma unroll
+    for (int k = 0; k < kRegRoutes; ++k) sl_r[k] = -1;
+    if (reaches_m) {
+        if (dd.vec) {
+            const i32x4* p = (const i32x4*)(route_slot + g * dd.K);
+#pragma unroll
+            for (int j = 0; j < kRegRoutes / 4; ++j)
+                if (4 * j < dd.K) {
+                    const i32x4 v = p[j];
+#pragma unroll
+                    for (int i = 0; i < 4; ++i) sl_r[4 * j + i] = v[i];
+                }
+        } else {
+#pragma unroll
+            for (int k = 0; k < kRegRoutes; ++k)
+                if (k < dd.K) sl_r[k] = route_slot[g * dd.K + k];
+        }
+    }
     uint64_t seen = 0;
-    auto visit = [&](int k, int d) {
+    auto visit = [&](int k, int d, int sl) {
         if (src == dd.m) {
             int p = -1;
             if ((unsigned)d < (unsigned)dd.R && !((seen >> d) & 1ull)) {
@@ -235,15 +261,15 @@ __global__ __launch_bounds__(kDedupThreads) void dedup_maps(DedupDims dd, DedupW
             }
             dpack_pos[(size_t)t * dd.K + k] = p;
         }
-        if (d == dd.m) {
-            const int sl = route_slot[g * dd.K + k];
-            if ((unsigned)sl < (unsigned)C) drecv_pos[sl] = row_m;
-        }
+        if (d == dd.m && (unsigned)sl < (unsigned)C) drecv_pos[sl] = row_m;
     };
 #pragma unroll
     for (int k = 0; k < kRegRoutes; ++k)
-        if (k < dd.K) visit(k, rd[k]);
-    for (int k = kRegRoutes; k < dd.K; ++k) visit(k, route_dest[g * dd.K + k]);
+        if (k < dd.K) visit(k, rd[k], sl_r[k]);
+    for (int k = kRegRoutes; k < dd.K; ++k) {
+        const int d = route_dest[g * dd.K + k];
+        visit(k, d, d == dd.m ? route_slot[g * dd.K + k] : -1);
+    }
 }
 
 bool dedup_dims(int R, int S, int K, int m, DedupDims* d) {
@@ -255,6 +281,7 @@ bool dedup_dims(int R, int S, int K, int m, DedupDims* d) {
     d->m = m;
     d->cps = (S + kDedupChunk - 1) / kDedupChunk;
     d->nchunks = R * d->cps;
+    d->vec = 0;
     return true;
 }
 
@@ -298,6 +325,7 @@ extern "C" int mep_plan_dedup(int R, int S, int K, int my_rank, const int32_t* r
     size_t oc, ob, os, oq;
     if (workspace_bytes < ws_bytes(d, &oc, &ob, &os, &oq)) return MEP_ERR_PARAM;
     if ((uintptr_t)workspace & 255u) return MEP_ERR_SHAPE;
+    d.vec = (K % 4) == 0 && ((uintptr_t)route_dest & 15u) == 0 && ((uintptr_t)route_slot & 15u) == 0;
     char* base = (char*)workspace;
     DedupWs w{(int*)(base + oc), (int*)(base + ob), (int*)(base + os), (int*)(base + oq)};
     hipStream_t s = (hipStream_t)stream;

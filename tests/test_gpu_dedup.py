@@ -49,6 +49,34 @@ def test_dedup_edge_shapes(orc, R, E, S, K):
             assert np.array_equal(host(got[k]), ref[k]), (k, m)
 
 
+def test_dedup_misaligned_route_maps(orc):
+    # K % 4 == 0 but route maps 4 bytes off a 16-byte boundary: the scalar
+    # read path must give the same maps as the vector path and the oracle
+    torch = require_gpu()
+    import combine_balancing_amd as cba
+    R, E, S, K = 8, 64, 1500, 8
+    rng = np.random.default_rng(77)
+    g = rng.gumbel(size=(R * S, E)) - 1.5 * np.log(np.arange(E) + 1.0)
+    ids = np.argsort(-g, axis=1, kind="stable")[:, :K].astype(np.int32)
+    note("dedup misaligned route maps R=8 S=1500 K=8")
+    p = cba.plan(dev(ids.reshape(-1)), R, E, S, K, my_rank=0)
+    off = {}
+    for k in ("route_dest", "route_slot"):
+        buf = torch.empty(p[k].numel() + 1, dtype=torch.int32, device="cuda")
+        buf[1:] = p[k]
+        off[k] = buf[1:]
+        assert off[k].data_ptr() % 16 != 0
+    ref_plan = orc.plan(ids, R, E, S, K, m=0)
+    for m in (0, 5):
+        got = cba.plan_dedup(off, R, S, K, m)
+        aligned = cba.plan_dedup(p, R, S, K, m)
+        torch.cuda.synchronize()
+        ref = orc.plan_dedup(ref_plan, R, S, K, m)
+        for k in KEYS:
+            assert np.array_equal(host(got[k]), ref[k]), (k, m)
+            assert np.array_equal(host(aligned[k]), ref[k]), (k, m)
+
+
 @pytest.mark.parametrize("name", ["tiny", "small"])
 def test_dedup_chain(orc, name):
     # dedup pack -> exchange -> dedup grouping equals every rank's grouped
