@@ -47,7 +47,7 @@ def lib():
     L.mep_plan.restype = I
     L.mep_remap_prune.argtypes = [I] * 8 + [P, P, P, I, P, P, P, P, P, P, P]
     L.mep_remap_prune.restype = I
-    L.mep_dispatch.argtypes = [I, I, I, P, P, P, I, P, P, P, P]
+    L.mep_dispatch.argtypes = [I, I, I, P, P, P, I, I, P, P, I, P, P]
     L.mep_dispatch.restype = I
     L.mep_combine.argtypes = [I, I, I, P, I, P, P, P, P, P]
     L.mep_combine.restype = I
@@ -111,10 +111,10 @@ def mep_remap_prune(BS, K, E, F, world_size, place_per_rank, local_rank_id,
                                  balanced_mask, send_pos, send_count, stream)
 
 
-def mep_dispatch(T, K, H, x, send_pos, send_buf, n_recv, recv_pos, recv_raw,
+def mep_dispatch(T, K, H, x, send_pos, send_buf, n_send, n_recv, recv_pos, recv_raw, n_raw,
                  recv_grouped, stream) -> int:
-    return lib().mep_dispatch(T, K, H, x, send_pos, send_buf, n_recv, recv_pos, recv_raw,
-                              recv_grouped, stream)
+    return lib().mep_dispatch(T, K, H, x, send_pos, send_buf, n_send, n_recv, recv_pos,
+                              recv_raw, n_raw, recv_grouped, stream)
 
 
 def mep_combine(T, K, H, y_ret, n_y, send_pos, scores, out_bf16, out_f32, stream) -> int:

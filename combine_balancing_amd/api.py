@@ -171,12 +171,16 @@ def dispatch(K, x=None, send_pos=None, send_buf=None, recv_raw=None, recv_pos=No
         n = recv_pos.numel() if recv_pos is not None else n_raw
         if recv_grouped is None:
             recv_grouped = torch.empty(n, H, dtype=recv_raw.dtype, device=recv_raw.device)
+    # the library bounds the pack's stores by send_buf's rows and the
+    # grouping's reads by recv_raw's rows
+    n_send = send_buf.shape[0] if x is not None else 0
+    n_raw = recv_raw.shape[0] if recv_raw is not None else 0
     rc = B.mep_dispatch(
         T, K, H, _opt(x, "x", _BF16_LIKE),
         _opt(send_pos, "send_pos", torch.int32, T * K if x is not None else None),
-        _opt(send_buf, "send_buf", _BF16_LIKE),
+        _opt(send_buf, "send_buf", _BF16_LIKE), n_send,
         n, _opt(recv_pos, "recv_pos", torch.int32, n if recv_raw is not None else None),
-        _opt(recv_raw, "recv_raw", _BF16_LIKE),
+        _opt(recv_raw, "recv_raw", _BF16_LIKE), n_raw,
         _opt(recv_grouped, "recv_grouped", _BF16_LIKE, n * H if recv_raw is not None else None),
         _stream_handle(stream))
     B.check("mep_dispatch", rc)

@@ -30,7 +30,8 @@ namespace {
 using namespace rows;
 
 // ------------------------------------------------------------------- pack
-// send_buf[send_pos[t*K+k]] = x[t] for each k with 0 <= send_pos < nrows.
+// send_buf[send_pos[t*K+k]] = x[t] for each k with 0 <= send_pos < nrows (the
+// send buffer's row count).
 // One thread per (token, vector): the token's row is read once and stored to
 // each of its K send rows, one store in flight at a time (each waits for the
 // previous one): fewer outstanding stores measured faster on MI355X (dsv3
@@ -74,19 +75,19 @@ __global__ __launch_bounds__(kFlatThreads) void pack_flat(const u32x4* __restric
 }
 
 // ------------------------------------------------------------------ group
-// recv_grouped[t] = recv_raw[recv_pos[t]] for 0 <= recv_pos[t] < n.
+// recv_grouped[t] = recv_raw[recv_pos[t]] for t < n and 0 <= recv_pos[t] < n_raw.
 // blockDim = tpr * rpb; row t = blockIdx * rpb + threadIdx / tpr.
 template <int VPT>
 __global__ __launch_bounds__(kMaxTpr) void group_rows(const u32x4* __restrict__ raw,
                                                       const int* __restrict__ recv_pos,
-                                                      u32x4* __restrict__ out, int n, int nvec,
-                                                      int tpr, int rpb) {
+                                                      u32x4* __restrict__ out, int n, int n_raw,
+                                                      int nvec, int tpr, int rpb) {
     const int r = row_in_group(tpr, rpb);
     const int tid = threadIdx.x - r * tpr;
     const int t = blockIdx.x * rpb + r;
     if (t >= n) return;
     const int from = recv_pos[t];
-    if ((unsigned)from >= (unsigned)n) return;
+    if ((unsigned)from >= (unsigned)n_raw) return;
     const u32x4* src = raw + (size_t)from * nvec;
     u32x4* dst = out + (size_t)t * nvec;
     for (int v0 = 0; v0 < nvec; v0 += tpr * VPT) {
@@ -163,17 +164,18 @@ __global__ __launch_bounds__(kCombineThreads) void combine_flat_any(
 }
 
 // ------------------------------------------------------------------- host
-void launch_group(hipStream_t s, const u32x4* raw, const int* rp, u32x4* out, int n, int nvec) {
+void launch_group(hipStream_t s, const u32x4* raw, const int* rp, u32x4* out, int n, int n_raw,
+                  int nvec) {
     // one vector per thread up to 1024 vectors (16 KiB rows), then 2, 4, 8
     int vpt = 1;
     while (vpt < 8 && nvec > kMaxTpr * vpt) vpt *= 2;
     const RowShape rs = row_shape(nvec, vpt, kMaxTpr);
     const dim3 g((n + rs.rpb - 1) / rs.rpb), b(rs.tpr * rs.rpb);
     switch (vpt) {
-        case 1: hipLaunchKernelGGL(group_rows<1>, g, b, 0, s, raw, rp, out, n, nvec, rs.tpr, rs.rpb); break;
-        case 2: hipLaunchKernelGGL(group_rows<2>, g, b, 0, s, raw, rp, out, n, nvec, rs.tpr, rs.rpb); break;
-        case 4: hipLaunchKernelGGL(group_rows<4>, g, b, 0, s, raw, rp, out, n, nvec, rs.tpr, rs.rpb); break;
-        default: hipLaunchKernelGGL(group_rows<8>, g, b, 0, s, raw, rp, out, n, nvec, rs.tpr, rs.rpb); break;
+        case 1: hipLaunchKernelGGL(group_rows<1>, g, b, 0, s, raw, rp, out, n, n_raw, nvec, rs.tpr, rs.rpb); break;
+        case 2: hipLaunchKernelGGL(group_rows<2>, g, b, 0, s, raw, rp, out, n, n_raw, nvec, rs.tpr, rs.rpb); break;
+        case 4: hipLaunchKernelGGL(group_rows<4>, g, b, 0, s, raw, rp, out, n, n_raw, nvec, rs.tpr, rs.rpb); break;
+        default: hipLaunchKernelGGL(group_rows<8>, g, b, 0, s, raw, rp, out, n, n_raw, nvec, rs.tpr, rs.rpb); break;
     }
 }
 
@@ -190,8 +192,9 @@ void launch_combine(hipStream_t s, const u32x4* y, int n_y, const int* sp, const
 using namespace mep;
 
 extern "C" int mep_dispatch(int T, int K, int H, const uint16_t* x, const int32_t* send_pos,
-                            uint16_t* send_buf, int n_recv, const int32_t* recv_pos,
-                            const uint16_t* recv_raw, uint16_t* recv_grouped, void* stream) {
+                            uint16_t* send_buf, int n_send, int n_recv, const int32_t* recv_pos,
+                            const uint16_t* recv_raw, int n_raw, uint16_t* recv_grouped,
+                            void* stream) {
     const bool do_pack = x != nullptr;
     const bool do_group = recv_raw != nullptr;
     if (!do_pack && !do_group) return (T == 0 && n_recv == 0) ? MEP_OK : MEP_ERR_PARAM;
@@ -201,12 +204,13 @@ extern "C" int mep_dispatch(int T, int K, int H, const uint16_t* x, const int32_
     if (do_pack && (T < 0 || K < 1 || K > 64 || (long long)T * K >= (1ll << 31) ||
                     !flat_fits(T, H / 8)))
         return MEP_ERR_SHAPE;
-    if (do_group && n_recv < 0) return MEP_ERR_SHAPE;
+    if (do_pack && n_send < 0) return MEP_ERR_SHAPE;
+    if (do_group && (n_recv < 0 || n_raw < 0)) return MEP_ERR_SHAPE;
     if (do_pack && (!aligned16(x) || !aligned16(send_buf))) return MEP_ERR_SHAPE;
     if (do_group && (!aligned16(recv_raw) || !aligned16(recv_grouped))) return MEP_ERR_SHAPE;
     hipStream_t s = (hipStream_t)stream;
     const int nvec = H / 8;
-    if (do_pack && T > 0) {
+    if (do_pack && T > 0 && n_send > 0) {
         const uint32_t total = (uint32_t)T * (uint32_t)nvec;
         const dim3 g((total + kFlatThreads - 1) / kFlatThreads), b(kFlatThreads);
         const FastDiv dv = make_fastdiv((uint32_t)nvec);
@@ -214,19 +218,19 @@ extern "C" int mep_dispatch(int T, int K, int H, const uint16_t* x, const int32_
         const int* sp = (const int*)send_pos;
         u32x4* buf = (u32x4*)send_buf;
         switch (K) {
-            case 1: hipLaunchKernelGGL(pack_flat<1>, g, b, 0, s, xv, sp, buf, total, K, T * K, dv); break;
-            case 2: hipLaunchKernelGGL(pack_flat<2>, g, b, 0, s, xv, sp, buf, total, K, T * K, dv); break;
-            case 4: hipLaunchKernelGGL(pack_flat<4>, g, b, 0, s, xv, sp, buf, total, K, T * K, dv); break;
-            case 6: hipLaunchKernelGGL(pack_flat<6>, g, b, 0, s, xv, sp, buf, total, K, T * K, dv); break;
-            case 8: hipLaunchKernelGGL(pack_flat<8>, g, b, 0, s, xv, sp, buf, total, K, T * K, dv); break;
-            case 16: hipLaunchKernelGGL(pack_flat<16>, g, b, 0, s, xv, sp, buf, total, K, T * K, dv); break;
-            default: hipLaunchKernelGGL(pack_flat<0>, g, b, 0, s, xv, sp, buf, total, K, T * K, dv); break;
+            case 1: hipLaunchKernelGGL(pack_flat<1>, g, b, 0, s, xv, sp, buf, total, K, n_send, dv); break;
+            case 2: hipLaunchKernelGGL(pack_flat<2>, g, b, 0, s, xv, sp, buf, total, K, n_send, dv); break;
+            case 4: hipLaunchKernelGGL(pack_flat<4>, g, b, 0, s, xv, sp, buf, total, K, n_send, dv); break;
+            case 6: hipLaunchKernelGGL(pack_flat<6>, g, b, 0, s, xv, sp, buf, total, K, n_send, dv); break;
+            case 8: hipLaunchKernelGGL(pack_flat<8>, g, b, 0, s, xv, sp, buf, total, K, n_send, dv); break;
+            case 16: hipLaunchKernelGGL(pack_flat<16>, g, b, 0, s, xv, sp, buf, total, K, n_send, dv); break;
+            default: hipLaunchKernelGGL(pack_flat<0>, g, b, 0, s, xv, sp, buf, total, K, n_send, dv); break;
         }
         MEP_LAUNCH_CHECK();
     }
-    if (do_group && n_recv > 0) {
+    if (do_group && n_recv > 0 && n_raw > 0) {
         launch_group(s, (const u32x4*)recv_raw, (const int*)recv_pos, (u32x4*)recv_grouped,
-                     n_recv, nvec);
+                     n_recv, n_raw, nvec);
         MEP_LAUNCH_CHECK();
     }
     return MEP_OK;

@@ -206,29 +206,31 @@ int mep_remap_prune(int BS, int K, int E, int F, int world_size,
  * 3.1; [MoonEP-TD]: rows land grouped by expert at the destination).
  *
  * Pack (runs when x != NULL):
- *   send_buf[send_pos[t*K+k], :] = x[t, :] for every send_pos >= 0.
- *   x [T,H] bf16; send_pos [T*K] int32 (a row index < T*K, or negative to
- *   skip the route); send_buf [n_send, H] bf16 holding every row send_pos
- *   names (n_send = T*K for the plan's map, the dedup send count for
- *   mep_plan_dedup's dpack_pos); rows not named are left untouched.
+ *   send_buf[send_pos[t*K+k], :] = x[t, :] for every 0 <= send_pos < n_send.
+ *   x [T,H] bf16; send_pos [T*K] int32 (a row index, or negative to skip
+ *   the route); send_buf [n_send, H] bf16, n_send its row count (T*K for
+ *   the plan's map, the dedup send count for mep_plan_dedup's dpack_pos);
+ *   an entry >= n_send is skipped, rows not named are left untouched.
  * Group (runs when recv_raw != NULL):
  *   recv_grouped[t, :] = recv_raw[recv_pos[t], :] for t in [0, n_recv).
- *   recv_raw [n_raw,H] bf16 in arrival (source-major) order; recv_pos
- *   [n_recv] int32; recv_grouped [n_recv,H] bf16. With the plan's own
- *   recv_pos, n_raw = n_recv; with mep_plan_dedup's drecv_pos the arrival
- *   buffer is shorter (n_raw = the dedup arrival count) and rows fan out.
- *   Entries outside [0, n_recv) skip the row; entries in range must be
- *   below n_raw (the caller's maps guarantee it).
+ *   recv_raw [n_raw,H] bf16 in arrival (source-major) order, n_raw its row
+ *   count; recv_pos [n_recv] int32; recv_grouped [n_recv,H] bf16. With the
+ *   plan's own recv_pos, n_raw = n_recv; with mep_plan_dedup's drecv_pos the
+ *   arrival buffer is shorter (n_raw = the dedup arrival count) and rows
+ *   fan out. An entry outside [0, n_raw) leaves row t untouched.
+ * The two buffer sizes bound every access, so a map paired with a buffer
+ * too short for it (say a plan map with a dedup-sized buffer) writes and
+ * reads nothing out of bounds; the rows it names past the end are skipped.
  * At least one of the two must run, unless T == 0 and n_recv == 0 (then
- * the call does nothing and may pass NULL buffers). Sizes: T >= 0, n_recv >= 0,
- * 1 <= K <= 64, 8 <= H <= 65536 with H % 8 == 0, T*K < 2^31 and
- * T*(H/8) < 2^31 (x below 32 GiB).
+ * the call does nothing and may pass NULL buffers). Sizes: T >= 0,
+ * n_send >= 0, n_recv >= 0, n_raw >= 0, 1 <= K <= 64, 8 <= H <= 65536 with
+ * H % 8 == 0, T*K < 2^31 and T*(H/8) < 2^31 (x below 32 GiB).
  * Errors: MEP_ERR_NULLPTR, MEP_ERR_PARAM (neither phase requested),
  *   MEP_ERR_SHAPE, MEP_ERR_HIP.
  */
 int mep_dispatch(int T, int K, int H,
-                 const uint16_t* x, const int32_t* send_pos, uint16_t* send_buf,
-                 int n_recv, const int32_t* recv_pos, const uint16_t* recv_raw,
+                 const uint16_t* x, const int32_t* send_pos, uint16_t* send_buf, int n_send,
+                 int n_recv, const int32_t* recv_pos, const uint16_t* recv_raw, int n_raw,
                  uint16_t* recv_grouped,
                  void* stream);
 

@@ -148,7 +148,7 @@ int main(void) {
              *d_ob = dev_alloc(2 * (size_t)S * H);
     float* d_of = dev_alloc(4 * (size_t)S * H);
     CHECK_HIP(hipMemset(d_send, 0, 2 * (size_t)C * H));
-    st = mep_dispatch(S, K, H, d_x, d_sp, d_send, C, d_rp, d_raw, d_grouped, NULL);
+    st = mep_dispatch(S, K, H, d_x, d_sp, d_send, C, C, d_rp, d_raw, C, d_grouped, NULL);
     st = st ? st : mep_combine(S, K, H, d_send, C, d_sp, d_scores, d_ob, d_of, NULL);
     if (st != MEP_OK) {
         printf("c abi: dispatch/combine returned %d (%s)\n", st, mep_status_str(st));
@@ -163,7 +163,7 @@ int main(void) {
     /* argument errors are reported, nothing is launched */
     ok &= mep_plan(R, E, S, K, R, d_ids, ws, wsb, d_ec, d_rl, d_rd, d_rs, d_ic, d_ie, d_icu,
                    d_igb, d_sp, d_sc, d_rp, d_rc, NULL) == MEP_ERR_PARAM;
-    ok &= mep_dispatch(S, K, 12, d_x, d_sp, d_send, 0, NULL, NULL, NULL, NULL) == MEP_ERR_SHAPE;
+    ok &= mep_dispatch(S, K, 12, d_x, d_sp, d_send, C, 0, NULL, NULL, 0, NULL, NULL) == MEP_ERR_SHAPE;
     ok &= mep_combine(S, K, H, NULL, C, d_sp, d_scores, d_ob, NULL, NULL) == MEP_ERR_NULLPTR;
     ok &= mep_version() > 0 && strlen(mep_status_str(MEP_ERR_SHAPE)) > 0;
 

@@ -127,14 +127,17 @@ def test_remap_validation(B):
 
 def test_dispatch_combine_validation(B):
     D = B.mep_dispatch
-    assert D(4, 2, 64, None, None, None, 0, None, None, None, None) == B.MEP_ERR_PARAM
-    assert D(0, 2, 64, None, None, None, 0, None, None, None, None) == B.MEP_OK
-    assert D(4, 2, 64, 16, None, 16, 0, None, None, None, None) == B.MEP_ERR_NULLPTR
-    assert D(4, 2, 60, 16, 16, 16, 0, None, None, None, None) == B.MEP_ERR_SHAPE   # H % 8
-    assert D(4, 2, 64, 8, 16, 16, 0, None, None, None, None) == B.MEP_ERR_SHAPE    # unaligned
-    assert D(4, 65, 64, 16, 16, 16, 0, None, None, None, None) == B.MEP_ERR_SHAPE  # K > 64
-    assert D(0, 2, 64, None, None, None, 4, 16, 16, None, None) == B.MEP_ERR_NULLPTR
-    assert D(0, 2, 64, None, None, None, -1, 16, 16, 16, None) == B.MEP_ERR_SHAPE
+    assert D(4, 2, 64, None, None, None, 8, 0, None, None, 8, None, None) == B.MEP_ERR_PARAM
+    assert D(0, 2, 64, None, None, None, 8, 0, None, None, 8, None, None) == B.MEP_OK
+    assert D(4, 2, 64, 16, None, 16, 8, 0, None, None, 8, None, None) == B.MEP_ERR_NULLPTR
+    assert D(4, 2, 60, 16, 16, 16, 8, 0, None, None, 8, None, None) == B.MEP_ERR_SHAPE   # H % 8
+    assert D(4, 2, 64, 8, 16, 16, 8, 0, None, None, 8, None, None) == B.MEP_ERR_SHAPE    # unaligned
+    assert D(4, 65, 64, 16, 16, 16, 8, 0, None, None, 8, None, None) == B.MEP_ERR_SHAPE  # K > 64
+    assert D(0, 2, 64, None, None, None, 8, 4, 16, 16, 8, None, None) == B.MEP_ERR_NULLPTR
+    assert D(0, 2, 64, None, None, None, 8, -1, 16, 16, 8, 16, None) == B.MEP_ERR_SHAPE
+    # buffer row counts: negative sizes are rejected before any launch
+    assert D(4, 2, 64, 16, 16, 16, -1, 0, None, None, 0, None, None) == B.MEP_ERR_SHAPE
+    assert D(0, 2, 64, None, None, None, 0, 4, 16, 16, -1, 16, None) == B.MEP_ERR_SHAPE
     Cb = B.mep_combine
     assert Cb(0, 2, 64, None, 0, None, None, None, None, None) == B.MEP_OK
     assert Cb(4, 2, 64, None, 8, 16, 16, 16, None, None) == B.MEP_ERR_NULLPTR
@@ -187,7 +190,7 @@ def test_combine_add_rmsnorm_validation(B):
 def test_flat_index_limit(B):
     # the flat row kernels index T*(H/8) vectors with 31 bits
     T, H = 1 << 20, 65536
-    assert B.mep_dispatch(T, 2, H, 16, 16, 16, 0, None, None, None, None) == B.MEP_ERR_SHAPE
+    assert B.mep_dispatch(T, 2, H, 16, 16, 16, 8, 0, None, None, 8, None, None) == B.MEP_ERR_SHAPE
     assert B.mep_combine(T, 2, H, 16, 4, 16, 16, 16, None, None) == B.MEP_ERR_SHAPE
     assert B.mep_dispatch_to_peers(T, 2, H, 2, 8, 16, 16, 16, 16, None) == B.MEP_ERR_SHAPE
 

@@ -30,9 +30,12 @@ def test_dedup_maps(orc, name):
 
 
 @pytest.mark.parametrize("R,E,S,K", [(2, 4, 1500, 3), (5, 9, 2047, 2), (64, 64, 40, 8),
-                                     (1, 4, 100, 2), (3, 3, 1025, 1)])
+                                     (1, 4, 100, 2), (3, 3, 1025, 1), (4, 32, 1500, 12),
+                                     (4, 32, 1500, 20)])
 def test_dedup_edge_shapes(orc, R, E, S, K):
-    # ragged 1024-token chunks, one rank, the 64-rank limit, K = 1
+    # ragged 1024-token chunks, one rank, the 64-rank limit, K = 1; K = 12
+    # (16-byte reads of a token's slots) and K = 20 (more slots than the
+    # register-held ones, the rest read one by one)
     torch = require_gpu()
     import combine_balancing_amd as cba
     rng = np.random.default_rng(R * 31 + S)
@@ -49,16 +52,16 @@ def test_dedup_edge_shapes(orc, R, E, S, K):
             assert np.array_equal(host(got[k]), ref[k]), (k, m)
 
 
-def test_dedup_misaligned_route_maps(orc):
-    # K % 4 == 0 but route maps 4 bytes off a 16-byte boundary: the scalar
-    # read path must give the same maps as the vector path and the oracle
+@pytest.mark.parametrize("R,E,S,K", [(8, 64, 1500, 8), (4, 32, 1500, 12), (4, 32, 1500, 20)])
+def test_dedup_misaligned_route_maps(orc, R, E, S, K):
+    # route maps 4 bytes off a 16-byte boundary: the scalar read path must
+    # give the same maps as the vector path (K % 4 == 0) and the oracle
     torch = require_gpu()
     import combine_balancing_amd as cba
-    R, E, S, K = 8, 64, 1500, 8
-    rng = np.random.default_rng(77)
+    rng = np.random.default_rng(77 + K)
     g = rng.gumbel(size=(R * S, E)) - 1.5 * np.log(np.arange(E) + 1.0)
     ids = np.argsort(-g, axis=1, kind="stable")[:, :K].astype(np.int32)
-    note("dedup misaligned route maps R=8 S=1500 K=8")
+    note(f"dedup misaligned route maps R={R} S={S} K={K}")
     p = cba.plan(dev(ids.reshape(-1)), R, E, S, K, my_rank=0)
     off = {}
     for k in ("route_dest", "route_slot"):
@@ -67,7 +70,7 @@ def test_dedup_misaligned_route_maps(orc):
         off[k] = buf[1:]
         assert off[k].data_ptr() % 16 != 0
     ref_plan = orc.plan(ids, R, E, S, K, m=0)
-    for m in (0, 5):
+    for m in (0, R - 1):
         got = cba.plan_dedup(off, R, S, K, m)
         aligned = cba.plan_dedup(p, R, S, K, m)
         torch.cuda.synchronize()

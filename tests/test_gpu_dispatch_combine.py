@@ -1,9 +1,11 @@
 """GPU parity of mep_dispatch (pack, grouping) and mep_combine.
 
-Pack and grouping are bit-exact against the oracle. Combine: bf16 output
-within 1 bf16 ulp and fp32 output within 1e-6 relative (to the larger of
-|reference| and the sum of |score * y| over the token's routes) of the
-oracle, which uses the same k order and rounding.
+Pack and grouping are bit-exact against the oracle. Combine computes the
+same fp32 operations in the same k order as the oracle (each product and
+each partial sum rounded on its own, from +0), so both of its outputs are
+asserted bit-exact. The stated tolerance (bf16 output within 1 bf16 ulp, fp32
+output within 1e-6 relative to the larger of |reference| and the sum of
+|score * y| over the token's routes) is checked beside it.
 """
 import numpy as np
 import pytest
@@ -37,6 +39,8 @@ def _check_combine(orc, y, sp, sc, ctx):
     rb, rf = orc.combine(y, sp, sc)
     assert np.all(bf16_ulp_diff(gb, rb) <= 1), ctx
     assert np.all(_combine_tol_ok(rf, gf, y, sp, sc)), ctx
+    assert np.array_equal(gb, rb), ctx
+    assert np.array_equal(gf.view(np.uint32), rf.view(np.uint32)), ctx
     # only the bf16 output requested
     ob2, _ = cba.combine(dev(y), dev(sp), dev(sc), out_bf16=True, out_f32=False)
     torch.cuda.synchronize()
@@ -86,9 +90,11 @@ def test_dsv3_identity_roundtrip(orc, dsv3):
     assert np.all(bf16_ulp_diff(host(ob), d["x"]) <= 1)
 
 
-def test_large_skew_sampled(orc):
-    # S=8192 rows of H=7168 for one rank of the R=64 plan, in the same launch
-    # configuration as the benchmark; outputs checked on sampled rows
+def test_large_skew_whole(orc):
+    # S=8192 rows of H=7168 for rank 0 of the R=64 plan (4,194,304 routes),
+    # in the benchmark's launch configuration. A few sampled rows are
+    # checked first (a fast first failure); then every row of the pack, the
+    # grouping and both combine outputs is compared with the oracle.
     torch = require_gpu()
     import combine_balancing_amd as cba
     d = synth.make_plan_inputs("large_skew")
@@ -99,26 +105,51 @@ def test_large_skew_sampled(orc):
     note("pack large_skew")
     sb, _ = cba.dispatch(K, x=dev(d["x"]), send_pos=dev(p["send_pos"]))
     torch.cuda.synchronize()
-    rows = rng.choice(S, 512, replace=False)
     sbh = host(sb)
-    for s in rows:
+    del sb
+    for s in rng.choice(S, 64, replace=False):
         for k in range(K):
             assert np.array_equal(sbh[p["send_pos"][s * K + k]], d["x"][s])
+    want = orc.pack(d["x"], p["send_pos"], K)
+    assert np.array_equal(sbh, want)
+    del sbh, want
     note("group large_skew")
     _, rg = cba.dispatch(K, recv_raw=dev(d["recv_raw"]), recv_pos=dev(p["recv_pos"]))
     torch.cuda.synchronize()
-    t = rng.choice(C, 4096, replace=False)
-    assert np.array_equal(host(rg)[t], orc.group(d["recv_raw"], p["recv_pos"][t]))
-    note("combine large_skew")
-    ob, of = cba.combine(dev(d["y_ret"]), dev(p["send_pos"]), dev(d["scores"][0]),
-                         out_bf16=True, out_f32=True)
-    torch.cuda.synchronize()
-    tok = np.sort(rng.choice(S, 256, replace=False))
-    sp_s = p["send_pos"].reshape(S, K)[tok].reshape(-1)
-    sc_s = d["scores"][0][tok]
-    rb, rf = orc.combine(d["y_ret"], sp_s, sc_s)
-    assert np.all(bf16_ulp_diff(host(ob)[tok], rb) <= 1)
-    assert np.all(_combine_tol_ok(rf, host(of)[tok], d["y_ret"], sp_s, sc_s))
+    rgh = host(rg)
+    del rg
+    assert np.array_equal(rgh, orc.group(d["recv_raw"], p["recv_pos"]))
+    del rgh
+    _check_combine(orc, d["y_ret"], p["send_pos"], d["scores"][0], "large_skew")
+
+
+def test_combine_order_vectors(orc):
+    # vectors whose result changes under any other order or rounding (an
+    # fp64 or reversed-order or pairwise sum, a fused multiply-add): the
+    # kernels give the oracle's bits, on the unrolled path (K = 4, 2) and the
+    # generic one (K = 20), with rows of a ragged vector count
+    require_gpu()
+
+    def rows(vals, H):
+        bits = (np.array(vals, np.float32).view(np.uint32) >> 16).astype(np.uint16)
+        return np.repeat(bits[:, None], H, axis=1)
+
+    H = 72
+    y = rows([1.0, 2.0 ** -24, 2.0 ** -24, -1.0], H)
+    _check_combine(orc, y, np.arange(4, dtype=np.int32), np.ones((1, 4), np.float32),
+                   "forward k order")
+    y = rows([1.0, 1.0 + 2.0 ** -7], H)
+    sc = np.array([[1.0, 1.0 + 2.0 ** -23]], np.float32)
+    gb, gf, _, _ = _check_combine(orc, y, np.array([0, 1], np.int32), sc, "product rounding")
+    assert np.all(gf == np.float32(2.0 + 2.0 ** -7)) and np.all(gb == 0x4000)
+    # K = 20 (generic kernel): the forward-order vector padded with zero
+    # rows and skipped routes
+    y = rows([1.0, 2.0 ** -24, 2.0 ** -24, -1.0, 0.0], H)
+    sp = np.full(20, -1, np.int32)
+    sp[[0, 5, 11, 19]] = [0, 1, 2, 3]
+    sp[[1, 2]] = 4
+    gb, gf, _, _ = _check_combine(orc, y, sp, np.ones((1, 20), np.float32), "generic K=20")
+    assert np.all(gf == 0.0)
 
 
 def test_eplb_pack_after_remap(orc):
@@ -174,6 +205,33 @@ def test_row_kernels_odd_shapes(orc, T, K, H):
     assert np.array_equal(host(rg), orc.group(raw, rp))
     sc = (rng.standard_normal((T, K)).astype(np.float32))
     _check_combine(orc, raw, sp, sc, f"T={T} K={K} H={H}")
+
+
+def test_short_buffers_bound_the_maps(orc):
+    # a map naming rows past the end of its buffer (a plan map paired with a
+    # dedup-sized buffer): the pack skips stores past send_buf's rows and the
+    # grouping leaves a row untouched when its source is past recv_raw's rows
+    torch = require_gpu()
+    import combine_balancing_amd as cba
+    rng = np.random.default_rng(77)
+    T, K, H = 40, 4, 136
+    x = synth.bf16_normal(rng, (T, H))
+    sp = rng.permutation(T * K).astype(np.int32)
+    n_short = T * K // 3
+    note("pack into a short send buffer")
+    sb = torch.zeros(n_short, H, dtype=torch.bfloat16, device="cuda")
+    cba.dispatch(K, x=dev(x), send_pos=dev(sp), send_buf=sb)
+    torch.cuda.synchronize()
+    assert np.array_equal(host(sb), orc.pack(x, sp, K)[:n_short])
+    raw = synth.bf16_normal(rng, (T * K, H))
+    rp = rng.permutation(T * K).astype(np.int32)
+    note("group from a short arrival buffer")
+    rg = torch.zeros(T * K, H, dtype=torch.bfloat16, device="cuda")
+    cba.dispatch(K, recv_raw=dev(raw[:n_short]), recv_pos=dev(rp), recv_grouped=rg)
+    torch.cuda.synchronize()
+    want = orc.group(raw, rp)
+    want[rp >= n_short] = 0
+    assert np.array_equal(host(rg), want)
 
 
 def test_empty_inputs():

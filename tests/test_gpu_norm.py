@@ -110,7 +110,8 @@ def test_fused_norm_matches_combine(orc):
 
 
 def test_fused_norm_headline_shape(orc):
-    # S=4096 K=8 H=7168 on rank 0's planned send map, sampled tokens
+    # S=4096 K=8 H=7168 on rank 0's planned send map: every token (x_out bit
+    # for bit, rstd and y within the bounds above)
     torch = require_gpu()
     note("combine_add_rmsnorm dsv3")
     d = synth.make_plan_inputs("dsv3")
@@ -119,6 +120,5 @@ def test_fused_norm_headline_shape(orc):
     rng = np.random.default_rng(44)
     res = synth.bf16_normal(rng, (S, d["H"]))
     g = synth.bf16_normal(rng, (d["H"],))
-    rows = np.sort(rng.choice(S, 256, replace=False))
-    _check(orc, d["y_ret"], p["send_pos"], d["scores"][0], res, g, 1e-6, rows=rows)
+    _check(orc, d["y_ret"], p["send_pos"], d["scores"][0], res, g, 1e-6)
     del torch

@@ -34,9 +34,16 @@ def _assert_same(ref, got, ctx):
 def _rand_ids(rng, R, E, S, K, skew):
     w = np.exp(-skew * np.log(np.arange(E) + 1.0))
     w /= w.sum()
-    # Gumbel top-K: distinct ids per token drawn with weights w
-    g = rng.gumbel(size=(R * S, E)) + np.log(w)
-    return np.argsort(-g, axis=1, kind="stable")[:, :K].astype(np.int32)
+    # Gumbel top-K: distinct ids per token drawn with weights w, in blocks
+    # of tokens so that large cases stay small in memory
+    out = np.empty((R * S, K), np.int32)
+    step = 8192
+    for t0 in range(0, R * S, step):
+        g = -(rng.gumbel(size=(min(step, R * S - t0), E)) + np.log(w))
+        top = np.argpartition(g, K - 1, axis=1)[:, :K] if K < E else np.tile(np.arange(E), (g.shape[0], 1))
+        order = np.argsort(np.take_along_axis(g, top, 1), axis=1, kind="stable")
+        out[t0:t0 + g.shape[0]] = np.take_along_axis(top, order, 1)
+    return out
 
 
 @pytest.mark.parametrize("name", ["tiny", "small", "dsv3", "large_skew"])
@@ -60,6 +67,9 @@ CASES = [
     (4, 4, 129, 1, 3.0), (6, 3, 200, 1, 1.0), (5, 1, 64, 1, 0.0), (16, 64, 333, 4, 1.5),
     (64, 256, 40, 8, 1.0), (7, 1024, 150, 16, 0.5), (33, 100, 77, 5, 2.5),
     (128, 1000, 20, 8, 1.0), (1024, 1024, 3, 2, 1.0), (2, 1024, 5000, 2, 3.0),
+    # chunks above 2048 routes with experts above 256: ids read from global
+    # memory (not staged) and 10-bit keys in the wave multi-split
+    (64, 1024, 2560, 8, 1.0),
 ]
 
 

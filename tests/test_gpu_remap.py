@@ -124,3 +124,28 @@ def test_rejects_unpaired_optionals():
         cba.remap_prune(ids, table, 2, 1, 0, 0, expert_scales=sc)
     with pytest.raises(B.MepError):
         cba.remap_prune(ids, table, 2, 1, 2, 0)
+
+
+def test_prune_order_vectors(orc):
+    # tokens whose mask flips under an fp64 or reversed-order threshold sum
+    # or a fused multiply-add: the kernel takes the oracle's decisions
+    require_gpu()
+    table = np.array([[1, 0], [1, 1], [1, 2]], np.int32)
+    ids = np.array([[0, 1, 2], [0, 1, 2]], np.int32)
+    one = 0x3F80
+    thr = np.array([1.0, 2.0 ** -24, 2.0 ** -24], np.float32)
+    for t, want in ((thr, 1), (thr[::-1].copy(), 0)):
+        note(f"prune order vector thr={t.tolist()}")
+        sc = np.full((2, 3), one, np.uint16)
+        got = _gpu(ids, table, 3, 1, 0, 0, scales=sc, thr=t)
+        ref = orc.remap_prune(ids, table, 3, 1, 0, 0, expert_scales=sc, pruning_threshold=t)
+        _cmp(ref, got, "prune order")
+        assert np.all(got["balanced_mask"] == want)
+    sc = np.array([[1.0, 1.0 + 2.0 ** -7, 2.0 + 2.0 ** -7]] * 2, np.float32)
+    thr = np.array([1.0, 1.0 + 2.0 ** -23, 0.0], np.float32)
+    note("prune product-rounding vector")
+    got = _gpu(ids, table, 3, 1, 0, 0, scales=sc, sdt="fp32", thr=thr)
+    ref = orc.remap_prune(ids, table, 3, 1, 0, 0, expert_scales=sc, scale_dtype="fp32",
+                          pruning_threshold=thr)
+    _cmp(ref, got, "prune product rounding")
+    assert got["balanced_mask"].tolist() == [[0, 0, 1], [0, 0, 1]]

@@ -210,3 +210,47 @@ def test_zero_copy_equals_pack_exchange_group(orc, name):
                                   d["scores"][m])
         assert np.array_equal(ob, res[m]["out_bf16"])
         assert np.array_equal(of, res[m]["out_f32"])
+
+
+# --- the fixed k order and the separate fp32 roundings of the combine -------
+# The combine sums in k order from +0, rounding each product and each partial
+# sum to fp32 on its own ("MoonEP API完全参考" §3.1 combine; the op doc's
+# combine takes the same per-route scales). These vectors give a different
+# answer under any other order or rounding: an fp64 accumulator, a reversed
+# or pairwise k order, or a fused multiply-add.
+
+def _bf16_rows(vals, H=8):
+    """bf16 rows of constant value (each value exact in bf16)."""
+    bits = (np.array(vals, np.float32).view(np.uint32) >> 16).astype(np.uint16)
+    assert np.array_equal(_f32(bits), np.array(vals, np.float32))
+    return np.repeat(bits[:, None], H, axis=1)
+
+
+def test_combine_order_pins_forward_k_sum(orc):
+    # rows 1, 2^-24, 2^-24, -1 with unit scores:
+    #   in k order: 1 + 2^-24 is a tie that rounds to 1 (even), twice, then
+    #               1 - 1 = 0
+    #   exact (fp64) 2^-23; reversed order 2^-23; pairwise (1 + 2^-24) +
+    #   (2^-24 - 1) = 2^-24
+    y = _bf16_rows([1.0, 2.0 ** -24, 2.0 ** -24, -1.0])
+    ob, of = orc.combine(y, np.arange(4, dtype=np.int32), np.ones((1, 4), np.float32))
+    assert np.all(of == 0.0) and not np.signbit(of).any()
+    assert np.all(ob == 0x0000)
+    # the first three routes alone: still exactly 1 (a tie kept at 1 twice)
+    ob, of = orc.combine(y, np.array([0, 1, 2, -1], np.int32), np.ones((1, 4), np.float32))
+    assert np.all(of == 1.0)
+
+
+def test_combine_pins_separate_product_rounding(orc):
+    # route 0: 1 * 1 = 1; route 1: (1 + 2^-23) * (1 + 2^-7)
+    #   = 1 + 2^-7 + 2^-23 + 2^-30, rounded alone to 1 + 2^-7 + 2^-23;
+    #   1 + that = 2 + 2^-7 + 2^-23, a tie at ulp 2^-22 -> 2 + 2^-7 (even).
+    # A fused multiply-add (or fp64) sees the 2^-30 and rounds up to
+    # 2 + 2^-7 + 2^-22. bf16 of 2 + 2^-7 is again a tie -> 2.0 (0x4000);
+    # of the fused result 2 + 2^-6 (0x4001).
+    y = _bf16_rows([1.0, 1.0 + 2.0 ** -7])
+    sc = np.array([[1.0, 1.0 + 2.0 ** -23]], np.float32)
+    assert sc[0, 1] == np.float32(1.0 + 2.0 ** -23)
+    ob, of = orc.combine(y, np.array([0, 1], np.int32), sc)
+    assert np.all(of == np.float32(2.0 + 2.0 ** -7))
+    assert np.all(ob == 0x4000)

@@ -166,3 +166,44 @@ def test_rejects_unpaired_optionals(orc):
         orc.remap_prune(ids, table, 2, 1, 0, 0, active_mask=np.ones(1, np.uint8))
     with pytest.raises(orc.OracleError):
         orc.remap_prune(ids, table, 2, 1, 0, 2)
+
+
+# --- the prune threshold sum: fp32, k order, products rounded alone ---------
+# "aclnnMoeUpdateExpert" 功能说明: a route is pruned when its scale is below
+# the token's sum of scale x threshold. The reading (R-h) fixes that sum as
+# fp32, added in k order from +0 with each product rounded on its own. These
+# tokens flip their mask under an fp64 (or reversed-order) sum, or under a
+# fused multiply-add.
+
+def test_prune_sum_is_sequential_fp32(orc):
+    # unit scales, thresholds 1, 2^-24, 2^-24: products 1, 2^-24, 2^-24.
+    #   k order: 1 + 2^-24 is a tie -> 1 (even), twice: sum 1, so every
+    #            scale (1) equals the sum and is kept.
+    #   fp64 or reversed order: 1 + 2^-23 > 1, every route pruned.
+    table = np.array([[1, 0], [1, 1], [1, 2]], np.int32)
+    ids = np.array([[0, 1, 2]], np.int32)
+    thr = np.array([1.0, 2.0 ** -24, 2.0 ** -24], np.float32)
+    out = orc.remap_prune(ids, table, 3, 1, 0, 0, expert_scales=_bf16([[1.0, 1.0, 1.0]]),
+                          pruning_threshold=thr)
+    assert out["balanced_mask"].tolist() == [[1, 1, 1]]
+    # the thresholds reversed: 2^-24 + 2^-24 = 2^-23 first, then 1 + 2^-23
+    # is exact, so the sum exceeds 1 and all three routes are pruned
+    out = orc.remap_prune(ids, table, 3, 1, 0, 0, expert_scales=_bf16([[1.0, 1.0, 1.0]]),
+                          pruning_threshold=thr[::-1].copy())
+    assert out["balanced_mask"].tolist() == [[0, 0, 0]]
+
+
+def test_prune_products_rounded_before_the_add(orc):
+    # fp32 scales 1, 1 + 2^-7, 2 + 2^-7 with thresholds 1, 1 + 2^-23, 0:
+    #   products 1, fl(1 + 2^-7 + 2^-23 + 2^-30) = 1 + 2^-7 + 2^-23, 0;
+    #   1 + (1 + 2^-7 + 2^-23) = 2 + 2^-7 + 2^-23 is a tie at ulp 2^-22 and
+    #   rounds to 2 + 2^-7 (even). The third scale equals the sum: kept.
+    #   A fused multiply-add (or fp64) keeps the 2^-30 and the sum rounds up
+    #   to 2 + 2^-7 + 2^-22: the third route would be pruned.
+    table = np.array([[1, 0], [1, 1], [1, 2]], np.int32)
+    ids = np.array([[0, 1, 2]], np.int32)
+    sc = np.array([[1.0, 1.0 + 2.0 ** -7, 2.0 + 2.0 ** -7]], np.float32)
+    thr = np.array([1.0, 1.0 + 2.0 ** -23, 0.0], np.float32)
+    out = orc.remap_prune(ids, table, 3, 1, 0, 0, expert_scales=sc, scale_dtype="fp32",
+                          pruning_threshold=thr)
+    assert out["balanced_mask"].tolist() == [[0, 0, 1]]
