@@ -15,6 +15,7 @@ LIB_PATH = os.path.join(_HERE, "libmep.so")
 
 MEP_OK, MEP_ERR_NULLPTR, MEP_ERR_PARAM, MEP_ERR_SHAPE, MEP_ERR_HIP = range(5)
 MEP_SCALE_F32, MEP_SCALE_BF16, MEP_SCALE_F16 = 0, 1, 2
+MEP_PLAN_NOALLOC_SCRATCH_BYTES = 4 << 20  # include/mep.h
 
 _lib = None
 
@@ -45,6 +46,8 @@ def lib():
     L.mep_plan_workspace_size.restype = Z
     L.mep_plan.argtypes = [I, I, I, I, I, P, P, Z] + [P] * 12 + [P]
     L.mep_plan.restype = I
+    L.mep_plan_noalloc.argtypes = [I, I, I, I, I, P] + [P] * 12 + [P]
+    L.mep_plan_noalloc.restype = I
     L.mep_remap_prune.argtypes = [I] * 8 + [P, P, P, I, P, P, P, P, P, P, P]
     L.mep_remap_prune.restype = I
     L.mep_dispatch.argtypes = [I, I, I, P, P, P, I, I, P, P, I, P, P]
@@ -99,6 +102,15 @@ def mep_plan(R, E, S, K, my_rank, topk_ids, workspace, workspace_bytes,
                           expert_count, rank_load, route_dest, route_slot, inst_count,
                           inst_expert, inst_cu, inst_gid_base, send_pos, send_count,
                           recv_pos, recv_count, stream)
+
+
+def mep_plan_noalloc(R, E, S, K, my_rank, topk_ids, expert_count, rank_load, route_dest,
+                     route_slot, inst_count, inst_expert, inst_cu, inst_gid_base, send_pos,
+                     send_count, recv_pos, recv_count, stream) -> int:
+    return lib().mep_plan_noalloc(R, E, S, K, my_rank, topk_ids, expert_count, rank_load,
+                                  route_dest, route_slot, inst_count, inst_expert, inst_cu,
+                                  inst_gid_base, send_pos, send_count, recv_pos, recv_count,
+                                  stream)
 
 
 def mep_remap_prune(BS, K, E, F, world_size, place_per_rank, local_rank_id,

@@ -94,6 +94,35 @@ def plan(topk_ids, R, E, S, K, my_rank=0, workspace=None, out=None, stream=None,
     return out
 
 
+def plan_noalloc(topk_ids, R, E, S, K, my_rank=0, out=None, stream=None, with_routes=True):
+    """mep_plan_noalloc: mep_plan with its workspace in the library's static
+    device array (no workspace argument, nothing allocated by the library).
+    Outputs are allocated here only when `out` is not given."""
+    N = R * S * K
+    ids = _need(topk_ids, "topk_ids", torch.int32, N)
+    if out is None:
+        out = plan_outputs(R, E, S, K, topk_ids.device, with_routes)
+    C = S * K
+    o = out
+    rc = B.mep_plan_noalloc(
+        R, E, S, K, my_rank, ids,
+        _need(o["expert_count"], "expert_count", torch.int32, E),
+        _need(o["rank_load"], "rank_load", torch.int32, R),
+        _opt(o["route_dest"], "route_dest", torch.int32, N),
+        _opt(o["route_slot"], "route_slot", torch.int32, N),
+        _need(o["inst_count"], "inst_count", torch.int32, R),
+        _need(o["inst_expert"], "inst_expert", torch.int32, R * E),
+        _need(o["inst_cu"], "inst_cu", torch.int32, R * (E + 1)),
+        _need(o["inst_gid_base"], "inst_gid_base", torch.int32, R + 1),
+        _need(o["send_pos"], "send_pos", torch.int32, C),
+        _need(o["send_count"], "send_count", torch.int32, R),
+        _need(o["recv_pos"], "recv_pos", torch.int32, C),
+        _need(o["recv_count"], "recv_count", torch.int32, R),
+        _stream_handle(stream))
+    B.check("mep_plan_noalloc", rc)
+    return out
+
+
 _SCALE_CODES = {torch.float32: B.MEP_SCALE_F32, torch.bfloat16: B.MEP_SCALE_BF16,
                 torch.float16: B.MEP_SCALE_F16}
 

@@ -33,6 +33,8 @@
 // position order, so a route's send (receive) row is a per-instance base
 // plus its rank among the same source's routes of that expert.
 #include <algorithm>
+#include <atomic>
+#include <mutex>
 
 #include "mep_device.h"
 
@@ -944,26 +946,33 @@ extern "C" size_t mep_plan_workspace_size(int R, int E, int S, int K) {
     return ws_offsets(d).total;
 }
 
-extern "C" int mep_plan(int R, int E, int S, int K, int my_rank, const int32_t* topk_ids,
-                        void* workspace, size_t workspace_bytes, int32_t* expert_count,
-                        int32_t* rank_load, int32_t* route_dest, int32_t* route_slot,
-                        int32_t* inst_count, int32_t* inst_expert, int32_t* inst_cu,
-                        int32_t* inst_gid_base, int32_t* send_pos, int32_t* send_count,
-                        int32_t* recv_pos, int32_t* recv_count, void* stream) {
-    if (!topk_ids || !workspace || !expert_count || !rank_load || !inst_count || !inst_expert ||
-        !inst_cu || !inst_gid_base || !send_pos || !send_count || !recv_pos || !recv_count)
+namespace mep {
+namespace {
+
+// Validation shared by both plan entry points (everything but the
+// workspace). On success *d holds the sizes and *o the outputs.
+int plan_check(int R, int E, int S, int K, int my_rank, const int32_t* topk_ids,
+               int32_t* expert_count, int32_t* rank_load, int32_t* route_dest,
+               int32_t* route_slot, int32_t* inst_count, int32_t* inst_expert, int32_t* inst_cu,
+               int32_t* inst_gid_base, int32_t* send_pos, int32_t* send_count, int32_t* recv_pos,
+               int32_t* recv_count, PlanDims* d, PlanOut* o) {
+    if (!topk_ids || !expert_count || !rank_load || !inst_count || !inst_expert || !inst_cu ||
+        !inst_gid_base || !send_pos || !send_count || !recv_pos || !recv_count)
         return MEP_ERR_NULLPTR;
-    PlanDims d;
-    if (!plan_dims(R, E, S, K, my_rank, &d)) return MEP_ERR_SHAPE;
+    if (!plan_dims(R, E, S, K, my_rank, d)) return MEP_ERR_SHAPE;
     if (K > E || my_rank < 0 || my_rank >= R) return MEP_ERR_PARAM;
     if ((route_dest == nullptr) != (route_slot == nullptr)) return MEP_ERR_PARAM;
-    const WsOffsets off = ws_offsets(d);
-    if (workspace_bytes < off.total || ((uintptr_t)workspace & 255u) != 0) return MEP_ERR_PARAM;
-    const size_t glds = global_lds_bytes(d), rlds = routes_lds_bytes(d);
+    const size_t glds = global_lds_bytes(*d), rlds = routes_lds_bytes(*d);
     if (glds > kMaxLds || rlds > kMaxLds) return MEP_ERR_SHAPE;  // not reachable within the limits
-    if ((glds > 64 * 1024 || rlds > 64 * 1024) && !lds_ready()) return MEP_ERR_HIP;
+    *o = PlanOut{expert_count, rank_load, route_dest, route_slot, inst_count, inst_expert,
+                 inst_cu, inst_gid_base, send_pos, send_count, recv_pos, recv_count};
+    return MEP_OK;
+}
 
-    char* ws = (char*)workspace;
+// The four launches on a workspace already checked against ws_offsets(d).
+int plan_launch(const PlanDims& d, char* ws, const int32_t* topk_ids, const PlanOut& o,
+                hipStream_t s) {
+    const WsOffsets off = ws_offsets(d);
     PlanWs w;
     w.chunk = (int*)(ws + off.chunk);
     w.cnt = (int*)(ws + off.cnt);
@@ -979,9 +988,8 @@ extern "C" int mep_plan(int R, int E, int S, int K, int my_rank, const int32_t* 
     w.recvbase = (int*)(ws + off.recvbase);
     w.rinfo = (int4*)(ws + off.rinfo);
     w.scal = (int*)(ws + off.scal);
-    PlanOut o{expert_count, rank_load, route_dest, route_slot, inst_count, inst_expert,
-              inst_cu, inst_gid_base, send_pos, send_count, recv_pos, recv_count};
-    hipStream_t s = (hipStream_t)stream;
+    const size_t glds = global_lds_bytes(d), rlds = routes_lds_bytes(d);
+    if ((glds > 64 * 1024 || rlds > 64 * 1024) && !lds_ready()) return MEP_ERR_HIP;
 
     hipLaunchKernelGGL(plan_hist, dim3(d.nchunks), dim3(kHistThreads), d.E * sizeof(int), s, d,
                        (const int*)topk_ids, w.chunk);
@@ -1003,4 +1011,90 @@ extern "C" int mep_plan(int R, int E, int S, int K, int my_rank, const int32_t* 
     }
     MEP_LAUNCH_CHECK();
     return MEP_OK;
+}
+
+}  // namespace
+}  // namespace mep
+
+extern "C" int mep_plan(int R, int E, int S, int K, int my_rank, const int32_t* topk_ids,
+                        void* workspace, size_t workspace_bytes, int32_t* expert_count,
+                        int32_t* rank_load, int32_t* route_dest, int32_t* route_slot,
+                        int32_t* inst_count, int32_t* inst_expert, int32_t* inst_cu,
+                        int32_t* inst_gid_base, int32_t* send_pos, int32_t* send_count,
+                        int32_t* recv_pos, int32_t* recv_count, void* stream) {
+    if (!workspace) return MEP_ERR_NULLPTR;
+    PlanDims d;
+    PlanOut o;
+    const int st = plan_check(R, E, S, K, my_rank, topk_ids, expert_count, rank_load, route_dest,
+                              route_slot, inst_count, inst_expert, inst_cu, inst_gid_base,
+                              send_pos, send_count, recv_pos, recv_count, &d, &o);
+    if (st != MEP_OK) return st;
+    if (workspace_bytes < ws_offsets(d).total || ((uintptr_t)workspace & 255u) != 0)
+        return MEP_ERR_PARAM;
+    return plan_launch(d, (char*)workspace, topk_ids, o, (hipStream_t)stream);
+}
+
+// ------------------------------------------------------ allocation-free plan
+// mep_plan_noalloc keeps its workspace in this file-scope device array: each
+// GPU holds its own copy, at its own address, for the life of the process.
+// In host code the name `scratch` stands for a host-side shadow, not a device
+// address, so the kernels only ever see the address hipGetSymbolAddress
+// returns for the current device.
+static __device__ __align__(256) unsigned char scratch[MEP_PLAN_NOALLOC_SCRATCH_BYTES];
+
+namespace mep {
+namespace {
+
+constexpr int kMaxDevices = 64;
+std::atomic<void*> g_scratch_ptr[kMaxDevices];
+std::mutex g_scratch_mu;
+
+// Device address of `scratch` on the current device, looked up once per
+// device (the first call on that device) and kept.
+int scratch_on_current_device(void** out) {
+    int dev = -1;
+    if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= kMaxDevices) {
+        (void)hipGetLastError();
+        return MEP_ERR_HIP;
+    }
+    void* p = g_scratch_ptr[dev].load(std::memory_order_acquire);
+    if (!p) {
+        std::lock_guard<std::mutex> lock(g_scratch_mu);
+        p = g_scratch_ptr[dev].load(std::memory_order_relaxed);
+        if (!p) {
+            if (hipGetSymbolAddress(&p, HIP_SYMBOL(scratch)) != hipSuccess || !p) {
+                (void)hipGetLastError();
+                return MEP_ERR_HIP;
+            }
+            g_scratch_ptr[dev].store(p, std::memory_order_release);
+        }
+    }
+    *out = p;
+    return MEP_OK;
+}
+
+}  // namespace
+}  // namespace mep
+
+extern "C" int mep_plan_noalloc(int R, int E, int S, int K, int my_rank, const int32_t* topk_ids,
+                                int32_t* expert_count, int32_t* rank_load, int32_t* route_dest,
+                                int32_t* route_slot, int32_t* inst_count, int32_t* inst_expert,
+                                int32_t* inst_cu, int32_t* inst_gid_base, int32_t* send_pos,
+                                int32_t* send_count, int32_t* recv_pos, int32_t* recv_count,
+                                void* stream) {
+    PlanDims d;
+    PlanOut o;
+    const int st = plan_check(R, E, S, K, my_rank, topk_ids, expert_count, rank_load, route_dest,
+                              route_slot, inst_count, inst_expert, inst_cu, inst_gid_base,
+                              send_pos, send_count, recv_pos, recv_count, &d, &o);
+    if (st != MEP_OK) return st;
+    // sizes whose workspace exceeds the static array are refused
+    if (ws_offsets(d).total > (size_t)MEP_PLAN_NOALLOC_SCRATCH_BYTES) return MEP_ERR_SHAPE;
+    void* ws = nullptr;
+    const int sst = scratch_on_current_device(&ws);
+    if (sst != MEP_OK) return sst;
+    // the plan's outputs do not depend on what its workspace holds on entry
+    // (every value it uses is written earlier in the same call), so the
+    // array needs no clearing between calls
+    return plan_launch(d, (char*)ws, topk_ids, o, (hipStream_t)stream);
 }

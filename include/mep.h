@@ -141,6 +141,43 @@ int mep_plan(int R, int E, int S, int K, int my_rank,
              int32_t* recv_pos, int32_t* recv_count,
              void* stream);
 
+/*
+ * mep_plan_noalloc - mep_plan with no workspace argument and no allocation,
+ * for callers that cannot allocate device memory: code under HIP graph
+ * capture, tight serving loops, harnesses that forbid hipMalloc.
+ *
+ * Computes exactly what mep_plan computes (same kernels, same outputs, same
+ * argument meaning and errors), with the workspace taken from a static
+ * device array of MEP_PLAN_NOALLOC_SCRATCH_BYTES inside the library. Each
+ * GPU the library runs on holds its own copy of that array until the
+ * process ends; its device address is looked up on the first call on each
+ * device. Nothing is allocated (no hipMalloc, no library allocation) at any
+ * call. The device current at the call must be the stream's device.
+ *
+ * Limit: sizes whose mep_plan_workspace_size() exceeds
+ * MEP_PLAN_NOALLOC_SCRATCH_BYTES (4 MiB) return MEP_ERR_SHAPE and enqueue
+ * nothing. For scale: R=8, E=256, S=4096, K=8 needs 0.28 MB and R=64,
+ * E=256, S=8192, K=8 0.61 MB; R = E = 1024 needs 8.5 MB and is refused.
+ *
+ * Every call on one GPU shares that GPU's array: calls that overlap on one
+ * GPU (on different streams, or from several threads) race on it and give
+ * undefined outputs; serialize them (one stream, or events between them).
+ * The plan's outputs do not depend on what the array holds on entry, so it
+ * needs no clearing between calls.
+ * Errors: as mep_plan (no workspace errors), plus MEP_ERR_SHAPE for sizes
+ * beyond the array and MEP_ERR_HIP if the array's address cannot be found.
+ */
+#define MEP_PLAN_NOALLOC_SCRATCH_BYTES (4u << 20)
+int mep_plan_noalloc(int R, int E, int S, int K, int my_rank,
+                     const int32_t* topk_ids,
+                     int32_t* expert_count, int32_t* rank_load,
+                     int32_t* route_dest, int32_t* route_slot,
+                     int32_t* inst_count, int32_t* inst_expert, int32_t* inst_cu,
+                     int32_t* inst_gid_base,
+                     int32_t* send_pos, int32_t* send_count,
+                     int32_t* recv_pos, int32_t* recv_count,
+                     void* stream);
+
 /* ---------------------------------------------------------- remap / prune */
 
 /* Scale element types accepted by mep_remap_prune ([UpdExp] "参数说明":

@@ -37,7 +37,7 @@ def test_header_declares_the_four_entry_points():
               "mep_dispatch_to_peers", "mep_combine_from_peers", "mep_ungroup",
               "mep_combine_add_rmsnorm", "mep_quant_msg_bytes", "mep_dispatch_quant",
               "mep_group_quant", "mep_plan_weight_rows", "mep_plan_dedup_workspace_size",
-              "mep_plan_dedup"):
+              "mep_plan_dedup", "mep_plan_noalloc"):
         assert n in names
 
 
@@ -264,3 +264,25 @@ def test_c_consumer_builds(B):
     import oracle
     oracle.build()
     assert os.path.exists(g.build_c_abi_check())
+
+
+def test_plan_noalloc_validation(B):
+    # argument errors are found on the host before the static array is
+    # looked up or anything is enqueued; sizes whose workspace exceeds the
+    # array are refused
+    f = B.mep_plan_noalloc
+    outs = [16] * 12
+    assert f(2, 4, 8, 2, 0, None, *outs, None) == B.MEP_ERR_NULLPTR
+    assert f(2, 4, 8, 2, 0, 16, *([None] + outs[1:]), None) == B.MEP_ERR_NULLPTR
+    assert f(2, 4, 8, 2, 2, 16, *outs, None) == B.MEP_ERR_PARAM          # my_rank == R
+    assert f(2, 4, 8, 5, 0, 16, *outs, None) == B.MEP_ERR_PARAM          # K > E
+    assert f(0, 4, 8, 2, 0, 16, *outs, None) == B.MEP_ERR_SHAPE
+    o = list(outs)
+    o[2] = None                                                        # route_dest alone
+    assert f(2, 4, 8, 2, 0, 16, *o, None) == B.MEP_ERR_PARAM
+    big = (1024, 1024, 64, 2)
+    assert B.mep_plan_workspace_size(*big) > B.MEP_PLAN_NOALLOC_SCRATCH_BYTES
+    assert f(*big, 0, 16, *outs, None) == B.MEP_ERR_SHAPE
+    # the workloads of the benchmark fit
+    for R, E, S, K in [(8, 256, 4096, 8), (64, 256, 8192, 8), (8, 384, 8192, 8)]:
+        assert 0 < B.mep_plan_workspace_size(R, E, S, K) <= B.MEP_PLAN_NOALLOC_SCRATCH_BYTES
