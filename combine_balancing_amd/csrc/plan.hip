@@ -41,28 +41,19 @@
 namespace mep {
 namespace {
 
-#ifndef MEP_PLAN_ROUTE_THREADS
-#define MEP_PLAN_ROUTE_THREADS 1024
-#endif
-#ifndef MEP_PLAN_TARGET_CHUNKS
+constexpr int kHistThreads = 256;
+constexpr int kMaxChunks = 1024;  // column length of the expert scan (>= the rank limit)
 // Chunks grow until there are at most 512 (or one per source rank when R is
 // larger). A 4M-route plan ran 48.0 us with 1024 chunks of 4096 routes and
 // 45.2 us with 512 of 8192 (the per-chunk kernels then fit the GPU in one
 // wave of work-groups).
-#define MEP_PLAN_TARGET_CHUNKS 512
-#endif
-#ifndef MEP_PLAN_CHUNK
-#define MEP_PLAN_CHUNK 1024
-#endif
-constexpr int kHistThreads = 256;
-constexpr int kMaxChunks = 1024;  // column length of the expert scan (>= the rank limit)
-constexpr int kTargetChunks = MEP_PLAN_TARGET_CHUNKS;
+constexpr int kTargetChunks = 512;
 constexpr int kBuckets = 1024;  // piece lookup: excess index >> shift -> first piece
 constexpr size_t kMaxLds = 160 * 1024;  // LDS a gfx950 work-group may allocate
 constexpr int kGlobalThreads = 1024;
 constexpr int kItemCache = 4;  // plan_global: per-thread items kept between two passes
-constexpr int kRouteThreads = MEP_PLAN_ROUTE_THREADS;  // work-group of plan_routes
-constexpr int kMinChunk = MEP_PLAN_CHUNK;              // routes per chunk (at least)
+constexpr int kRouteThreads = 1024;  // work-group of plan_routes
+constexpr int kMinChunk = 1024;      // routes per chunk (at least)
 constexpr int kRouteWaves = kRouteThreads / kWave;
 constexpr int kMaxR = 1024;
 static_assert(kMaxChunks >= kMaxR, "a source rank holds at least one chunk");
@@ -149,10 +140,7 @@ __global__ __launch_bounds__(kHistThreads) void plan_hist(PlanDims d, const int*
 // across the wave's ranges with shuffles and across the 16 waves through
 // LDS. Measured on MI355X (warm): 8 experts per group beat 4, 16 and 32,
 // and the whole plan went from 63 to 56 us on a 1024-chunk plan.
-#ifndef MEP_PLAN_SCAN_EXPERTS
-#define MEP_PLAN_SCAN_EXPERTS 8
-#endif
-constexpr int kScanExperts = MEP_PLAN_SCAN_EXPERTS;
+constexpr int kScanExperts = 8;
 constexpr int kScanSubs = kWave / kScanExperts;                   // ranges per wave
 constexpr int kScanThreads = 1024;
 constexpr int kScanRanges = (kScanThreads / kWave) * kScanSubs;  // 128
