@@ -483,9 +483,9 @@ def main():
     ap.add_argument("--no-large-skew", action="store_true", help="drop the large_skew leg")
     ap.add_argument("--no-zero-copy", action="store_true", help="drop the zero_copy leg")
     ap.add_argument("--copy-calibration", action="store_true",
-                    help="after the timed steps, run plain device-to-device copies of "
-                         "the group kernel's output size (a known-size reference for "
-                         "HBM byte counters)")
+                    help="after the timed steps, run plain row copies (the library's "
+                         "ungroup kernel with the identity map) of the group kernel's "
+                         "output size: a known-size reference for HBM byte counters")
     args = ap.parse_args()
     if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) != 1:
         print("bench.py runs on exactly one GPU: the hot path is one rank's share "
@@ -664,11 +664,18 @@ def main():
     if "skew_sweep" in legs:
         res["skew_sweep"] = skew_sweep(torch, cba, synth, steps=leg_steps, flush=flush)
     if args.copy_calibration:
+        # a plain copy of known size for scaling the byte counters: the
+        # library's own row copy (mep_ungroup with the identity map, so the
+        # same one-row-per-work-group request pattern as the grouping; a
+        # kernel name of its own, launched nowhere else in a run). torch's
+        # device copy may run on a DMA engine, which no kernel counter sees.
         nbytes = C * H * 2
+        ident = torch.arange(C, dtype=torch.int32, device="cuda")
         for _ in range(3):
-            grouped.copy_(recv_raw)
+            cba.ungroup(recv_raw, ident, y_arrival=grouped)
         torch.cuda.synchronize()
         res["copy_calibration_bytes"] = nbytes
+        res["copy_calibration_kernel"] = "ungroup_rows (identity map)"
     if not args.no_cpu_baseline:
         import oracle
         plan_ref = oracle.plan(d["topk_ids"], R, E, S, K, 0)
