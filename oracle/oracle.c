@@ -33,8 +33,11 @@
  * force, equivalence with already pinned functions). Parity unpinned, where
  * the pages print no formula or example and the pins fix the reading taken
  * rather than the pages: remap with instance counts above one beyond the
- * hand-derived examples; prune decisions within rounding distance of the
- * threshold sum; the combine + add + RMSNorm formula
+ * hand-derived examples; the precision and order of the prune threshold sum
+ * (the pins fix the stated reading, fp32 in k order with each product
+ * rounded, by tokens whose mask flips under fp64, a reversed order or a
+ * fused multiply-add; the pages say nothing of it); the combine + add +
+ * RMSNorm formula
  * (oracle_combine_add_rmsnorm); the int8 quantization formula
  * (oracle_dispatch_quant); the prefetch-slot order (oracle_weight_rows);
  * the dedup orders (oracle_plan_dedup).
