@@ -440,6 +440,36 @@ def graph_step(torch, step, steps, flush=None):
             "what": "plan + remap/prune + pack + group + combine, one graph replay"}
 
 
+def plan_graph(torch, cba, ids, R, E, S, K, pout, steps, flush=None):
+    """The plan alone, captured in a HIP graph through the allocation-free
+    entry point (mep_plan_noalloc: no workspace to allocate, nothing to
+    clear) and replayed with cold caches. Beside the eager plan_us this
+    shows how much of the plan's time is the host enqueueing its launches."""
+    s = torch.cuda.Stream()
+    s.wait_stream(torch.cuda.current_stream())
+    with torch.cuda.stream(s):
+        cba.plan_noalloc(ids, R, E, S, K, my_rank=0, out=pout)
+    torch.cuda.current_stream().wait_stream(s)
+    torch.cuda.synchronize()
+    g = torch.cuda.CUDAGraph()
+    with torch.cuda.graph(g):
+        cba.plan_noalloc(ids, R, E, S, K, my_rank=0, out=pout)
+    torch.cuda.synchronize()
+    stream = torch.cuda.current_stream()
+    t = []
+    for it in range(steps + 3):
+        if flush is not None:
+            flush.fill_(it & 0xFF)
+        ev = [torch.cuda.Event(enable_timing=True) for _ in range(2)]
+        ev[0].record(stream)
+        g.replay()
+        ev[1].record(stream)
+        torch.cuda.synchronize()
+        if it >= 3:
+            t.append(ev[0].elapsed_time(ev[1]) * 1e3)
+    return round(float(np.median(t)), 2)
+
+
 def copy_reference(torch, cba, K, recv_raw, grouped, group_gbs, steps, flush=None):
     """Copy references at the grouping's size, same cold caches: the grouping
     kernel with the identity map (a purely sequential copy) and torch's
@@ -650,6 +680,8 @@ def main():
                                                steps=leg_steps, flush=flush)
     if "graph_step" in legs:
         res["graph_step"] = graph_step(torch, step, steps=leg_steps, flush=flush)
+        res["graph_step"]["plan_us_median"] = plan_graph(torch, cba, ids, R, E, S, K, pout,
+                                                         steps=leg_steps, flush=flush)
     if "combine_add_rmsnorm" in legs:
         res["combine_add_rmsnorm"] = fused_norm(torch, cba, d, pout, y_ret, scores,
                                                 steps=leg_steps, flush=flush)

@@ -88,3 +88,38 @@ def test_step_graph_replays(orc, name):
         ref = orc.plan(d2["topk_ids"], R, E, S, K, m=0)
         assert np.array_equal(got["send_pos"], ref["send_pos"])
         assert np.array_equal(got["recv_pos"], ref["recv_pos"])
+
+
+def test_noalloc_plan_graph_replays(orc):
+    # the allocation-free plan (its workspace in the library's static array)
+    # captured alone in a HIP graph: each replay, on new routing written
+    # into the captured input, equals the oracle's plan on every output
+    torch = require_gpu()
+    import combine_balancing_amd as cba
+    d = synth.make_routing("dsv3")
+    R, E, S, K = d["R"], d["E"], d["S"], d["K"]
+    ids = dev(d["topk_ids"].reshape(-1))
+    out = cba.plan_outputs(R, E, S, K)
+    note("graph noalloc plan: warm-up and capture")
+    s = torch.cuda.Stream()
+    s.wait_stream(torch.cuda.current_stream())
+    with torch.cuda.stream(s):
+        cba.plan_noalloc(ids, R, E, S, K, my_rank=2, out=out)
+    torch.cuda.current_stream().wait_stream(s)
+    torch.cuda.synchronize()
+    g = torch.cuda.CUDAGraph()
+    with torch.cuda.graph(g):
+        cba.plan_noalloc(ids, R, E, S, K, my_rank=2, out=out)
+    torch.cuda.synchronize()
+    for rep in range(3):
+        d2 = synth.make_routing("dsv3", seed=200 + rep)
+        ids.copy_(dev(d2["topk_ids"].reshape(-1)))
+        note(f"graph noalloc plan: replay {rep}")
+        g.replay()
+        torch.cuda.synchronize()
+        ref = orc.plan(d2["topk_ids"], R, E, S, K, m=2)
+        for k, v in ref.items():
+            assert np.array_equal(host(out[k]).reshape(-1), v.reshape(-1)), (rep, k)
+        # eager work of another entry point between replays
+        cba.plan(ids, R, E, S, K, my_rank=0)
+        torch.cuda.synchronize()
