@@ -274,24 +274,187 @@ __device__ __forceinline__ int wave0_exclusive_sum(int v, int* total) {
     return inc - v;
 }
 
-// One element per thread in the per-expert and per-rank phases (E, R <= NT).
-__global__ __launch_bounds__(kGlobalThreads) void plan_global(PlanDims d, PlanWs w, PlanOut o) {
-    extern __shared__ int lds[];
+// Tables that the fused kernel (plan_fused) keeps in its own LDS where the
+// two-kernel form passes them through the workspace.
+struct FusedLds {
+    int* pre0;    // [E] routes of expert e from source ranks below this block's source
+    int* pre1;    // [E] the same below the next source rank
+    int4* prec;   // [E+R+1] piece records, as PlanWs::prec
+    int* nsend;   // [E] send base of each native instance (this rank)
+    int* rcv;     // [E] receive base of this block's source per local instance of this rank
+    int* bkt;     // [kBuckets]
+};
+
+// What the per-route passes need from the global phases (block-uniform).
+struct PhaseScalars {
+    int NP, ef_m, nat_m, fp_m, nim, shift;
+};
+
+// Phases F to J of a plan_fused work-group (see global_phases). Only this
+// rank's own chunks place routes with the send bases of phase H; the
+// others take the piece records' host, slot base and expert alone. Phase I
+// covers the work-group's own source. Returns before a closing barrier:
+// f.rcv, f.bkt, f.nsend and f.prec are read after the caller's next one.
+// (Run in one epoch, F, I and J measured 0.4 us slower on a 262144-route
+// plan than in this order.)
+__device__ __forceinline__ PhaseScalars fused_tail(const PlanDims& d, const PlanOut& o,
+                                                   const GlobalLds& g, const FusedLds& f, int NP,
+                                                   int totU, int src, int sub) {
+    const int R = d.R, m = d.m;
+    const int tid = threadIdx.x, NT = blockDim.x;
+    const bool out_block = blockIdx.x == 0;
+    int* scr0 = g.scratch;
+    int* scr1 = g.scratch + 2 * (kGlobalThreads / kWave + 1);
+
+    // F. instance counts and gid bases
+    int ic = 0;
+    if (tid < R) {
+        ic = g.ef[tid + 1] - g.ef[tid] + g.np[tid];
+        if (out_block) o.inst_count[tid] = ic;
+    }
+    int NI, gb = 0;
+    if (R <= kWave) {
+        if (tid < kWave) gb = wave0_exclusive_sum(ic, &NI);
+    } else {
+        gb = block_exclusive_sum<false>(ic, scr0, &NI);
+    }
+    if (tid < R) {
+        g.gid[tid] = gb;
+        if (out_block) o.inst_gid_base[tid] = gb;
+    }
+    if (tid == 0) {
+        g.gid[R] = NI;
+        if (out_block) o.inst_gid_base[R] = NI;
+    }
+    lds_barrier();
+    NI = g.gid[R];
+
+    // H. send bases of this rank: instances in gid order = (dest, slot)
+    //    order; c_m(I) = this rank's routes inside instance I. A thread's
+    //    first kItemCache items keep what the first pass found for the
+    //    second.
+    if (src != m) {
+        for (int pi = tid; pi < NP; pi += NT) {
+            const int host = g.phost[pi];
+            f.prec[pi] = make_int4(host, g.L[host] - g.dex[host], 0, g.pexp[pi]);
+        }
+    } else {
+        const int ipt = (NI + NT - 1) / NT;
+        const int g0 = min(tid * ipt, NI), g1 = min(g0 + ipt, NI);
+        int hq0[kItemCache], hcm[kItemCache], hpi[kItemCache], he[kItemCache], hfirst[kItemCache];
+        auto counts = [&](int gi, int* q0o, int* cm, int* pi_out, int* e_out, int* first) {
+            const int u = upper_bound(g.gid, R + 1, gi) - 1;
+            int e, P, n, pi;
+            inst_of(g, u, gi - g.gid[u], &e, &P, &n, &pi);
+            const int Hm = g.prem1[e] - g.prem[e];
+            *q0o = clampi(P - g.eex[e] - g.prem[e], 0, Hm);
+            *cm = clampi(P + n - g.eex[e] - g.prem[e], 0, Hm) - *q0o;
+            *pi_out = pi;
+            *e_out = e;
+            *first = gi == g.gid[u] ? u : -1;
+        };
+        int sum = 0;
+#pragma unroll
+        for (int k = 0; k < kItemCache; ++k) {
+            hcm[k] = 0;
+            if (g0 + k < g1) counts(g0 + k, &hq0[k], &hcm[k], &hpi[k], &he[k], &hfirst[k]);
+            sum += hcm[k];
+        }
+        for (int gi = g0 + kItemCache; gi < g1; ++gi) {
+            int a, cm, pi, e, first;
+            counts(gi, &a, &cm, &pi, &e, &first);
+            sum += cm;
+        }
+        int tot;
+        int run = block_exclusive_sum<false>(sum, scr1, &tot);
+        auto place = [&](int a, int cm, int pi, int e, int first) {
+            if (pi < 0) {
+                f.nsend[e] = run - a;
+            } else {
+                const int host = g.phost[pi];
+                f.prec[pi] = make_int4(host, g.L[host] - g.dex[host], run - a, g.pexp[pi]);
+            }
+            if (first >= 0) g.sbase[first] = run;
+            run += cm;
+        };
+#pragma unroll
+        for (int k = 0; k < kItemCache; ++k)
+            if (g0 + k < g1) place(hq0[k], hcm[k], hpi[k], he[k], hfirst[k]);
+        for (int gi = g0 + kItemCache; gi < g1; ++gi) {
+            int a, cm, pi, e, first;
+            counts(gi, &a, &cm, &pi, &e, &first);
+            place(a, cm, pi, e, first);
+        }
+        if (tid == 0) g.sbase[R] = tot;
+    }
+
+    // I. one source: local instance i of m (thread i; nim <= E <= NT)
+    //    covers positions [P', P' + n) of its expert, and this source's
+    //    routes of that expert are [pre0, pre1). The rows that earlier
+    //    sources send to the instance are its overlap with [0, pre0); the
+    //    rows before the item are those of every instance plus this
+    //    source's rows in the instances before it.
+    const int ef_m = g.ef[m];
+    const int nat_m = g.ef[m + 1] - ef_m;
+    const int nim = nat_m + g.np[m];
+    int q0 = 0, cs = 0, before = 0;
+    if (tid < nim) {
+        int e, P, n, pi;
+        inst_of(g, m, tid, &e, &P, &n, &pi);
+        const int pre = f.pre0[e];
+        const int Hs = f.pre1[e] - pre;
+        const int Pl = P - g.eex[e];
+        q0 = clampi(Pl - pre, 0, Hs);
+        cs = clampi(Pl + n - pre, 0, Hs) - q0;
+        before = clampi(pre - Pl, 0, n);
+    }
+    int xcs, xbefore, tcs, tbefore;
+    block_exclusive_sum2<false>(cs, before, scr0, &xcs, &xbefore, &tcs, &tbefore);
+    if (tid < nim) f.rcv[tid] = tbefore + xcs - q0;
+    if (sub == 0 && tid == 0) o.recv_count[src] = tcs;
+    // g.sbase (phase H) is visible after the scan's barriers
+    if (src == m && sub == 0)
+        for (int r = tid; r < R; r += NT) o.send_count[r] = g.sbase[r + 1] - g.sbase[r];
+
+    // J. bucket table: a route finds its piece with one lookup and a short
+    //    walk (piece starts are read from g.pst in place)
+    int shift = 0;
+    while (((long long)kBuckets << shift) < totU) ++shift;
+    for (int b = tid; b < kBuckets; b += NT) {
+        const long long start = (long long)b << shift;
+        f.bkt[b] = start < totU ? upper_bound(g.pst, NP, (int)start) - 1 : max(NP - 1, 0);
+    }
+    return PhaseScalars{NP, ef_m, nat_m, g.fp[m], nim, shift};
+}
+
+// Phases A-J of the plan, run by one work-group with every table in LDS.
+// FUSED = false: the single plan_global work-group, which writes the whole
+// plan's tables to the workspace for plan_routes. FUSED = true: every
+// plan_fused work-group runs them for itself (phases F-J in fused_tail);
+// work-group 0 writes the per-expert and per-rank outputs, the first
+// work-group of each source rank its receive count (and, for this rank, the
+// send counts), and only this rank's own source chunks need the send bases
+// of phase H. The receive bases of phase I are then those of the
+// work-group's source alone, which only needs the routes of each expert
+// below that source and below the next (f.pre0, f.pre1). c, pm, pm1: expert e's route total and the routes of e
+// from source ranks below m and below m+1 (-1 when m is the last rank),
+// held by thread e; pm and pm1 are read only by phase H (fused: only where
+// src == m). One element per thread in the per-expert and per-rank phases
+// (E, R <= NT).
+template <bool FUSED>
+__device__ __forceinline__ PhaseScalars global_phases(const PlanDims& d, const PlanWs& w,
+                                                      const PlanOut& o, const GlobalLds& g,
+                                                      const FusedLds& f, int c, int pm, int pm1,
+                                                      int src, int sub) {
     const int E = d.E, R = d.R, C = d.C, m = d.m;
     const int tid = threadIdx.x, NT = blockDim.x;
-    const GlobalLds g = carve_global(lds, E, R);
+    const bool out_block = !FUSED || blockIdx.x == 0;
     // two scan buffers, alternated between the block scans so that a scan
     // needs no closing barrier
     int* scr0 = g.scratch;
     int* scr1 = g.scratch + 2 * (kGlobalThreads / kWave + 1);
 
-    // A. one round trip: expert totals and this rank's per-expert offsets
-    int c = 0, pm = 0, pm1 = 0;
-    if (tid < E) {
-        c = w.cnt[tid];
-        pm = w.chunk[(m * d.cps) * E + tid];
-        pm1 = m + 1 < R ? w.chunk[((m + 1) * d.cps) * E + tid] : -1;
-    }
+    // A. expert totals and this rank's per-expert offsets
     int total;
     const int ex = block_exclusive_sum<false>(c, scr0, &total);
     if (tid < E) {
@@ -299,12 +462,12 @@ __global__ __launch_bounds__(kGlobalThreads) void plan_global(PlanDims d, PlanWs
         g.eex[tid] = ex;
         g.prem[tid] = pm;
         g.prem1[tid] = pm1 < 0 ? c : pm1;
-        w.eex[tid] = ex;
-        o.expert_count[tid] = c;
+        if constexpr (!FUSED) w.eex[tid] = ex;
+        if (out_block) o.expert_count[tid] = c;
     }
     if (tid == 0) {
         g.eex[E] = total;
-        w.eex[E] = total;
+        if constexpr (!FUSED) w.eex[E] = total;
     }
     lds_barrier();
 
@@ -314,7 +477,7 @@ __global__ __launch_bounds__(kGlobalThreads) void plan_global(PlanDims d, PlanWs
         const int rb = g.eex[ef];
         g.ef[r] = ef;
         g.rb[r] = rb;
-        w.rb[r] = rb;
+        if constexpr (!FUSED) w.rb[r] = rb;
     }
     int U = 0, D = 0;
     if (tid < R) {
@@ -322,8 +485,8 @@ __global__ __launch_bounds__(kGlobalThreads) void plan_global(PlanDims d, PlanWs
         U = max(Lr - C, 0);
         D = max(C - Lr, 0);
         g.L[tid] = Lr;
-        w.load[tid] = Lr;
-        o.rank_load[tid] = Lr;
+        if constexpr (!FUSED) w.load[tid] = Lr;
+        if (out_block) o.rank_load[tid] = Lr;
     }
     int uex = 0, dex = 0, totU, totD;
     if (R <= kWave) {
@@ -337,14 +500,18 @@ __global__ __launch_bounds__(kGlobalThreads) void plan_global(PlanDims d, PlanWs
     if (tid < R) {
         g.uex[tid] = uex;
         g.dex[tid] = dex;
-        w.uex[tid] = uex;
-        w.dex[tid] = dex;
+        if constexpr (!FUSED) {
+            w.uex[tid] = uex;
+            w.dex[tid] = dex;
+        }
     }
     if (tid == 0) {
         g.uex[R] = totU;
         g.dex[R] = totD;
-        w.uex[R] = totU;
-        w.dex[R] = totD;
+        if constexpr (!FUSED) {
+            w.uex[R] = totU;
+            w.dex[R] = totD;
+        }
     }
     lds_barrier();
     totU = g.uex[R];
@@ -437,6 +604,8 @@ __global__ __launch_bounds__(kGlobalThreads) void plan_global(PlanDims d, PlanWs
         g.np[u] = nxt - g.fp[u];
     }
     lds_barrier();
+
+    if constexpr (FUSED) return fused_tail(d, o, g, f, NP, totU, src, sub);
 
     // F. instance counts and gid bases
     int ic = 0;
@@ -596,6 +765,23 @@ __global__ __launch_bounds__(kGlobalThreads) void plan_global(PlanDims d, PlanWs
         w.scal[SC_NIM] = nim;
         w.scal[SC_SHIFT] = shift;
     }
+    return PhaseScalars{NP, ef_m, nat_m, g.fp[m], nim, shift};
+}
+
+// One element per thread in the per-expert and per-rank phases (E, R <= NT).
+__global__ __launch_bounds__(kGlobalThreads) void plan_global(PlanDims d, PlanWs w, PlanOut o) {
+    extern __shared__ int lds[];
+    const int E = d.E, R = d.R, m = d.m;
+    const int tid = threadIdx.x;
+    const GlobalLds g = carve_global(lds, E, R);
+    // one round trip: expert totals and this rank's per-expert offsets
+    int c = 0, pm = 0, pm1 = 0;
+    if (tid < E) {
+        c = w.cnt[tid];
+        pm = w.chunk[(m * d.cps) * E + tid];
+        pm1 = m + 1 < R ? w.chunk[((m + 1) * d.cps) * E + tid] : -1;
+    }
+    (void)global_phases<false>(d, w, o, g, FusedLds{}, c, pm, pm1, 0, 0);
 }
 
 // -------------------------------------------------------------- plan_routes
@@ -641,107 +827,21 @@ __host__ __device__ inline size_t routes_lds_ints(int E, int R, int T) {
            (T <= kStageIds ? T : 0);
 }
 
-// STAGED: the chunk's ids are copied to LDS (chunks of at most kStageIds
-// routes), else both passes read them from global memory (the second time
-// from L2): pass 1 with several loads in flight per lane, pass 2 loading the
-// next step's ids before this step's work. Larger chunks only occur at
-// N > 2M routes, where leaving the ids out of LDS shortened the table-staging
-// prologue and measured 2 us faster on a 4M-route plan. KEY_BITS: width of
-// the expert ids in the wave multi-split (8 ballots when E <= 256).
+// Passes 1 and 2 of a chunk (shared by plan_routes and plan_fused), on the
+// staged tables: s_ex0/s_ex1 per expert, piece starts s_ps and records
+// s_prec, the bucket table s_bkt, zeroed per-wave counters s_cnt and, when
+// STAGED, the chunk's ids in s_ids. The chunk is routes [f0, f0 + len) of
+// source rank src.
 template <bool STAGED, int KEY_BITS>
-__global__ __launch_bounds__(kRouteThreads) void plan_routes(PlanDims d, PlanWs w,
-                                                             const int* __restrict__ ids,
-                                                             PlanOut o) {
-    extern __shared__ int4 lds4[];  // 16-byte aligned base
+__device__ __forceinline__ void route_passes(const PlanDims& d, const int* __restrict__ ids,
+                                             const PlanOut& o, int src, int f0, int len,
+                                             const int4* s_ex0, const int4* s_ex1,
+                                             const int4* s_prec, const int* s_ps,
+                                             const int* s_bkt, int* s_cnt, const int* s_ids,
+                                             int NP, int nat_m, int fp_m, int shift) {
     const int E = d.E, R = d.R, C = d.C, m = d.m;
     const int tid = threadIdx.x;
-    const int PM = E + R + 1;  // room for every piece start
-    int4* s_ex0 = lds4;                                   // [E] {qbase, q0, nsend, home}
-    int4* s_prec = s_ex0 + E;                             // [PM] piece records
-    int4* s_ex1 = s_prec + PM;  // [E] {jbase, native recv base, native cu, recv base of local instance e}
-    int* s_cnt = (int*)(s_ex1 + E);                       // [waves][E]
-    int* s_ps = s_cnt + kRouteWaves * E;                  // [PM] piece starts
-    int* s_bkt = s_ps + PM;                               // [kBuckets]
-    int* s_ids = s_bkt + kBuckets;                        // [T] when T <= kStageIds
-
-    const int c = blockIdx.x;
-    const int src = c / d.cps, sub = c - src * d.cps;
-    const int f0 = src * C + sub * d.T;
-    const int f1 = min(f0 + d.T, (src + 1) * C);
-    const int len = f1 - f0;  // >= 1: a source's last chunk holds the rest of its C routes
-
-    // the staged tables' loads go out first (their LDS writes follow below)
-    int ps_r[kPmRegs], bk_r[kBktRegs], id_r[STAGED ? kIdRegs : 1];
-    i32x4 pr_r[kPmRegs];
-    regs_load(ps_r, w.pstart, PM);
-    regs_load(pr_r, (const i32x4*)w.prec, PM);
-    regs_load(bk_r, w.bucket, kBuckets);
-    if constexpr (STAGED) regs_load(id_r, ids + f0, len);
-    // this block's share of the instance tables (filled after the barrier):
-    // its first rank record joins this round trip
-    const int E1 = E + 1;
-    const int per = (R * E1 + gridDim.x - 1) / gridDim.x;
-    const int lo = min(blockIdx.x * per, R * E1), hi = min(lo + per, R * E1);
-    const int step_u = kRouteThreads / E1, step_i = kRouteThreads - step_u * E1;
-    const int u0 = (lo + tid) / E1, i0 = (lo + tid) - u0 * E1;
-    const int4 ri0 = lo + tid < hi ? w.rinfo[u0] : make_int4(0, 0, 0, 0);
-
-    // one round trip: every table this block reads, and its routes.
-    // For a route of expert e at rank rin among the chunk's routes of e:
-    //   q  = qbase[e] + rin   slot on the home rank if q < C
-    //   qs = q0[e] + rin      rank among this source's routes of e
-    //   j  = jbase[e] + rin   index in the global excess list otherwise
-    const int NP = w.scal[SC_NP];
-    const int ef_m = w.scal[SC_EFIRST_M];
-    const int nat_m = w.scal[SC_NAT_M];
-    const int fp_m = w.scal[SC_FP_M];
-    const int shift = w.scal[SC_SHIFT];
-    for (int e = tid; e < E; e += kRouteThreads) {
-        const int h = home_of(e, R, E);
-        const int off = w.chunk[c * E + e];
-        const int pre = w.chunk[(src * d.cps) * E + e];
-        const int eex = w.eex[e], rbh = w.rb[h];
-        const int qbase = eex + off - rbh;
-        const int rcv = w.recvbase[src * E + e];
-        const int nrcv = h == m ? w.recvbase[src * E + (e - ef_m)] : 0;
-        s_ex0[e] = make_int4(qbase, off - pre, w.nsend[e], h);
-        s_ex1[e] = make_int4(w.uex[h] + qbase - C, nrcv, min(eex - rbh, C), rcv);
-    }
-    for (int i = tid; i < kRouteWaves * E; i += kRouteThreads) s_cnt[i] = 0;
-    regs_store(s_ps, ps_r, PM);
-    regs_store((i32x4*)s_prec, pr_r, PM);
-    regs_store(s_bkt, bk_r, kBuckets);
-    if constexpr (STAGED) regs_store(s_ids, id_r, len);
-    lds_barrier();
-
-    // this block's slice of the instance tables inst_cu [R][E+1] and
-    // inst_expert [R][E]: idx = u*(E+1) + i, walked without divisions; the
-    // first step's rank record was loaded with the tables above
-    {
-        int u = u0, i = i0;
-        for (int idx = lo + tid; idx < hi; idx += kRouteThreads) {
-            const int4 ri = idx == lo + tid ? ri0 : w.rinfo[u];
-            int cu = C, ie = -1;
-            if (i < ri.y) {
-                ie = ri.x + i;
-                cu = s_ex1[ie].z;
-            } else if (i < ri.y + ri.z) {
-                const int pi = ri.w + i - ri.y;
-                const int4 pr = s_prec[pi];
-                cu = pr.y + s_ps[pi];
-                ie = pr.w;
-            }
-            o.inst_cu[idx] = cu;
-            if (i < E) o.inst_expert[u * E + i] = ie;
-            u += step_u;
-            i += step_i;
-            if (i >= E1) {
-                i -= E1;
-                ++u;
-            }
-        }
-    }
-
+    const int PM = E + R + 1;
     const int wave = tid / kWave;
     const int lane = tid & (kWave - 1);
     const int seg = (((len + kRouteWaves - 1) / kRouteWaves) + kWave - 1) & ~(kWave - 1);
@@ -847,6 +947,224 @@ __global__ __launch_bounds__(kRouteThreads) void plan_routes(PlanDims d, PlanWs 
     }
 }
 
+// STAGED: the chunk's ids are copied to LDS (chunks of at most kStageIds
+// routes), else both passes read them from global memory (the second time
+// from L2): pass 1 with several loads in flight per lane, pass 2 loading the
+// next step's ids before this step's work. Larger chunks only occur at
+// N > 2M routes, where leaving the ids out of LDS shortened the table-staging
+// prologue and measured 2 us faster on a 4M-route plan. KEY_BITS: width of
+// the expert ids in the wave multi-split (8 ballots when E <= 256).
+template <bool STAGED, int KEY_BITS>
+__global__ __launch_bounds__(kRouteThreads) void plan_routes(PlanDims d, PlanWs w,
+                                                             const int* __restrict__ ids,
+                                                             PlanOut o) {
+    extern __shared__ int4 lds4[];  // 16-byte aligned base
+    const int E = d.E, R = d.R, C = d.C, m = d.m;
+    const int tid = threadIdx.x;
+    const int PM = E + R + 1;  // room for every piece start
+    int4* s_ex0 = lds4;                                   // [E] {qbase, q0, nsend, home}
+    int4* s_prec = s_ex0 + E;                             // [PM] piece records
+    int4* s_ex1 = s_prec + PM;  // [E] {jbase, native recv base, native cu, recv base of local instance e}
+    int* s_cnt = (int*)(s_ex1 + E);                       // [waves][E]
+    int* s_ps = s_cnt + kRouteWaves * E;                  // [PM] piece starts
+    int* s_bkt = s_ps + PM;                               // [kBuckets]
+    int* s_ids = s_bkt + kBuckets;                        // [T] when T <= kStageIds
+
+    const int c = blockIdx.x;
+    const int src = c / d.cps, sub = c - src * d.cps;
+    const int f0 = src * C + sub * d.T;
+    const int f1 = min(f0 + d.T, (src + 1) * C);
+    const int len = f1 - f0;  // >= 1: a source's last chunk holds the rest of its C routes
+
+    // the staged tables' loads go out first (their LDS writes follow below)
+    int ps_r[kPmRegs], bk_r[kBktRegs], id_r[STAGED ? kIdRegs : 1];
+    i32x4 pr_r[kPmRegs];
+    regs_load(ps_r, w.pstart, PM);
+    regs_load(pr_r, (const i32x4*)w.prec, PM);
+    regs_load(bk_r, w.bucket, kBuckets);
+    if constexpr (STAGED) regs_load(id_r, ids + f0, len);
+    // this block's share of the instance tables (filled after the barrier):
+    // its first rank record joins this round trip
+    const int E1 = E + 1;
+    const int per = (R * E1 + gridDim.x - 1) / gridDim.x;
+    const int lo = min(blockIdx.x * per, R * E1), hi = min(lo + per, R * E1);
+    const int step_u = kRouteThreads / E1, step_i = kRouteThreads - step_u * E1;
+    const int u0 = (lo + tid) / E1, i0 = (lo + tid) - u0 * E1;
+    const int4 ri0 = lo + tid < hi ? w.rinfo[u0] : make_int4(0, 0, 0, 0);
+
+    // one round trip: every table this block reads, and its routes.
+    // For a route of expert e at rank rin among the chunk's routes of e:
+    //   q  = qbase[e] + rin   slot on the home rank if q < C
+    //   qs = q0[e] + rin      rank among this source's routes of e
+    //   j  = jbase[e] + rin   index in the global excess list otherwise
+    const int NP = w.scal[SC_NP];
+    const int ef_m = w.scal[SC_EFIRST_M];
+    const int nat_m = w.scal[SC_NAT_M];
+    const int fp_m = w.scal[SC_FP_M];
+    const int shift = w.scal[SC_SHIFT];
+    for (int e = tid; e < E; e += kRouteThreads) {
+        const int h = home_of(e, R, E);
+        const int off = w.chunk[c * E + e];
+        const int pre = w.chunk[(src * d.cps) * E + e];
+        const int eex = w.eex[e], rbh = w.rb[h];
+        const int qbase = eex + off - rbh;
+        const int rcv = w.recvbase[src * E + e];
+        const int nrcv = h == m ? w.recvbase[src * E + (e - ef_m)] : 0;
+        s_ex0[e] = make_int4(qbase, off - pre, w.nsend[e], h);
+        s_ex1[e] = make_int4(w.uex[h] + qbase - C, nrcv, min(eex - rbh, C), rcv);
+    }
+    for (int i = tid; i < kRouteWaves * E; i += kRouteThreads) s_cnt[i] = 0;
+    regs_store(s_ps, ps_r, PM);
+    regs_store((i32x4*)s_prec, pr_r, PM);
+    regs_store(s_bkt, bk_r, kBuckets);
+    if constexpr (STAGED) regs_store(s_ids, id_r, len);
+    lds_barrier();
+
+    // this block's slice of the instance tables inst_cu [R][E+1] and
+    // inst_expert [R][E]: idx = u*(E+1) + i, walked without divisions; the
+    // first step's rank record was loaded with the tables above
+    {
+        int u = u0, i = i0;
+        for (int idx = lo + tid; idx < hi; idx += kRouteThreads) {
+            const int4 ri = idx == lo + tid ? ri0 : w.rinfo[u];
+            int cu = C, ie = -1;
+            if (i < ri.y) {
+                ie = ri.x + i;
+                cu = s_ex1[ie].z;
+            } else if (i < ri.y + ri.z) {
+                const int pi = ri.w + i - ri.y;
+                const int4 pr = s_prec[pi];
+                cu = pr.y + s_ps[pi];
+                ie = pr.w;
+            }
+            o.inst_cu[idx] = cu;
+            if (i < E) o.inst_expert[u * E + i] = ie;
+            u += step_u;
+            i += step_i;
+            if (i >= E1) {
+                i -= E1;
+                ++u;
+            }
+        }
+    }
+
+    route_passes<STAGED, KEY_BITS>(d, ids, o, src, f0, len, s_ex0, s_ex1, s_prec, s_ps, s_bkt,
+                                   s_cnt, s_ids, NP, nat_m, fp_m, shift);
+}
+
+// -------------------------------------------------------------- plan_fused
+// plan_global and plan_routes in one launch: every work-group runs the
+// global phases for itself in LDS, then its chunk's routes. It saves the
+// launch boundary between the two and the prologue in which plan_routes
+// stages the global tables from the workspace; the loads the work-group
+// needs (expert totals, chunk offsets, its ids) go out together at the
+// start. Used when its LDS fits (the global and the per-route tables side
+// by side).
+__host__ __device__ inline size_t fused_lds_ints(int E, int R, int T) {
+    const size_t PM = (size_t)E + R + 1;
+    return (size_t)4 * E + 4 * PM + (size_t)4 * E + (size_t)kRouteWaves * E + kBuckets +
+           (T <= kStageIds ? T : 0) + (size_t)4 * E + global_lds_ints(E, R);
+}
+
+static_assert(kRouteThreads == kGlobalThreads, "the global phases assume their block size");
+
+// Two work-groups per CU (8 waves per SIMD) when there are more chunks than
+// CUs: without the waves-per-EU bound the fused body took 106 scalar
+// registers, which leaves room for 7 waves per SIMD, i.e. one work-group.
+template <bool STAGED, int KEY_BITS>
+__global__ __launch_bounds__(kRouteThreads) __attribute__((amdgpu_waves_per_eu(8)))
+void plan_fused(PlanDims d, PlanWs w,
+                                                            const int* __restrict__ ids,
+                                                            PlanOut o) {
+    extern __shared__ int4 lds4[];  // 16-byte aligned base
+    const int E = d.E, R = d.R, C = d.C, m = d.m;
+    const int tid = threadIdx.x;
+    const int PM = E + R + 1;
+    int4* s_ex0 = lds4;          // [E] {qbase, q0, nsend, home}
+    int4* s_prec = s_ex0 + E;    // [PM] piece records
+    int4* s_ex1 = s_prec + PM;   // [E] {jbase, native recv base, native cu, recv base of local instance e}
+    int* s_cnt = (int*)(s_ex1 + E);        // [waves][E]
+    int* s_bkt = s_cnt + kRouteWaves * E;  // [kBuckets]
+    int* s_ids = s_bkt + kBuckets;         // [T] when STAGED
+    int* s_pre0 = s_ids + (STAGED ? d.T : 0);
+    int* s_pre1 = s_pre0 + E;
+    int* s_nsend = s_pre1 + E;
+    int* s_rcv = s_nsend + E;
+    const GlobalLds g = carve_global(s_rcv + E, E, R);
+    const FusedLds f{s_pre0, s_pre1, s_prec, s_nsend, s_rcv, s_bkt};
+
+    const int c = blockIdx.x;
+    const int src = c / d.cps, sub = c - src * d.cps;
+    const int f0 = src * C + sub * d.T;
+    const int f1 = min(f0 + d.T, (src + 1) * C);
+    const int len = f1 - f0;  // >= 1: a source's last chunk holds the rest of its C routes
+
+    // one round trip: expert e's total and its routes from source ranks
+    // below this chunk, below this source and below the next. The global
+    // phases need the routes below m and m + 1 only in this rank's own
+    // chunks (src == m), where they are the last two. The ids' loads go out
+    // after the LDS writes that wait for these, so that the wait does not
+    // include them; they are needed only after the global phases.
+    const int sn = min(src + 1, R - 1);
+    int cnt = 0, off = 0, pre0 = 0, pre1 = -1;
+    if (tid < E) {
+        cnt = w.cnt[tid];
+        off = w.chunk[c * E + tid];
+        pre0 = w.chunk[(src * d.cps) * E + tid];
+        const int nxt = w.chunk[(sn * d.cps) * E + tid];
+        if (src + 1 < R) pre1 = nxt;
+        s_pre0[tid] = pre0;
+        s_pre1[tid] = pre1 < 0 ? cnt : pre1;
+    }
+    int id_r[STAGED ? kIdRegs : 1];
+    if constexpr (STAGED) regs_load(id_r, ids + f0, len);
+
+    const PhaseScalars ps = global_phases<true>(d, w, o, g, f, cnt, pre0, pre1, src, sub);
+
+    for (int i = tid; i < kRouteWaves * E; i += kRouteThreads) s_cnt[i] = 0;
+    if constexpr (STAGED) regs_store(s_ids, id_r, len);
+    lds_barrier();
+
+    // per-expert records of this chunk (see plan_routes)
+    if (tid < E) {
+        const int e = tid;
+        const int h = home_of(e, R, E);
+        const int eex = g.eex[e], rbh = g.rb[h];
+        const int qbase = eex + off - rbh;
+        const int nrcv = h == m ? s_rcv[e - ps.ef_m] : 0;
+        s_ex0[e] = make_int4(qbase, off - pre0, s_nsend[e], h);
+        s_ex1[e] = make_int4(g.uex[h] + qbase - C, nrcv, min(eex - rbh, C), s_rcv[e]);
+    }
+
+    // this block's slice of the instance tables inst_cu [R][E+1] and
+    // inst_expert [R][E], idx = u*(E+1) + i
+    {
+        const int E1 = E + 1;
+        const int per = (R * E1 + gridDim.x - 1) / gridDim.x;
+        const int lo = min(blockIdx.x * per, R * E1), hi = min(lo + per, R * E1);
+        for (int idx = lo + tid; idx < hi; idx += kRouteThreads) {
+            const int u = idx / E1, i = idx - u * E1;
+            const int ef = g.ef[u], nat = g.ef[u + 1] - ef;
+            int cu = C, ie = -1;
+            if (i < nat) {
+                ie = ef + i;
+                cu = min(g.eex[ie] - g.rb[u], C);
+            } else if (i < nat + g.np[u]) {
+                const int pi = g.fp[u] + i - nat;
+                const int4 pr = s_prec[pi];
+                cu = pr.y + g.pst[pi];
+                ie = pr.w;
+            }
+            o.inst_cu[idx] = cu;
+            if (i < E) o.inst_expert[u * E + i] = ie;
+        }
+    }
+
+    // the records above are read after the first pass's barriers
+    route_passes<STAGED, KEY_BITS>(d, ids, o, src, f0, len, s_ex0, s_ex1, s_prec, g.pst, s_bkt,
+                                   s_cnt, s_ids, ps.NP, ps.nat_m, ps.fp_m, ps.shift);
+}
+
 // ------------------------------------------------------------------- host
 bool plan_dims(int R, int E, int S, int K, int m, PlanDims* d) {
     if (R < 1 || R > kMaxR || E < 1 || E > kMaxE || S < 1 || K < 1) return false;
@@ -903,8 +1221,10 @@ size_t global_lds_bytes(const PlanDims& d) { return global_lds_ints(d.E, d.R) * 
 
 size_t routes_lds_bytes(const PlanDims& d) { return routes_lds_ints(d.E, d.R, d.T) * sizeof(int); }
 
+size_t fused_lds_bytes(const PlanDims& d) { return fused_lds_ints(d.E, d.R, d.T) * sizeof(int); }
+
 bool lds_ready() {
-    // Allow the two single-pass kernels to use more than 64 KiB of LDS when
+    // Allow the single-pass kernels to use more than 64 KiB of LDS when
     // the sizes call for it (gfx950 has 160 KiB per CU).
     static const bool ok = [] {
         const int lim = (int)kMaxLds;
@@ -913,7 +1233,10 @@ bool lds_ready() {
                                         lim) == hipSuccess;
         for (const void* k : {(const void*)plan_routes<true, 8>, (const void*)plan_routes<true, kKeyBits>,
                               (const void*)plan_routes<false, 8>,
-                              (const void*)plan_routes<false, kKeyBits>})
+                              (const void*)plan_routes<false, kKeyBits>,
+                              (const void*)plan_fused<true, 8>, (const void*)plan_fused<true, kKeyBits>,
+                              (const void*)plan_fused<false, 8>,
+                              (const void*)plan_fused<false, kKeyBits>})
             good = hipFuncSetAttribute(k, hipFuncAttributeMaxDynamicSharedMemorySize, lim) ==
                        hipSuccess &&
                    good;
@@ -976,8 +1299,10 @@ int plan_launch(const PlanDims& d, char* ws, const int32_t* topk_ids, const Plan
     w.recvbase = (int*)(ws + off.recvbase);
     w.rinfo = (int4*)(ws + off.rinfo);
     w.scal = (int*)(ws + off.scal);
-    const size_t glds = global_lds_bytes(d), rlds = routes_lds_bytes(d);
-    if ((glds > 64 * 1024 || rlds > 64 * 1024) && !lds_ready()) return MEP_ERR_HIP;
+    const size_t glds = global_lds_bytes(d), rlds = routes_lds_bytes(d), flds = fused_lds_bytes(d);
+    const bool fused = flds <= kMaxLds;
+    const size_t big = fused ? flds : std::max(glds, rlds);
+    if (big > 64 * 1024 && !lds_ready()) return MEP_ERR_HIP;
 
     hipLaunchKernelGGL(plan_hist, dim3(d.nchunks), dim3(kHistThreads), d.E * sizeof(int), s, d,
                        (const int*)topk_ids, w.chunk);
@@ -985,11 +1310,22 @@ int plan_launch(const PlanDims& d, char* ws, const int32_t* topk_ids, const Plan
     hipLaunchKernelGGL(plan_scan, dim3((d.E + kScanExperts - 1) / kScanExperts),
                        dim3(kScanThreads), 0, s, d, w.chunk, w.cnt);
     MEP_LAUNCH_CHECK();
-    hipLaunchKernelGGL(plan_global, dim3(1), dim3(kGlobalThreads), glds, s, d, w, o);
-    MEP_LAUNCH_CHECK();
     // expert ids below 256 need 8 ballots in the multi-split, not 10
     const dim3 rg(d.nchunks), rb(kRouteThreads);
     const int* ids = (const int*)topk_ids;
+    if (fused) {
+        if (d.T <= kStageIds) {
+            if (d.E <= 256) hipLaunchKernelGGL((plan_fused<true, 8>), rg, rb, flds, s, d, w, ids, o);
+            else hipLaunchKernelGGL((plan_fused<true, kKeyBits>), rg, rb, flds, s, d, w, ids, o);
+        } else {
+            if (d.E <= 256) hipLaunchKernelGGL((plan_fused<false, 8>), rg, rb, flds, s, d, w, ids, o);
+            else hipLaunchKernelGGL((plan_fused<false, kKeyBits>), rg, rb, flds, s, d, w, ids, o);
+        }
+        MEP_LAUNCH_CHECK();
+        return MEP_OK;
+    }
+    hipLaunchKernelGGL(plan_global, dim3(1), dim3(kGlobalThreads), glds, s, d, w, o);
+    MEP_LAUNCH_CHECK();
     if (d.T <= kStageIds) {
         if (d.E <= 256) hipLaunchKernelGGL((plan_routes<true, 8>), rg, rb, rlds, s, d, w, ids, o);
         else hipLaunchKernelGGL((plan_routes<true, kKeyBits>), rg, rb, rlds, s, d, w, ids, o);
