@@ -8,22 +8,26 @@
 // C routes; the rest spill, in the same order, to the under-loaded ranks in
 // ascending rank order, filling each to exactly C.
 //
-// GPU design (four launches, all deterministic, no host sync):
+// GPU design (three launches, all deterministic, no host sync):
 //   plan_hist    one block per chunk of T routes (chunks never straddle a
 //                source rank): per-chunk expert histogram in LDS.
 //   plan_scan    one block per 8 experts: exclusive scan of each expert's
 //                column over the chunks, so chunk c knows how many routes of
 //                expert e precede it in (expert, f) order.
-//   plan_global  one block: expert offsets, native loads, surplus/deficit
-//                scans, the redundant instances (the pieces that the ordered
-//                excess list forms against the ordered deficit list, found by
-//                a merge-path style co-rank with binary searches), instance
-//                tables, and per-instance bases for this rank's send and
-//                receive maps.
-//   plan_routes  one block per chunk: stable within-chunk rank of each route
-//                among equal experts (per-wave ballot multi-split plus
-//                cross-wave offsets), then the closed-form destination and
-//                slot and the send/receive positions.
+//   plan_fused   one block per chunk. First the global phases, in the
+//                block's own LDS: expert offsets, native loads,
+//                surplus/deficit scans, the redundant instances (the pieces
+//                that the ordered excess list forms against the ordered
+//                deficit list, found by a merge-path style co-rank with
+//                binary searches), instance tables, and per-instance bases
+//                for this rank's send and receive maps. Then the chunk's
+//                routes: stable within-chunk rank of each route among equal
+//                experts (per-wave ballot multi-split plus cross-wave
+//                offsets), the closed-form destination and slot and the
+//                send/receive positions.
+// Where the fused block's LDS does not fit, the two halves run as separate
+// launches: plan_global (one block, tables to the workspace) and
+// plan_routes (one block per chunk).
 // Closed forms used by plan_routes. With p the route's position in
 // (expert, f) order, r its home rank and rb[r] the first position of rank r:
 //   q = p - rb[r];  q < C  -> (r, q)

@@ -61,15 +61,22 @@ def test_plan_workloads(orc, name):
         check_plan(d["topk_ids"], R, E, S, K, ranks[-1], got)
 
 
+# Shapes whose tables fit one work-group's LDS beside the route tables run
+# the one-launch form (plan_fused); E near 1000 runs plan_global and
+# plan_routes. Both forms are covered with staged ids (chunks up to 2048
+# routes) and ids read from global memory, with 8- and 10-bit keys.
 CASES = [
     # (R, E, S, K, skew): ragged chunks, E <= R, one rank, one expert per rank
     (1, 1, 5, 1, 0.0), (1, 7, 300, 3, 1.0), (2, 2, 3, 2, 0.0), (3, 50, 700, 3, 2.0),
     (4, 4, 129, 1, 3.0), (6, 3, 200, 1, 1.0), (5, 1, 64, 1, 0.0), (16, 64, 333, 4, 1.5),
     (64, 256, 40, 8, 1.0), (7, 1024, 150, 16, 0.5), (33, 100, 77, 5, 2.5),
     (128, 1000, 20, 8, 1.0), (1024, 1024, 3, 2, 1.0), (2, 1024, 5000, 2, 3.0),
-    # chunks above 2048 routes with experts above 256: ids read from global
-    # memory (not staged) and 10-bit keys in the wave multi-split
+    # two-launch form, chunks above 2048 routes (ids read from global
+    # memory) and 10-bit keys in the wave multi-split
     (64, 1024, 2560, 8, 1.0),
+    # one-launch form with experts above 256 (10-bit keys): staged ids, and
+    # 4096-route chunks read from global memory
+    (8, 384, 1024, 8, 1.0), (64, 300, 2048, 16, 1.0),
 ]
 
 
