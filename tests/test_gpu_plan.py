@@ -77,6 +77,8 @@ CASES = [
     # one-launch form with experts above 256 (10-bit keys): staged ids, and
     # 4096-route chunks read from global memory
     (8, 384, 1024, 8, 1.0), (64, 300, 2048, 16, 1.0),
+    # five chunks per source, the last one ragged
+    (8, 64, 1149, 4, 1.5),
 ]
 
 
