@@ -294,6 +294,106 @@ struct PhaseScalars {
     int NP, ef_m, nat_m, fp_m, nim, shift;
 };
 
+// F. instance counts and gid bases (written to the outputs when `out`).
+// Returns the instance total NI, after a closing barrier.
+__device__ __forceinline__ int instance_bases(const GlobalLds& g, const PlanOut& o, int R, bool out,
+                                              int* scr) {
+    const int tid = threadIdx.x;
+    int ic = 0;
+    if (tid < R) {
+        ic = g.ef[tid + 1] - g.ef[tid] + g.np[tid];
+        if (out) o.inst_count[tid] = ic;
+    }
+    int NI, gb = 0;
+    if (R <= kWave) {
+        if (tid < kWave) gb = wave0_exclusive_sum(ic, &NI);
+    } else {
+        gb = block_exclusive_sum<false>(ic, scr, &NI);
+    }
+    if (tid < R) {
+        g.gid[tid] = gb;
+        if (out) o.inst_gid_base[tid] = gb;
+    }
+    if (tid == 0) {
+        g.gid[R] = NI;
+        if (out) o.inst_gid_base[R] = NI;
+    }
+    lds_barrier();
+    return g.gid[R];
+}
+
+// H. send bases of this rank: instances in gid order = (dest, slot) order;
+// c_m(I) = this rank's routes inside instance I. Writes each native
+// instance's base to nsend, each piece's record to prec and each
+// destination's first row to g.sbase (no closing barrier). A thread's items
+// (at most 3: NI <= 2E + R - 1) keep what the first pass found for the
+// second, which would otherwise repeat the dependent LDS lookups after the
+// scan's barriers.
+__device__ __forceinline__ void send_bases(const GlobalLds& g, int R, int NI, int* nsend,
+                                           int4* prec, int* scr) {
+    const int tid = threadIdx.x, NT = blockDim.x;
+    const int ipt = (NI + NT - 1) / NT;
+    const int g0 = min(tid * ipt, NI), g1 = min(g0 + ipt, NI);
+    int hq0[kItemCache], hcm[kItemCache], hpi[kItemCache], he[kItemCache], hfirst[kItemCache];
+    auto counts = [&](int gi, int* q0, int* cm, int* pi_out, int* e_out, int* first) {
+        const int u = upper_bound(g.gid, R + 1, gi) - 1;
+        int e, P, n, pi;
+        inst_of(g, u, gi - g.gid[u], &e, &P, &n, &pi);
+        const int Hm = g.prem1[e] - g.prem[e];
+        *q0 = clampi(P - g.eex[e] - g.prem[e], 0, Hm);
+        *cm = clampi(P + n - g.eex[e] - g.prem[e], 0, Hm) - *q0;
+        *pi_out = pi;
+        *e_out = e;
+        *first = gi == g.gid[u] ? u : -1;
+    };
+    int sum = 0;
+#pragma unroll
+    for (int k = 0; k < kItemCache; ++k) {
+        hcm[k] = 0;
+        if (g0 + k < g1) counts(g0 + k, &hq0[k], &hcm[k], &hpi[k], &he[k], &hfirst[k]);
+        sum += hcm[k];
+    }
+    for (int gi = g0 + kItemCache; gi < g1; ++gi) {
+        int q0, cm, pi, e, first;
+        counts(gi, &q0, &cm, &pi, &e, &first);
+        sum += cm;
+    }
+    int tot;
+    int run = block_exclusive_sum<false>(sum, scr, &tot);
+    auto place = [&](int q0, int cm, int pi, int e, int first) {
+        if (pi < 0) {
+            nsend[e] = run - q0;
+        } else {
+            const int host = g.phost[pi];
+            prec[pi] = make_int4(host, g.L[host] - g.dex[host], run - q0, g.pexp[pi]);
+        }
+        if (first >= 0) g.sbase[first] = run;
+        run += cm;
+    };
+#pragma unroll
+    for (int k = 0; k < kItemCache; ++k)
+        if (g0 + k < g1) place(hq0[k], hcm[k], hpi[k], he[k], hfirst[k]);
+    for (int gi = g0 + kItemCache; gi < g1; ++gi) {
+        int q0, cm, pi, e, first;
+        counts(gi, &q0, &cm, &pi, &e, &first);
+        place(q0, cm, pi, e, first);
+    }
+    if (tid == 0) g.sbase[R] = tot;
+}
+
+// J. bucket table: bkt[b] = the piece holding excess index b << shift, so
+// that a route finds its piece with one lookup and a short walk. Returns
+// shift.
+__device__ __forceinline__ int bucket_table(const GlobalLds& g, int NP, int totU, int* bkt) {
+    int shift = 0;
+    while (((long long)kBuckets << shift) < totU) ++shift;
+    for (int b = threadIdx.x; b < kBuckets; b += blockDim.x) {
+        const long long start = (long long)b << shift;
+        bkt[b] = start < totU ? upper_bound(g.pst, NP, (int)start) - 1 : max(NP - 1, 0);
+    }
+    return shift;
+}
+
 // Phases F to J of a plan_fused work-group (see global_phases). Only this
 // rank's own chunks place routes with the send bases of phase H; the
 // others take the piece records' host, slot base and expert alone. Phase I
@@ -310,86 +410,17 @@ __device__ __forceinline__ PhaseScalars fused_tail(const PlanDims& d, const Plan
     int* scr0 = g.scratch;
     int* scr1 = g.scratch + 2 * (kGlobalThreads / kWave + 1);
 
-    // F. instance counts and gid bases
-    int ic = 0;
-    if (tid < R) {
-        ic = g.ef[tid + 1] - g.ef[tid] + g.np[tid];
-        if (out_block) o.inst_count[tid] = ic;
-    }
-    int NI, gb = 0;
-    if (R <= kWave) {
-        if (tid < kWave) gb = wave0_exclusive_sum(ic, &NI);
-    } else {
-        gb = block_exclusive_sum<false>(ic, scr0, &NI);
-    }
-    if (tid < R) {
-        g.gid[tid] = gb;
-        if (out_block) o.inst_gid_base[tid] = gb;
-    }
-    if (tid == 0) {
-        g.gid[R] = NI;
-        if (out_block) o.inst_gid_base[R] = NI;
-    }
-    lds_barrier();
-    NI = g.gid[R];
+    const int NI = instance_bases(g, o, R, out_block, scr0);  // F
 
-    // H. send bases of this rank: instances in gid order = (dest, slot)
-    //    order; c_m(I) = this rank's routes inside instance I. A thread's
-    //    first kItemCache items keep what the first pass found for the
-    //    second.
+    // H. send bases (this rank's own chunks); elsewhere the piece records
+    //    without them
     if (src != m) {
         for (int pi = tid; pi < NP; pi += NT) {
             const int host = g.phost[pi];
             f.prec[pi] = make_int4(host, g.L[host] - g.dex[host], 0, g.pexp[pi]);
         }
     } else {
-        const int ipt = (NI + NT - 1) / NT;
-        const int g0 = min(tid * ipt, NI), g1 = min(g0 + ipt, NI);
-        int hq0[kItemCache], hcm[kItemCache], hpi[kItemCache], he[kItemCache], hfirst[kItemCache];
-        auto counts = [&](int gi, int* q0o, int* cm, int* pi_out, int* e_out, int* first) {
-            const int u = upper_bound(g.gid, R + 1, gi) - 1;
-            int e, P, n, pi;
-            inst_of(g, u, gi - g.gid[u], &e, &P, &n, &pi);
-            const int Hm = g.prem1[e] - g.prem[e];
-            *q0o = clampi(P - g.eex[e] - g.prem[e], 0, Hm);
-            *cm = clampi(P + n - g.eex[e] - g.prem[e], 0, Hm) - *q0o;
-            *pi_out = pi;
-            *e_out = e;
-            *first = gi == g.gid[u] ? u : -1;
-        };
-        int sum = 0;
-#pragma unroll
-        for (int k = 0; k < kItemCache; ++k) {
-            hcm[k] = 0;
-            if (g0 + k < g1) counts(g0 + k, &hq0[k], &hcm[k], &hpi[k], &he[k], &hfirst[k]);
-            sum += hcm[k];
-        }
-        for (int gi = g0 + kItemCache; gi < g1; ++gi) {
-            int a, cm, pi, e, first;
-            counts(gi, &a, &cm, &pi, &e, &first);
-            sum += cm;
-        }
-        int tot;
-        int run = block_exclusive_sum<false>(sum, scr1, &tot);
-        auto place = [&](int a, int cm, int pi, int e, int first) {
-            if (pi < 0) {
-                f.nsend[e] = run - a;
-            } else {
-                const int host = g.phost[pi];
-                f.prec[pi] = make_int4(host, g.L[host] - g.dex[host], run - a, g.pexp[pi]);
-            }
-            if (first >= 0) g.sbase[first] = run;
-            run += cm;
-        };
-#pragma unroll
-        for (int k = 0; k < kItemCache; ++k)
-            if (g0 + k < g1) place(hq0[k], hcm[k], hpi[k], he[k], hfirst[k]);
-        for (int gi = g0 + kItemCache; gi < g1; ++gi) {
-            int a, cm, pi, e, first;
-            counts(gi, &a, &cm, &pi, &e, &first);
-            place(a, cm, pi, e, first);
-        }
-        if (tid == 0) g.sbase[R] = tot;
+        send_bases(g, R, NI, f.nsend, f.prec, scr1);
     }
 
     // I. one source: local instance i of m (thread i; nim <= E <= NT)
@@ -420,14 +451,8 @@ __device__ __forceinline__ PhaseScalars fused_tail(const PlanDims& d, const Plan
     if (src == m && sub == 0)
         for (int r = tid; r < R; r += NT) o.send_count[r] = g.sbase[r + 1] - g.sbase[r];
 
-    // J. bucket table: a route finds its piece with one lookup and a short
-    //    walk (piece starts are read from g.pst in place)
-    int shift = 0;
-    while (((long long)kBuckets << shift) < totU) ++shift;
-    for (int b = tid; b < kBuckets; b += NT) {
-        const long long start = (long long)b << shift;
-        f.bkt[b] = start < totU ? upper_bound(g.pst, NP, (int)start) - 1 : max(NP - 1, 0);
-    }
+    // J. (piece starts are read from g.pst in place)
+    const int shift = bucket_table(g, NP, totU, f.bkt);
     return PhaseScalars{NP, ef_m, nat_m, g.fp[m], nim, shift};
 }
 
@@ -611,87 +636,13 @@ __device__ __forceinline__ PhaseScalars global_phases(const PlanDims& d, const P
 
     if constexpr (FUSED) return fused_tail(d, o, g, f, NP, totU, src, sub);
 
-    // F. instance counts and gid bases
-    int ic = 0;
-    if (tid < R) {
-        ic = g.ef[tid + 1] - g.ef[tid] + g.np[tid];
-        o.inst_count[tid] = ic;
-    }
-    int NI, gb = 0;
-    if (R <= kWave) {
-        if (tid < kWave) gb = wave0_exclusive_sum(ic, &NI);
-    } else {
-        gb = block_exclusive_sum<false>(ic, scr0, &NI);
-    }
-    if (tid < R) {
-        g.gid[tid] = gb;
-        o.inst_gid_base[tid] = gb;
-    }
-    if (tid == 0) {
-        g.gid[R] = NI;
-        o.inst_gid_base[R] = NI;
-    }
-    lds_barrier();
-    NI = g.gid[R];
+    const int NI = instance_bases(g, o, R, true, scr0);  // F
 
     // G. per-rank instance layout for the table fill done by plan_routes
     for (int u = tid; u < R; u += NT)
         w.rinfo[u] = make_int4(g.ef[u], g.ef[u + 1] - g.ef[u], g.np[u], g.fp[u]);
 
-    // H. send bases of this rank: instances in gid order = (dest, slot)
-    //    order; c_m(I) = this rank's routes inside instance I. A thread's
-    //    items (at most 3: NI <= 2E + R - 1) keep what the first pass found
-    //    for the second, which would otherwise repeat the dependent LDS
-    //    lookups after the scan's barriers.
-    {
-        const int ipt = (NI + NT - 1) / NT;
-        const int g0 = min(tid * ipt, NI), g1 = min(g0 + ipt, NI);
-        int hq0[kItemCache], hcm[kItemCache], hpi[kItemCache], he[kItemCache], hfirst[kItemCache];
-        auto counts = [&](int gi, int* q0, int* cm, int* pi_out, int* e_out, int* first) {
-            const int u = upper_bound(g.gid, R + 1, gi) - 1;
-            int e, P, n, pi;
-            inst_of(g, u, gi - g.gid[u], &e, &P, &n, &pi);
-            const int Hm = g.prem1[e] - g.prem[e];
-            *q0 = clampi(P - g.eex[e] - g.prem[e], 0, Hm);
-            *cm = clampi(P + n - g.eex[e] - g.prem[e], 0, Hm) - *q0;
-            *pi_out = pi;
-            *e_out = e;
-            *first = gi == g.gid[u] ? u : -1;
-        };
-        int sum = 0;
-#pragma unroll
-        for (int k = 0; k < kItemCache; ++k) {
-            hcm[k] = 0;
-            if (g0 + k < g1) counts(g0 + k, &hq0[k], &hcm[k], &hpi[k], &he[k], &hfirst[k]);
-            sum += hcm[k];
-        }
-        for (int gi = g0 + kItemCache; gi < g1; ++gi) {
-            int q0, cm, pi, e, first;
-            counts(gi, &q0, &cm, &pi, &e, &first);
-            sum += cm;
-        }
-        int tot;
-        int run = block_exclusive_sum<false>(sum, scr1, &tot);
-        auto place = [&](int q0, int cm, int pi, int e, int first) {
-            if (pi < 0) {
-                w.nsend[e] = run - q0;
-            } else {
-                const int host = g.phost[pi];
-                w.prec[pi] = make_int4(host, g.L[host] - g.dex[host], run - q0, g.pexp[pi]);
-            }
-            if (first >= 0) g.sbase[first] = run;
-            run += cm;
-        };
-#pragma unroll
-        for (int k = 0; k < kItemCache; ++k)
-            if (g0 + k < g1) place(hq0[k], hcm[k], hpi[k], he[k], hfirst[k]);
-        for (int gi = g0 + kItemCache; gi < g1; ++gi) {
-            int q0, cm, pi, e, first;
-            counts(gi, &q0, &cm, &pi, &e, &first);
-            place(q0, cm, pi, e, first);
-        }
-        if (tid == 0) g.sbase[R] = tot;
-    }
+    send_bases(g, R, NI, w.nsend, w.prec, scr1);  // H
 
     // I. receive bases of this rank: items (source, local instance i) in
     //    arrival order; recvbase = sources' rows before the item minus the
@@ -751,16 +702,9 @@ __device__ __forceinline__ PhaseScalars global_phases(const PlanDims& d, const P
         o.recv_count[r] = g.roff[r + 1] - g.roff[r];
     }
 
-    // J. tables the per-route kernel stages: piece starts, and a bucket table
-    //    so that a route finds its piece with one lookup and a short walk
-
-    int shift = 0;
-    while (((long long)kBuckets << shift) < totU) ++shift;
+    // J. tables the per-route kernel stages: piece starts and the bucket table
     for (int i = tid; i <= NP; i += NT) w.pstart[i] = g.pst[i];
-    for (int b = tid; b < kBuckets; b += NT) {
-        const long long start = (long long)b << shift;
-        w.bucket[b] = start < totU ? upper_bound(g.pst, NP, (int)start) - 1 : max(NP - 1, 0);
-    }
+    const int shift = bucket_table(g, NP, totU, w.bucket);
     if (tid == 0) {
         w.scal[SC_NP] = NP;
         w.scal[SC_EFIRST_M] = ef_m;
