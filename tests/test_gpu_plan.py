@@ -174,3 +174,21 @@ def test_plan_weight_rows(orc, name):
         w = cba.plan_weight_rows(p, R, E, slots)
         torch.cuda.synchronize()
         assert np.array_equal(host(w), orc.weight_rows(ref, R, E, slots)), slots
+
+
+def test_plan_random_shapes(orc):
+    """Forty seeded shapes across both plan forms (E up to 1024, R up to 96,
+    ragged chunks, skewed and flat routing), each at one random rank."""
+    require_gpu()
+    shapes = np.random.default_rng(20261204)
+    for case in range(40):
+        R = int(shapes.integers(1, 97))
+        E = int(shapes.integers(1, 1025))
+        K = int(shapes.integers(1, min(E, 16) + 1))
+        S = min(int(shapes.integers(1, max(2, 300000 // (R * K)))), 2000)
+        skew = float(shapes.choice([0.0, 1.0, 2.5]))
+        m = int(shapes.integers(0, R))
+        ids = _rand_ids(np.random.default_rng(case), R, E, S, K, skew)
+        note(f"plan random case {case}: R={R} E={E} S={S} K={K} skew={skew} m={m}")
+        _assert_same(orc.plan(ids, R, E, S, K, m=m), _gpu_plan(ids, R, E, S, K, m),
+                     f"case {case} R={R} E={E} S={S} K={K} m={m}")
