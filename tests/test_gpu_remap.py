@@ -149,3 +149,45 @@ def test_prune_order_vectors(orc):
                           pruning_threshold=thr)
     _cmp(ref, got, "prune product rounding")
     assert got["balanced_mask"].tolist() == [[0, 0, 1], [0, 0, 1]]
+
+
+def test_random_shapes(orc):
+    """Thirty seeded shapes: BS, K, E, F, world size and instances per card
+    drawn over their limits, both modes, all three scale types, with and
+    without the active mask and the send map."""
+    require_gpu()
+    rng = np.random.default_rng(20261205)
+    for case in range(30):
+        ws = int(rng.integers(1, 1025))
+        ppr = int(rng.integers(1, max(2, 1024 // ws + 1)))
+        ppr = min(ppr, 1024 // ws)
+        E = int(rng.integers(1, 1025))
+        K = int(rng.integers(1, min(E, 16) + 1))
+        BS = int(rng.integers(1, 513))
+        F = int(rng.integers(2, min(ws + 1, 17) + 1))
+        n_inst = ws * ppr
+        table = np.zeros((E, F), np.int32)
+        table[:, 0] = rng.integers(1, F, E)
+        for e in range(E):
+            table[e, 1:] = rng.choice(n_inst, F - 1, replace=n_inst < F - 1)
+        ids = np.argsort(rng.random((BS, E)), axis=1)[:, :K].astype(np.int32)
+        mode = int(rng.integers(0, 2))
+        rank = int(rng.integers(0, ws))
+        sdt = str(rng.choice(["fp32", "bf16", "fp16"]))
+        v = -np.sort(-rng.random((BS, K)).astype(np.float32), axis=1)
+        v /= v.sum(axis=1, keepdims=True)
+        sc = {"fp32": v, "bf16": synth.bf16_from_f32_trunc(v),
+              "fp16": v.astype(np.float16).view(np.uint16)}[sdt]
+        thr = rng.uniform(0, 0.3, K).astype(np.float32)
+        active = (rng.random(BS) < 0.9).astype(np.uint8) if rng.random() < 0.5 else None
+        want_send = bool(rng.random() < 0.8)
+        prune = bool(rng.random() < 0.8)
+        note(f"remap random case {case}: BS={BS} K={K} E={E} F={F} ws={ws} ppr={ppr} "
+             f"mode={mode} rank={rank} {sdt} prune={prune} active={active is not None}")
+        kw = dict(expert_scales=sc, scale_dtype=sdt, pruning_threshold=thr,
+                  active_mask=active) if prune else {}
+        ref = orc.remap_prune(ids, table, ws, ppr, rank, mode, want_send=want_send, **kw)
+        got = _gpu(ids, table, ws, ppr, rank, mode, scales=sc if prune else None, sdt=sdt,
+                   thr=thr if prune else None, active=active if prune else None,
+                   want_send=want_send)
+        _cmp(ref, got, f"case {case}")
