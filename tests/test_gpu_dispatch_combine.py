@@ -207,6 +207,34 @@ def test_row_kernels_odd_shapes(orc, T, K, H):
     _check_combine(orc, raw, sp, sc, f"T={T} K={K} H={H}")
 
 
+def test_row_kernels_random_shapes(orc):
+    # twenty-four seeded (T, K, H) with random skip rates: pack and grouping
+    # bit-exact, both combine outputs bit-exact
+    torch = require_gpu()
+    import combine_balancing_amd as cba
+    shapes = np.random.default_rng(20261206)
+    for case in range(24):
+        T = int(shapes.integers(1, 301))
+        K = int(shapes.integers(1, 25))
+        H = 8 * int(shapes.integers(1, 2049))
+        skip = float(shapes.choice([0.0, 0.1, 0.5]))
+        rng = np.random.default_rng(case)
+        x = synth.bf16_normal(rng, (T, H))
+        sp = rng.permutation(T * K).astype(np.int32)
+        sp[rng.random(T * K) < skip] = -1
+        note(f"row kernels random case {case}: T={T} K={K} H={H} skip={skip}")
+        sb, _ = cba.dispatch(K, x=dev(x), send_pos=dev(sp))
+        torch.cuda.synchronize()
+        assert np.array_equal(host(sb), orc.pack(x, sp, K)), f"pack case {case}"
+        raw = synth.bf16_normal(rng, (T * K, H))
+        rp = rng.permutation(T * K).astype(np.int32)
+        _, rg = cba.dispatch(K, recv_raw=dev(raw), recv_pos=dev(rp))
+        torch.cuda.synchronize()
+        assert np.array_equal(host(rg), orc.group(raw, rp)), f"group case {case}"
+        sc = rng.standard_normal((T, K)).astype(np.float32)
+        _check_combine(orc, raw, sp, sc, f"random case {case} T={T} K={K} H={H}")
+
+
 def test_short_buffers_bound_the_maps(orc):
     # a map naming rows past the end of its buffer (a plan map paired with a
     # dedup-sized buffer): the pack skips stores past send_buf's rows and the
