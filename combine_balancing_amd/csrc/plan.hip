@@ -59,6 +59,9 @@ constexpr int kItemCache = 4;  // plan_global: per-thread items kept between two
 constexpr int kRouteThreads = 1024;  // work-group of plan_routes
 constexpr int kMinChunk = 1024;      // routes per chunk (at least)
 constexpr int kRouteWaves = kRouteThreads / kWave;
+// plan_fused work-group: 1024 threads, or 512 when there are more chunks
+// than CUs and the chunks are short (see plan_launch)
+constexpr int kFusedThreadsSmall = 512;
 constexpr int kMaxR = 1024;
 static_assert(kMaxChunks >= kMaxR, "a source rank holds at least one chunk");
 static_assert(kTargetChunks <= kMaxChunks, "chunk target within the scan's capacity");
@@ -749,19 +752,19 @@ constexpr int kPmRegs = (kMaxE + kMaxR + 1 + kRouteThreads - 1) / kRouteThreads;
 constexpr int kBktRegs = (kBuckets + kRouteThreads - 1) / kRouteThreads;
 constexpr int kIdRegs = (kStageIds + kRouteThreads - 1) / kRouteThreads;
 
-// v[u] = src[min(u * kRouteThreads + tid, n - 1)]; needs 1 <= n.
-template <int U, typename T>
+// v[u] = src[min(u * NT + tid, n - 1)]; needs 1 <= n.
+template <int NT, int U, typename T>
 __device__ __forceinline__ void regs_load(T (&v)[U], const T* __restrict__ src, int n) {
 #pragma unroll
-    for (int u = 0; u < U; ++u) v[u] = src[min(u * kRouteThreads + (int)threadIdx.x, n - 1)];
+    for (int u = 0; u < U; ++u) v[u] = src[min(u * NT + (int)threadIdx.x, n - 1)];
 }
 
-// dst[i] = v[u] for i = u * kRouteThreads + tid < n.
-template <int U, typename T>
+// dst[i] = v[u] for i = u * NT + tid < n.
+template <int NT, int U, typename T>
 __device__ __forceinline__ void regs_store(T* dst, const T (&v)[U], int n) {
 #pragma unroll
     for (int u = 0; u < U; ++u) {
-        const int i = u * kRouteThreads + (int)threadIdx.x;
+        const int i = u * NT + (int)threadIdx.x;
         if (i < n) dst[i] = v[u];
     }
 }
@@ -780,7 +783,7 @@ __host__ __device__ inline size_t routes_lds_ints(int E, int R, int T) {
 // s_prec, the bucket table s_bkt, zeroed per-wave counters s_cnt and, when
 // STAGED, the chunk's ids in s_ids. The chunk is routes [f0, f0 + len) of
 // source rank src.
-template <bool STAGED, int KEY_BITS>
+template <bool STAGED, int KEY_BITS, int NT>
 __device__ __forceinline__ void route_passes(const PlanDims& d, const int* __restrict__ ids,
                                              const PlanOut& o, int src, int f0, int len,
                                              const int4* s_ex0, const int4* s_ex1,
@@ -792,7 +795,7 @@ __device__ __forceinline__ void route_passes(const PlanDims& d, const int* __res
     const int PM = E + R + 1;
     const int wave = tid / kWave;
     const int lane = tid & (kWave - 1);
-    const int seg = (((len + kRouteWaves - 1) / kRouteWaves) + kWave - 1) & ~(kWave - 1);
+    const int seg = (((len + (NT / kWave) - 1) / (NT / kWave)) + kWave - 1) & ~(kWave - 1);
     const int a = min(wave * seg, len);
     const int b = min(a + seg, len);
     int* my_cnt = s_cnt + wave * E;
@@ -815,10 +818,10 @@ __device__ __forceinline__ void route_passes(const PlanDims& d, const int* __res
         }
     }
     lds_barrier();
-    for (int e = tid; e < E; e += kRouteThreads) {
+    for (int e = tid; e < E; e += NT) {
         int run = 0;
 #pragma unroll 4
-        for (int v = 0; v < kRouteWaves; ++v) {
+        for (int v = 0; v < (NT / kWave); ++v) {
             const int t = s_cnt[v * E + e];
             s_cnt[v * E + e] = run;
             run += t;
@@ -927,10 +930,10 @@ __global__ __launch_bounds__(kRouteThreads) void plan_routes(PlanDims d, PlanWs 
     // the staged tables' loads go out first (their LDS writes follow below)
     int ps_r[kPmRegs], bk_r[kBktRegs], id_r[STAGED ? kIdRegs : 1];
     i32x4 pr_r[kPmRegs];
-    regs_load(ps_r, w.pstart, PM);
-    regs_load(pr_r, (const i32x4*)w.prec, PM);
-    regs_load(bk_r, w.bucket, kBuckets);
-    if constexpr (STAGED) regs_load(id_r, ids + f0, len);
+    regs_load<kRouteThreads>(ps_r, w.pstart, PM);
+    regs_load<kRouteThreads>(pr_r, (const i32x4*)w.prec, PM);
+    regs_load<kRouteThreads>(bk_r, w.bucket, kBuckets);
+    if constexpr (STAGED) regs_load<kRouteThreads>(id_r, ids + f0, len);
     // this block's share of the instance tables (filled after the barrier):
     // its first rank record joins this round trip
     const int E1 = E + 1;
@@ -962,10 +965,10 @@ __global__ __launch_bounds__(kRouteThreads) void plan_routes(PlanDims d, PlanWs 
         s_ex1[e] = make_int4(w.uex[h] + qbase - C, nrcv, min(eex - rbh, C), rcv);
     }
     for (int i = tid; i < kRouteWaves * E; i += kRouteThreads) s_cnt[i] = 0;
-    regs_store(s_ps, ps_r, PM);
-    regs_store((i32x4*)s_prec, pr_r, PM);
-    regs_store(s_bkt, bk_r, kBuckets);
-    if constexpr (STAGED) regs_store(s_ids, id_r, len);
+    regs_store<kRouteThreads>(s_ps, ps_r, PM);
+    regs_store<kRouteThreads>((i32x4*)s_prec, pr_r, PM);
+    regs_store<kRouteThreads>(s_bkt, bk_r, kBuckets);
+    if constexpr (STAGED) regs_store<kRouteThreads>(s_ids, id_r, len);
     lds_barrier();
 
     // this block's slice of the instance tables inst_cu [R][E+1] and
@@ -996,8 +999,9 @@ __global__ __launch_bounds__(kRouteThreads) void plan_routes(PlanDims d, PlanWs 
         }
     }
 
-    route_passes<STAGED, KEY_BITS>(d, ids, o, src, f0, len, s_ex0, s_ex1, s_prec, s_ps, s_bkt,
-                                   s_cnt, s_ids, NP, nat_m, fp_m, shift);
+    route_passes<STAGED, KEY_BITS, kRouteThreads>(d, ids, o, src, f0, len, s_ex0, s_ex1, s_prec,
+                                                  s_ps, s_bkt, s_cnt, s_ids, NP, nat_m, fp_m,
+                                                  shift);
 }
 
 // -------------------------------------------------------------- plan_fused
@@ -1008,19 +1012,19 @@ __global__ __launch_bounds__(kRouteThreads) void plan_routes(PlanDims d, PlanWs 
 // needs (expert totals, chunk offsets, its ids) go out together at the
 // start. Used when its LDS fits (the global and the per-route tables side
 // by side).
-__host__ __device__ inline size_t fused_lds_ints(int E, int R, int T) {
+__host__ __device__ inline size_t fused_lds_ints(int E, int R, int T, int NT) {
     const size_t PM = (size_t)E + R + 1;
-    return (size_t)4 * E + 4 * PM + (size_t)4 * E + (size_t)kRouteWaves * E + kBuckets +
+    return (size_t)4 * E + 4 * PM + (size_t)4 * E + (size_t)(NT / kWave) * E + kBuckets +
            (T <= kStageIds ? T : 0) + (size_t)4 * E + global_lds_ints(E, R);
 }
 
-static_assert(kRouteThreads == kGlobalThreads, "the global phases assume their block size");
+static_assert(kRouteThreads <= kGlobalThreads, "the global phases' scan scratch covers the block");
 
 // Two work-groups per CU (8 waves per SIMD) when there are more chunks than
 // CUs: without the waves-per-EU bound the fused body took 106 scalar
 // registers, which leaves room for 7 waves per SIMD, i.e. one work-group.
-template <bool STAGED, int KEY_BITS>
-__global__ __launch_bounds__(kRouteThreads) __attribute__((amdgpu_waves_per_eu(8)))
+template <bool STAGED, int KEY_BITS, int NT>
+__global__ __launch_bounds__(NT) __attribute__((amdgpu_waves_per_eu(8)))
 void plan_fused(PlanDims d, PlanWs w,
                                                             const int* __restrict__ ids,
                                                             PlanOut o) {
@@ -1032,7 +1036,7 @@ void plan_fused(PlanDims d, PlanWs w,
     int4* s_prec = s_ex0 + E;    // [PM] piece records
     int4* s_ex1 = s_prec + PM;   // [E] {jbase, native recv base, native cu, recv base of local instance e}
     int* s_cnt = (int*)(s_ex1 + E);        // [waves][E]
-    int* s_bkt = s_cnt + kRouteWaves * E;  // [kBuckets]
+    int* s_bkt = s_cnt + (NT / kWave) * E;  // [kBuckets]
     int* s_ids = s_bkt + kBuckets;         // [T] when STAGED
     int* s_pre0 = s_ids + (STAGED ? d.T : 0);
     int* s_pre1 = s_pre0 + E;
@@ -1064,13 +1068,13 @@ void plan_fused(PlanDims d, PlanWs w,
         s_pre0[tid] = pre0;
         s_pre1[tid] = pre1 < 0 ? cnt : pre1;
     }
-    int id_r[STAGED ? kIdRegs : 1];
-    if constexpr (STAGED) regs_load(id_r, ids + f0, len);
+    int id_r[STAGED ? ((kStageIds + NT - 1) / NT) : 1];
+    if constexpr (STAGED) regs_load<NT>(id_r, ids + f0, len);
 
     const PhaseScalars ps = global_phases<true>(d, w, o, g, f, cnt, pre0, pre1, src, sub);
 
-    for (int i = tid; i < kRouteWaves * E; i += kRouteThreads) s_cnt[i] = 0;
-    if constexpr (STAGED) regs_store(s_ids, id_r, len);
+    for (int i = tid; i < (NT / kWave) * E; i += NT) s_cnt[i] = 0;
+    if constexpr (STAGED) regs_store<NT>(s_ids, id_r, len);
     lds_barrier();
 
     // per-expert records of this chunk (see plan_routes)
@@ -1090,7 +1094,7 @@ void plan_fused(PlanDims d, PlanWs w,
         const int E1 = E + 1;
         const int per = (R * E1 + gridDim.x - 1) / gridDim.x;
         const int lo = min(blockIdx.x * per, R * E1), hi = min(lo + per, R * E1);
-        for (int idx = lo + tid; idx < hi; idx += kRouteThreads) {
+        for (int idx = lo + tid; idx < hi; idx += NT) {
             const int u = idx / E1, i = idx - u * E1;
             const int ef = g.ef[u], nat = g.ef[u + 1] - ef;
             int cu = C, ie = -1;
@@ -1109,8 +1113,9 @@ void plan_fused(PlanDims d, PlanWs w,
     }
 
     // the records above are read after the first pass's barriers
-    route_passes<STAGED, KEY_BITS>(d, ids, o, src, f0, len, s_ex0, s_ex1, s_prec, g.pst, s_bkt,
-                                   s_cnt, s_ids, ps.NP, ps.nat_m, ps.fp_m, ps.shift);
+    route_passes<STAGED, KEY_BITS, NT>(d, ids, o, src, f0, len, s_ex0, s_ex1, s_prec,
+                                                  g.pst, s_bkt, s_cnt, s_ids, ps.NP, ps.nat_m,
+                                                  ps.fp_m, ps.shift);
 }
 
 // ------------------------------------------------------------------- host
@@ -1169,7 +1174,21 @@ size_t global_lds_bytes(const PlanDims& d) { return global_lds_ints(d.E, d.R) * 
 
 size_t routes_lds_bytes(const PlanDims& d) { return routes_lds_ints(d.E, d.R, d.T) * sizeof(int); }
 
-size_t fused_lds_bytes(const PlanDims& d) { return fused_lds_ints(d.E, d.R, d.T) * sizeof(int); }
+// plan_fused's block size: 512 threads when the chunks outnumber the CUs
+// (two or more work-groups per CU) and are short enough to stage, else
+// 1024. Measured: a 524288-route plan with E=384 in 512 chunks of 1024
+// routes took 25.3 us with 512 threads against 27.1 us with 1024; the
+// 262144-route plan in 256 chunks 23.5 against 23.2 us, and the 4M-route
+// plan in 512 chunks of 8192 routes 46.0 against 43.4 us.
+int fused_threads(const PlanDims& d) {
+    const bool small = d.nchunks > 256 && d.T <= kStageIds && d.E <= kFusedThreadsSmall &&
+                       d.R <= kFusedThreadsSmall;
+    return small ? kFusedThreadsSmall : kRouteThreads;
+}
+
+size_t fused_lds_bytes(const PlanDims& d) {
+    return fused_lds_ints(d.E, d.R, d.T, fused_threads(d)) * sizeof(int);
+}
 
 bool lds_ready() {
     // Allow the single-pass kernels to use more than 64 KiB of LDS when
@@ -1182,9 +1201,12 @@ bool lds_ready() {
         for (const void* k : {(const void*)plan_routes<true, 8>, (const void*)plan_routes<true, kKeyBits>,
                               (const void*)plan_routes<false, 8>,
                               (const void*)plan_routes<false, kKeyBits>,
-                              (const void*)plan_fused<true, 8>, (const void*)plan_fused<true, kKeyBits>,
-                              (const void*)plan_fused<false, 8>,
-                              (const void*)plan_fused<false, kKeyBits>})
+                              (const void*)plan_fused<true, 8, kRouteThreads>,
+                              (const void*)plan_fused<true, kKeyBits, kRouteThreads>,
+                              (const void*)plan_fused<false, 8, kRouteThreads>,
+                              (const void*)plan_fused<false, kKeyBits, kRouteThreads>,
+                              (const void*)plan_fused<true, 8, kFusedThreadsSmall>,
+                              (const void*)plan_fused<true, kKeyBits, kFusedThreadsSmall>})
             good = hipFuncSetAttribute(k, hipFuncAttributeMaxDynamicSharedMemorySize, lim) ==
                        hipSuccess &&
                    good;
@@ -1248,7 +1270,10 @@ int plan_launch(const PlanDims& d, char* ws, const int32_t* topk_ids, const Plan
     w.rinfo = (int4*)(ws + off.rinfo);
     w.scal = (int*)(ws + off.scal);
     const size_t glds = global_lds_bytes(d), rlds = routes_lds_bytes(d), flds = fused_lds_bytes(d);
-    const bool fused = flds <= kMaxLds;
+    // the fused work-group runs the global phases with one element per
+    // thread
+    const int fnt = fused_threads(d);
+    const bool fused = flds <= kMaxLds && d.E <= fnt && d.R <= fnt;
     const size_t big = fused ? flds : std::max(glds, rlds);
     if (big > 64 * 1024 && !lds_ready()) return MEP_ERR_HIP;
 
@@ -1259,15 +1284,19 @@ int plan_launch(const PlanDims& d, char* ws, const int32_t* topk_ids, const Plan
                        dim3(kScanThreads), 0, s, d, w.chunk, w.cnt);
     MEP_LAUNCH_CHECK();
     // expert ids below 256 need 8 ballots in the multi-split, not 10
-    const dim3 rg(d.nchunks), rb(kRouteThreads);
+    const dim3 rg(d.nchunks), rb(kRouteThreads), fb(fnt);
     const int* ids = (const int*)topk_ids;
     if (fused) {
-        if (d.T <= kStageIds) {
-            if (d.E <= 256) hipLaunchKernelGGL((plan_fused<true, 8>), rg, rb, flds, s, d, w, ids, o);
-            else hipLaunchKernelGGL((plan_fused<true, kKeyBits>), rg, rb, flds, s, d, w, ids, o);
+        constexpr int NS = kFusedThreadsSmall, NL = kRouteThreads;
+        if (fnt == NS) {  // staged ids only
+            if (d.E <= 256) hipLaunchKernelGGL((plan_fused<true, 8, NS>), rg, fb, flds, s, d, w, ids, o);
+            else hipLaunchKernelGGL((plan_fused<true, kKeyBits, NS>), rg, fb, flds, s, d, w, ids, o);
+        } else if (d.T <= kStageIds) {
+            if (d.E <= 256) hipLaunchKernelGGL((plan_fused<true, 8, NL>), rg, fb, flds, s, d, w, ids, o);
+            else hipLaunchKernelGGL((plan_fused<true, kKeyBits, NL>), rg, fb, flds, s, d, w, ids, o);
         } else {
-            if (d.E <= 256) hipLaunchKernelGGL((plan_fused<false, 8>), rg, rb, flds, s, d, w, ids, o);
-            else hipLaunchKernelGGL((plan_fused<false, kKeyBits>), rg, rb, flds, s, d, w, ids, o);
+            if (d.E <= 256) hipLaunchKernelGGL((plan_fused<false, 8, NL>), rg, fb, flds, s, d, w, ids, o);
+            else hipLaunchKernelGGL((plan_fused<false, kKeyBits, NL>), rg, fb, flds, s, d, w, ids, o);
         }
         MEP_LAUNCH_CHECK();
         return MEP_OK;

@@ -64,7 +64,9 @@ def test_plan_workloads(orc, name):
 # Shapes whose tables fit one work-group's LDS beside the route tables run
 # the one-launch form (plan_fused); E near 1000 runs plan_global and
 # plan_routes. Both forms are covered with staged ids (chunks up to 2048
-# routes) and ids read from global memory, with 8- and 10-bit keys.
+# routes) and ids read from global memory, with 8- and 10-bit keys; the
+# fused form in 512-thread groups (more than 256 short chunks) by the
+# imbalance sweep, the case below and some of the random shapes.
 CASES = [
     # (R, E, S, K, skew): ragged chunks, E <= R, one rank, one expert per rank
     (1, 1, 5, 1, 0.0), (1, 7, 300, 3, 1.0), (2, 2, 3, 2, 0.0), (3, 50, 700, 3, 2.0),
@@ -79,6 +81,8 @@ CASES = [
     (8, 384, 1024, 8, 1.0), (64, 300, 2048, 16, 1.0),
     # five chunks per source, the last one ragged
     (8, 64, 1149, 4, 1.5),
+    # more chunks than CUs, short ones: the fused form in 512-thread groups
+    (64, 256, 600, 8, 1.0),
 ]
 
 
