@@ -47,11 +47,15 @@ namespace {
 
 constexpr int kHistThreads = 256;
 constexpr int kMaxChunks = 1024;  // column length of the expert scan (>= the rank limit)
-// Chunks grow until there are at most 512 (or one per source rank when R is
-// larger). A 4M-route plan ran 48.0 us with 1024 chunks of 4096 routes and
-// 45.2 us with 512 of 8192 (the per-chunk kernels then fit the GPU in one
-// wave of work-groups).
-constexpr int kTargetChunks = 512;
+// Chunks grow until there are at most 256 while they stay short enough to
+// stage their ids (2048 routes), then until there are at most 512 (or one
+// per source rank when R is larger). Measured on the fused plan: a
+// 524288-route plan (R=8, E=384) took 24.4 us with 256 chunks of 2048
+// routes against 25.3 us with 512 of 1024; a 4M-route plan 43.4 us with
+// 512 chunks of 8192 routes against 49.7 us with 256 of 16384 (and, in the
+// four-launch form, 45.2 against 48.0 us with 1024 of 4096).
+constexpr int kTargetChunks = 256;
+constexpr int kTargetChunksLong = 512;
 constexpr int kBuckets = 1024;  // piece lookup: excess index >> shift -> first piece
 constexpr size_t kMaxLds = 160 * 1024;  // LDS a gfx950 work-group may allocate
 constexpr int kGlobalThreads = 1024;
@@ -64,7 +68,7 @@ constexpr int kRouteWaves = kRouteThreads / kWave;
 constexpr int kFusedThreadsSmall = 512;
 constexpr int kMaxR = 1024;
 static_assert(kMaxChunks >= kMaxR, "a source rank holds at least one chunk");
-static_assert(kTargetChunks <= kMaxChunks, "chunk target within the scan's capacity");
+static_assert(kTargetChunksLong <= kMaxChunks, "chunk target within the scan's capacity");
 constexpr int kMaxE = 1024;
 constexpr int kStageIds = 2048;  // chunk sizes up to this keep their ids in LDS (plan_routes)
 
@@ -1132,7 +1136,8 @@ bool plan_dims(int R, int E, int S, int K, int m, PlanDims* d) {
     d->C = (int)C;
     d->N = (int)N;
     long long T = kMinChunk;
-    while (T < C && (long long)R * ((C + T - 1) / T) > kTargetChunks) T *= 2;
+    while (T < C && T < kStageIds && (long long)R * ((C + T - 1) / T) > kTargetChunks) T *= 2;
+    while (T < C && (long long)R * ((C + T - 1) / T) > kTargetChunksLong) T *= 2;
     d->T = (int)std::min<long long>(T, C);
     d->cps = (int)((C + d->T - 1) / d->T);
     d->nchunks = R * d->cps;
@@ -1198,8 +1203,7 @@ bool lds_ready() {
         bool good = hipFuncSetAttribute((const void*)plan_global,
                                         hipFuncAttributeMaxDynamicSharedMemorySize,
                                         lim) == hipSuccess;
-        for (const void* k : {(const void*)plan_routes<true, 8>, (const void*)plan_routes<true, kKeyBits>,
-                              (const void*)plan_routes<false, 8>,
+        for (const void* k : {(const void*)plan_routes<true, kKeyBits>,
                               (const void*)plan_routes<false, kKeyBits>,
                               (const void*)plan_fused<true, 8, kRouteThreads>,
                               (const void*)plan_fused<true, kKeyBits, kRouteThreads>,
@@ -1303,13 +1307,12 @@ int plan_launch(const PlanDims& d, char* ws, const int32_t* topk_ids, const Plan
     }
     hipLaunchKernelGGL(plan_global, dim3(1), dim3(kGlobalThreads), glds, s, d, w, o);
     MEP_LAUNCH_CHECK();
-    if (d.T <= kStageIds) {
-        if (d.E <= 256) hipLaunchKernelGGL((plan_routes<true, 8>), rg, rb, rlds, s, d, w, ids, o);
-        else hipLaunchKernelGGL((plan_routes<true, kKeyBits>), rg, rb, rlds, s, d, w, ids, o);
-    } else {
-        if (d.E <= 256) hipLaunchKernelGGL((plan_routes<false, 8>), rg, rb, rlds, s, d, w, ids, o);
-        else hipLaunchKernelGGL((plan_routes<false, kKeyBits>), rg, rb, rlds, s, d, w, ids, o);
-    }
+    // only E above 256 reaches the two-launch form (with E <= 256 the fused
+    // tables fit for every R up to the limit), so its keys are 10-bit
+    if (d.T <= kStageIds)
+        hipLaunchKernelGGL((plan_routes<true, kKeyBits>), rg, rb, rlds, s, d, w, ids, o);
+    else
+        hipLaunchKernelGGL((plan_routes<false, kKeyBits>), rg, rb, rlds, s, d, w, ids, o);
     MEP_LAUNCH_CHECK();
     return MEP_OK;
 }

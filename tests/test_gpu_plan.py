@@ -82,7 +82,7 @@ CASES = [
     # five chunks per source, the last one ragged
     (8, 64, 1149, 4, 1.5),
     # more chunks than CUs, short ones: the fused form in 512-thread groups
-    (64, 256, 600, 8, 1.0),
+    (300, 128, 125, 8, 1.0), (300, 300, 125, 8, 1.0),
 ]
 
 
