@@ -28,7 +28,7 @@ constexpr int kMaxK = 16;
 constexpr int kMaxEntries = kMaxBS * kMaxK;
 constexpr int kPerThread = kMaxEntries / kRemapThreads;
 constexpr int kCountWaves = kRemapWaves;  // waves that build the send map
-constexpr int kStageTable = kCountWaves * kMaxInst;  // eplb_table entries kept in LDS
+constexpr int kStageTable = 9216;  // eplb_table entries kept in LDS (36 KiB)
 
 struct RemapArgs {
     int BS, K, E, F, ws, ppr, rank, mode, scale_dtype;
@@ -61,13 +61,11 @@ __device__ __forceinline__ float scale_value(uint32_t raw, int dtype) {
 // made them generic loads, which wait on both memory counters).
 template <bool TAB_STAGED>
 __global__ __launch_bounds__(kRemapThreads) void remap_prune_kernel(RemapArgs a) {
-    // s_tab is dead once the ids are remapped; the send-map counters reuse
-    // its space.
-    __shared__ int s_region[kCountWaves * kMaxInst];
-    int* s_tab = s_region;                            // [kStageTable] eplb_table, when it fits
-    int* s_cnt = s_region;                            // [kCountWaves][n_inst] send-map counts
-    __shared__ int s_bal[kMaxEntries];                // remapped ids
-    __shared__ uint8_t s_keep[kMaxEntries];           // prune mask
+    // The send-map counters have their own space, so they are cleared while
+    // the first loads are in flight.
+    __shared__ int s_tab[kStageTable];                // eplb_table, when it fits
+    __shared__ int s_cnt[kCountWaves * kMaxInst];     // [kCountWaves][n_inst] send-map counts
+    __shared__ int16_t s_inst[kMaxEntries];           // kept route's instance, else -1
     __shared__ float s_sc[kMaxK * (kMaxBS + 1)];      // scales as fp32, [k][t] skewed by one
     __shared__ float s_sum[kMaxBS];                   // per-token threshold sums
     __shared__ uint8_t s_act[kMaxBS];
@@ -107,6 +105,9 @@ __global__ __launch_bounds__(kRemapThreads) void remap_prune_kernel(RemapArgs a)
             }
         }
     }
+    // the send-map counters are cleared while the loads above are in flight
+    if (a.send_pos)
+        for (int i = tid; i < kCountWaves * n_inst; i += kRemapThreads) s_cnt[i] = 0;
     if (TAB_STAGED) stage<kRemapThreads, kStageTable / kRemapThreads>(s_tab, a.table, tab_n);
     if (pruning && tid < a.K) s_thr[tid] = a.thr[tid];
     if (tid < a.BS) s_act[tid] = (pruning && a.active) ? (a.active[tid] != 0) : 1;
@@ -162,15 +163,12 @@ __global__ __launch_bounds__(kRemapThreads) void remap_prune_kernel(RemapArgs a)
             pruning ? (uint8_t)(s_act[t] && !(s_sc[(i - t * a.K) * S1 + t] < s_sum[t])) : (uint8_t)1;
         a.out_ids[i] = bal;
         a.out_mask[i] = keep;
-        s_bal[i] = bal;
-        s_keep[i] = keep;
+        s_inst[i] = (int16_t)(keep && (unsigned)bal < (unsigned)n_inst ? bal : -1);
     }
     if (!a.send_pos) return;
 
     // 4. send map: stable counting sort of kept routes by instance; the
     //    first kCountWaves waves each own a contiguous range of entries
-    lds_barrier();  // s_cnt reuses the table's space read just above
-    for (int i = tid; i < kCountWaves * n_inst; i += kRemapThreads) s_cnt[i] = 0;
     lds_barrier();
     const int wave = tid / kWave;
     const int lane = tid & (kWave - 1);
@@ -179,23 +177,28 @@ __global__ __launch_bounds__(kRemapThreads) void remap_prune_kernel(RemapArgs a)
     const int hi = wave < kCountWaves ? min(lo + seg, n) : n;
     int* my_cnt = s_cnt + min(wave, kCountWaves - 1) * n_inst;
     for (int i = lo + lane; i < hi; i += kWave) {
-        const int inst = s_bal[i];
-        if (s_keep[i] && (unsigned)inst < (unsigned)n_inst) atomicAdd(&my_cnt[inst], 1);
+        const int inst = s_inst[i];
+        if (inst >= 0) atomicAdd(&my_cnt[inst], 1);
     }
     lds_barrier();
-    // per-instance totals, then exclusive offsets in (instance, wave) order
+    // per-instance totals, then exclusive offsets in (instance, wave) order;
+    // an instance's wave counts are read once and kept for the offsets
     int tot = 0;
-    if (tid < n_inst)
-        for (int v = 0; v < kCountWaves; ++v) tot += s_cnt[v * n_inst + tid];
+    int wc[kCountWaves];
+#pragma unroll
+    for (int v = 0; v < kCountWaves; ++v) {
+        wc[v] = tid < n_inst ? s_cnt[v * n_inst + tid] : 0;
+        tot += wc[v];
+    }
     int all;
     const int base = block_exclusive_sum<false>(tot, scratch, &all);  // scratch is not reused
     if (tid < n_inst) {
         s_tot[tid] = tot;
         int run = base;
+#pragma unroll
         for (int v = 0; v < kCountWaves; ++v) {
-            const int c = s_cnt[v * n_inst + tid];
             s_cnt[v * n_inst + tid] = run;
-            run += c;
+            run += wc[v];
         }
     }
     lds_barrier();
@@ -207,8 +210,8 @@ __global__ __launch_bounds__(kRemapThreads) void remap_prune_kernel(RemapArgs a)
     for (int b0 = lo; b0 < hi; b0 += kWave) {
         const int i = b0 + lane;
         bool valid = i < hi;
-        int inst = valid ? s_bal[i] : 0;
-        valid = valid && s_keep[i] && (unsigned)inst < (unsigned)n_inst;
+        int inst = valid ? s_inst[i] : -1;
+        valid = inst >= 0;
         if (!valid) inst = 0;
         const uint64_t peers = match_peers(inst, valid);
         const int below = count_below(peers);
