@@ -28,7 +28,7 @@
 // Where the fused block's LDS does not fit, the two halves run as separate
 // launches: plan_global (one block, tables to the workspace) and
 // plan_routes (one block per chunk).
-// Closed forms used by plan_routes. With p the route's position in
+// Closed forms used by the route passes. With p the route's position in
 // (expert, f) order, r its home rank and rb[r] the first position of rank r:
 //   q = p - rb[r];  q < C  -> (r, q)
 //   else j = Uex[r] + q - C is the route's index in the global excess list;
@@ -64,7 +64,7 @@ constexpr int kRouteThreads = 1024;  // work-group of plan_routes
 constexpr int kMinChunk = 1024;      // routes per chunk (at least)
 constexpr int kRouteWaves = kRouteThreads / kWave;
 // plan_fused work-group: 1024 threads, or 512 when there are more chunks
-// than CUs and the chunks are short (see plan_launch)
+// than CUs and the chunks are short (see fused_threads)
 constexpr int kFusedThreadsSmall = 512;
 constexpr int kMaxR = 1024;
 static_assert(kMaxChunks >= kMaxR, "a source rank holds at least one chunk");
