@@ -90,17 +90,24 @@ __global__ __launch_bounds__(kMaxTpr) void group_rows(const u32x4* __restrict__ 
     if ((unsigned)from >= (unsigned)n_raw) return;
     const u32x4* src = raw + (size_t)from * nvec;
     u32x4* dst = out + (size_t)t * nvec;
-    for (int v0 = 0; v0 < nvec; v0 += tpr * VPT) {
-        u32x4 q[VPT];
+    if constexpr (VPT == 1) {
+        // tpr >= nvec here (one vector per thread covers the row): no loop.
+        // The single-pass loop it replaces cost 2 us of 147 on the dsv3
+        // grouping (probe on the real map).
+        if (tid < nvec) __builtin_nontemporal_store(__builtin_nontemporal_load(src + tid), dst + tid);
+    } else {
+        for (int v0 = 0; v0 < nvec; v0 += tpr * VPT) {
+            u32x4 q[VPT];
 #pragma unroll
-        for (int i = 0; i < VPT; ++i) {
-            const int v = v0 + i * tpr + tid;
-            if (v < nvec) q[i] = __builtin_nontemporal_load(src + v);
-        }
+            for (int i = 0; i < VPT; ++i) {
+                const int v = v0 + i * tpr + tid;
+                if (v < nvec) q[i] = __builtin_nontemporal_load(src + v);
+            }
 #pragma unroll
-        for (int i = 0; i < VPT; ++i) {
-            const int v = v0 + i * tpr + tid;
-            if (v < nvec) __builtin_nontemporal_store(q[i], dst + v);
+            for (int i = 0; i < VPT; ++i) {
+                const int v = v0 + i * tpr + tid;
+                if (v < nvec) __builtin_nontemporal_store(q[i], dst + v);
+            }
         }
     }
 }
