@@ -10,10 +10,13 @@
 // contiguous segment per card.
 //
 // One work-group does the whole call (BS*K is at most a few thousand
-// entries, so this is latency-bound): a strided pass computes ids and
-// masks; the send map is a stable counting sort by instance built from
-// per-wave LDS counts and a ballot multi-split (no atomics decide an
-// order, so the output is deterministic).
+// entries, so this is latency-bound). Each wave owns a contiguous range of
+// entries. One pass computes their ids and masks and, for the send map,
+// each kept route's rank among the wave's earlier routes to the same
+// instance (a ballot multi-split per 64 entries and a running per-wave
+// count in LDS). A block scan over the (instance, wave) counts then gives
+// every wave's base per instance. No atomics decide an order, so the
+// output is deterministic.
 #include "mep_device.h"
 
 namespace mep {
@@ -26,8 +29,7 @@ constexpr int kMaxE = 1024;
 constexpr int kMaxBS = 512;
 constexpr int kMaxK = 16;
 constexpr int kMaxEntries = kMaxBS * kMaxK;
-constexpr int kPerThread = kMaxEntries / kRemapThreads;
-constexpr int kCountWaves = kRemapWaves;  // waves that build the send map
+constexpr int kMaxBatches = kMaxEntries / kRemapThreads;  // 64-entry batches per wave, at most
 constexpr int kStageTable = 9216;  // eplb_table entries kept in LDS (36 KiB)
 
 struct RemapArgs {
@@ -50,22 +52,24 @@ __device__ __forceinline__ float scale_value(uint32_t raw, int dtype) {
     return (float)__builtin_bit_cast(_Float16, (uint16_t)raw);
 }
 
-// Entry i = t*K + k of the thread's r-th slot: i = tid + r * kRemapThreads
-// (coalesced loads and stores). Token and column indices use exact
-// multiply-shift reciprocals instead of integer divisions: t = (i*kmag) >> 21
-// for i < 8192 and K <= 16, and t / count = (t*m) >> 20 for t < 512 and
-// count <= 1024, with kmag = ceil(2^21/K) and m = ceil(2^20/count).
+// Entry i = t*K + k of the thread's r-th slot: i = lo + r * 64 + lane, where
+// wave w owns entries [lo, hi) = [w*seg, w*seg + seg) clipped to n and seg
+// is n/16 rounded up to a multiple of 64, at most NB batches (every access
+// of a wave covers 64 consecutive entries). Token and column indices use
+// exact multiply-shift reciprocals instead of integer divisions:
+// t = (i*kmag) >> 21 for i < 8192 and K <= 16, and t / count = (t*m) >> 20
+// for t < 512 and count <= 1024, with kmag = ceil(2^21/K) and
+// m = ceil(2^20/count).
 // TAB_STAGED: the table fits the LDS stage (E*F <= kStageTable) and is read
 // from LDS; otherwise from global memory. A compile-time choice keeps the
 // table reads plain LDS loads (a pointer chosen at run time between the two
 // made them generic loads, which wait on both memory counters).
-template <bool TAB_STAGED>
+template <bool TAB_STAGED, int NB>
 __global__ __launch_bounds__(kRemapThreads) void remap_prune_kernel(RemapArgs a) {
     // The send-map counters have their own space, so they are cleared while
     // the first loads are in flight.
     __shared__ int s_tab[kStageTable];                // eplb_table, when it fits
-    __shared__ int s_cnt[kCountWaves * kMaxInst];     // [kCountWaves][n_inst] send-map counts
-    __shared__ int16_t s_inst[kMaxEntries];           // kept route's instance, else -1
+    __shared__ int s_cnt[kRemapWaves * kMaxInst];     // [wave][n_inst] send-map counts, then bases
     __shared__ float s_sc[kMaxK * (kMaxBS + 1)];      // scales as fp32, [k][t] skewed by one
     __shared__ float s_sum[kMaxBS];                   // per-token threshold sums
     __shared__ uint8_t s_act[kMaxBS];
@@ -80,45 +84,63 @@ __global__ __launch_bounds__(kRemapThreads) void remap_prune_kernel(RemapArgs a)
     const int tab_n = a.E * a.F;
     const unsigned kmag = ((1u << 21) + a.K - 1) / a.K;
     const int S1 = a.BS + 1;
+    const int wave = tid / kWave;
+    const int lane = tid & (kWave - 1);
+    const int seg = (((n + kRemapWaves - 1) / kRemapWaves) + kWave - 1) & ~(kWave - 1);
+    const int lo = min(wave * seg, n);
+    const int hi = min(lo + seg, n);
 
-    // 1. one round trip: ids, scales, thresholds, the active mask and (when
-    //    it fits) the whole table
-    int e[kPerThread];
-    uint32_t raw[kPerThread];  // scale bit patterns; converted after every load is issued
+    // 1. one round trip: the table (when it fits), ids, scales, thresholds
+    //    and the active mask are all requested before any is used.
+    //  - The table goes straight from global memory into LDS (gfx950's
+    //    global_load_lds; each wave instruction fills 64 consecutive ints
+    //    at a wave-uniform LDS address), so it holds no registers.
+    //  - Ids and scales: NB batches per wave, unconditionally, at indices
+    //    clamped into range (a lane past the wave's entries reloads its last
+    //    one and never uses it). A load under a lane condition made the
+    //    compiler wait for it where the branches join.
+    if (TAB_STAGED)
+        for (int b = wave * kWave; b < tab_n; b += kRemapThreads)
+            if (b + lane < tab_n) __builtin_amdgcn_global_load_lds(a.table + b + lane, s_tab + b, 4, 0, 0);
+    const int last = max(hi - 1, 0);
+    int e[NB];
+    uint32_t raw[NB];  // scale bit patterns
 #pragma unroll
-    for (int r = 0; r < kPerThread; ++r) {
-        const int i = tid + r * kRemapThreads;
-        e[r] = i < n ? a.ids[i] : -1;
-    }
+    for (int r = 0; r < NB; ++r) e[r] = a.ids[min(lo + r * kWave + lane, last)];
     if (pruning) {
         if (a.scale_dtype == MEP_SCALE_F32) {
 #pragma unroll
-            for (int r = 0; r < kPerThread; ++r) {
-                const int i = tid + r * kRemapThreads;
-                raw[r] = i < n ? ((const uint32_t*)a.scales)[i] : 0u;
-            }
+            for (int r = 0; r < NB; ++r)
+                raw[r] = ((const uint32_t*)a.scales)[min(lo + r * kWave + lane, last)];
         } else {
 #pragma unroll
-            for (int r = 0; r < kPerThread; ++r) {
-                const int i = tid + r * kRemapThreads;
-                raw[r] = i < n ? ((const uint16_t*)a.scales)[i] : 0u;
-            }
+            for (int r = 0; r < NB; ++r)
+                raw[r] = ((const uint16_t*)a.scales)[min(lo + r * kWave + lane, last)];
         }
     }
+    float thr = 0.0f;
+    if (pruning) thr = a.thr[min(tid, a.K - 1)];
+    uint32_t act = 1u;
+    if (pruning && a.active) act = a.active[min(tid, a.BS - 1)];
     // the send-map counters are cleared while the loads above are in flight
     if (a.send_pos)
-        for (int i = tid; i < kCountWaves * n_inst; i += kRemapThreads) s_cnt[i] = 0;
-    if (TAB_STAGED) stage<kRemapThreads, kStageTable / kRemapThreads>(s_tab, a.table, tab_n);
-    if (pruning && tid < a.K) s_thr[tid] = a.thr[tid];
-    if (tid < a.BS) s_act[tid] = (pruning && a.active) ? (a.active[tid] != 0) : 1;
+        for (int i = tid; i < kRemapWaves * n_inst; i += kRemapThreads) s_cnt[i] = 0;
+    if (pruning && tid < a.K) s_thr[tid] = thr;
+    // opaque here, so the test below is not moved up to the load and its
+    // wait with it
+    asm volatile("" : "+v"(act));
+    if (tid < a.BS) s_act[tid] = act != 0;
     if (pruning) {
 #pragma unroll
-        for (int r = 0; r < kPerThread; ++r) {
-            const int i = tid + r * kRemapThreads;
+        for (int r = 0; r < NB; ++r) {
+            const int i = lo + r * kWave + lane;
             const int t = (int)(((unsigned)i * kmag) >> 21);
-            if (i < n) s_sc[(i - t * a.K) * S1 + t] = scale_value(raw[r], a.scale_dtype);
+            if (i < hi) s_sc[(i - t * a.K) * S1 + t] = scale_value(raw[r], a.scale_dtype);
         }
     }
+    // the table's LDS writes count on vmcnt: every wave's must be done
+    // before the barrier
+    if (TAB_STAGED) asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
     lds_barrier();
     const int* tab = TAB_STAGED ? s_tab : a.table;
 
@@ -140,53 +162,62 @@ __global__ __launch_bounds__(kRemapThreads) void remap_prune_kernel(RemapArgs a)
     }
     lds_barrier();
 
-    // 3. remap and mask every entry; outputs
+    // 3. remap and mask every entry; outputs. With a send map, each kept
+    //    route's rank among this wave's earlier routes to its instance: the
+    //    lowest lane of each equal-key group advances the wave's count.
+    const bool mapping = a.send_pos != nullptr;
+    int* my_cnt = s_cnt + wave * n_inst;
+    int inst[NB];
+    int rank[NB];
 #pragma unroll
-    for (int r = 0; r < kPerThread; ++r) {
-        const int i = tid + r * kRemapThreads;
-        if (i >= n) continue;
-        const int t = (int)(((unsigned)i * kmag) >> 21);
-        int bal = -1;
-        if ((unsigned)e[r] < (unsigned)a.E) {
-            const int* row = tab + (size_t)e[r] * a.F;
-            int col;
-            if (a.mode == 0) {
-                col = s_col[e[r]];
-            } else {
-                const int count = row[0];
-                col = count > 1 ? t - count * (int)(((unsigned)t * (unsigned)s_col[e[r]]) >> 20) + 1
-                                : 1;
+    for (int r = 0; r < NB; ++r) {
+        const int b0 = lo + r * kWave;
+        if (b0 >= hi) break;  // wave-uniform
+        const int i = b0 + lane;
+        int ins = -1;
+        if (i < hi) {
+            const int t = (int)(((unsigned)i * kmag) >> 21);
+            int bal = -1;
+            if ((unsigned)e[r] < (unsigned)a.E) {
+                const int* row = tab + (size_t)e[r] * a.F;
+                int col;
+                if (a.mode == 0) {
+                    col = s_col[e[r]];
+                } else {
+                    const int count = row[0];
+                    col = count > 1
+                              ? t - count * (int)(((unsigned)t * (unsigned)s_col[e[r]]) >> 20) + 1
+                              : 1;
+                }
+                bal = row[clampi(col, 1, a.F - 1)];
             }
-            bal = row[clampi(col, 1, a.F - 1)];
+            const uint8_t keep =
+                pruning ? (uint8_t)(s_act[t] && !(scale_value(raw[r], a.scale_dtype) < s_sum[t]))
+                        : (uint8_t)1;
+            a.out_ids[i] = bal;
+            a.out_mask[i] = keep;
+            if (keep && (unsigned)bal < (unsigned)n_inst) ins = bal;
         }
-        const uint8_t keep =
-            pruning ? (uint8_t)(s_act[t] && !(s_sc[(i - t * a.K) * S1 + t] < s_sum[t])) : (uint8_t)1;
-        a.out_ids[i] = bal;
-        a.out_mask[i] = keep;
-        s_inst[i] = (int16_t)(keep && (unsigned)bal < (unsigned)n_inst ? bal : -1);
+        inst[r] = ins;
+        if (mapping) {
+            const bool valid = ins >= 0;
+            const int key = valid ? ins : 0;
+            const uint64_t peers = match_peers(key, valid);
+            const int below = count_below(peers);
+            rank[r] = my_cnt[key] + below;
+            if (valid && below == 0) my_cnt[key] += __popcll(peers);
+        }
     }
-    if (!a.send_pos) return;
+    if (!mapping) return;
 
-    // 4. send map: stable counting sort of kept routes by instance; the
-    //    first kCountWaves waves each own a contiguous range of entries
+    // 4. send map: per-instance totals, then each wave's base per instance
+    //    in (instance, wave) order; an instance's wave counts are read once
+    //    and kept for the bases
     lds_barrier();
-    const int wave = tid / kWave;
-    const int lane = tid & (kWave - 1);
-    const int seg = (((n + kCountWaves - 1) / kCountWaves) + kWave - 1) & ~(kWave - 1);
-    const int lo = wave < kCountWaves ? min(wave * seg, n) : n;
-    const int hi = wave < kCountWaves ? min(lo + seg, n) : n;
-    int* my_cnt = s_cnt + min(wave, kCountWaves - 1) * n_inst;
-    for (int i = lo + lane; i < hi; i += kWave) {
-        const int inst = s_inst[i];
-        if (inst >= 0) atomicAdd(&my_cnt[inst], 1);
-    }
-    lds_barrier();
-    // per-instance totals, then exclusive offsets in (instance, wave) order;
-    // an instance's wave counts are read once and kept for the offsets
     int tot = 0;
-    int wc[kCountWaves];
+    int wc[kRemapWaves];
 #pragma unroll
-    for (int v = 0; v < kCountWaves; ++v) {
+    for (int v = 0; v < kRemapWaves; ++v) {
         wc[v] = tid < n_inst ? s_cnt[v * n_inst + tid] : 0;
         tot += wc[v];
     }
@@ -196,7 +227,7 @@ __global__ __launch_bounds__(kRemapThreads) void remap_prune_kernel(RemapArgs a)
         s_tot[tid] = tot;
         int run = base;
 #pragma unroll
-        for (int v = 0; v < kCountWaves; ++v) {
+        for (int v = 0; v < kRemapWaves; ++v) {
             s_cnt[v * n_inst + tid] = run;
             run += wc[v];
         }
@@ -207,17 +238,12 @@ __global__ __launch_bounds__(kRemapThreads) void remap_prune_kernel(RemapArgs a)
         for (int j = 0; j < a.ppr; ++j) c += s_tot[card * a.ppr + j];
         a.send_count[card] = c;
     }
-    for (int b0 = lo; b0 < hi; b0 += kWave) {
+#pragma unroll
+    for (int r = 0; r < NB; ++r) {
+        const int b0 = lo + r * kWave;
+        if (b0 >= hi) break;
         const int i = b0 + lane;
-        bool valid = i < hi;
-        int inst = valid ? s_inst[i] : -1;
-        valid = inst >= 0;
-        if (!valid) inst = 0;
-        const uint64_t peers = match_peers(inst, valid);
-        const int below = count_below(peers);
-        const int r = my_cnt[inst] + below;
-        if (valid && below == 0) my_cnt[inst] += __popcll(peers);  // the group's lowest lane
-        if (i < hi) a.send_pos[i] = valid ? r : -1;
+        if (i < hi) a.send_pos[i] = inst[r] >= 0 ? my_cnt[inst[r]] + rank[r] : -1;
     }
 }
 
@@ -251,12 +277,21 @@ extern "C" int mep_remap_prune(int BS, int K, int E, int F, int world_size, int 
     RemapArgs a{BS, K, E, F, world_size, place_per_rank, local_rank_id, balance_mode, scale_dtype,
                 (const int*)expert_ids, (const int*)eplb_table, expert_scales, pruning_threshold,
                 active_mask, (int*)balanced_ids, balanced_mask, (int*)send_pos, (int*)send_count};
-    if ((long long)E * F <= kStageTable)
-        hipLaunchKernelGGL(remap_prune_kernel<true>, dim3(1), dim3(kRemapThreads), 0,
-                           (hipStream_t)stream, a);
-    else
-        hipLaunchKernelGGL(remap_prune_kernel<false>, dim3(1), dim3(kRemapThreads), 0,
-                           (hipStream_t)stream, a);
+    // batches per wave (the kernel's seg / 64), rounded up to a power of two
+    const int n = BS * K;
+    const int nbat = ((n + kRemapWaves - 1) / kRemapWaves + kWave - 1) / kWave;
+    const int nb = nbat <= 1 ? 1 : nbat <= 2 ? 2 : nbat <= 4 ? 4 : kMaxBatches;
+    const bool staged = (long long)E * F <= kStageTable;
+    const dim3 g(1), b(kRemapThreads);
+    hipStream_t st = (hipStream_t)stream;
+    if (staged && nb == 1) hipLaunchKernelGGL((remap_prune_kernel<true, 1>), g, b, 0, st, a);
+    else if (staged && nb == 2) hipLaunchKernelGGL((remap_prune_kernel<true, 2>), g, b, 0, st, a);
+    else if (staged && nb == 4) hipLaunchKernelGGL((remap_prune_kernel<true, 4>), g, b, 0, st, a);
+    else if (staged) hipLaunchKernelGGL((remap_prune_kernel<true, kMaxBatches>), g, b, 0, st, a);
+    else if (nb == 1) hipLaunchKernelGGL((remap_prune_kernel<false, 1>), g, b, 0, st, a);
+    else if (nb == 2) hipLaunchKernelGGL((remap_prune_kernel<false, 2>), g, b, 0, st, a);
+    else if (nb == 4) hipLaunchKernelGGL((remap_prune_kernel<false, 4>), g, b, 0, st, a);
+    else hipLaunchKernelGGL((remap_prune_kernel<false, kMaxBatches>), g, b, 0, st, a);
     MEP_LAUNCH_CHECK();
     return MEP_OK;
 }

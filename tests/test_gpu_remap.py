@@ -191,3 +191,38 @@ def test_random_shapes(orc):
                    thr=thr if prune else None, active=active if prune else None,
                    want_send=want_send)
         _cmp(ref, got, f"case {case}")
+
+
+# The kernel is compiled for 1, 2, 4 or 8 batches of 64 entries per wave
+# (BS*K up to 1024, 2048, 4096 and 8192 over its 16 waves), each with the
+# table staged in LDS (E*F <= 9216) or read from global memory. Every
+# variant runs at the top of its range and on a ragged size inside it.
+VARIANT_CASES = [
+    # (BS, K, E, F): staged tables (E*F <= 9216), then tables in global memory
+    (64, 16, 600, 9), (7, 5, 600, 9), (128, 16, 700, 13), (65, 16, 700, 13),
+    (256, 16, 1000, 9), (129, 16, 1000, 9), (512, 16, 512, 17), (300, 15, 512, 17),
+    (64, 16, 1024, 10), (7, 5, 1024, 10), (128, 16, 1000, 12), (65, 16, 1000, 12),
+    (256, 16, 1024, 17), (129, 16, 1024, 17), (512, 16, 1024, 11), (300, 15, 1024, 11),
+]
+
+
+@pytest.mark.parametrize("BS,K,E,F", VARIANT_CASES)
+def test_batch_and_table_variants(orc, BS, K, E, F):
+    require_gpu()
+    rng = np.random.default_rng(BS * 131 + K * 17 + E + F)
+    ws, ppr = 300, 3
+    table = np.zeros((E, F), np.int32)
+    table[:, 0] = rng.integers(1, F, E)
+    for e in range(E):
+        table[e, 1:] = rng.choice(ws * ppr, F - 1, replace=False)
+    ids = np.argsort(rng.random((BS, E)), axis=1)[:, :K].astype(np.int32)
+    v = -np.sort(-rng.random((BS, K)).astype(np.float32), axis=1)
+    sc = synth.bf16_from_f32_trunc(v / v.sum(axis=1, keepdims=True))
+    thr = rng.uniform(0, 0.3, K).astype(np.float32)
+    active = (rng.random(BS) < 0.9).astype(np.uint8)
+    for mode in (0, 1):
+        note(f"remap variant BS={BS} K={K} E={E} F={F} mode={mode}")
+        ref = orc.remap_prune(ids, table, ws, ppr, 7, mode, expert_scales=sc,
+                              pruning_threshold=thr, active_mask=active)
+        got = _gpu(ids, table, ws, ppr, 7, mode, scales=sc, thr=thr, active=active)
+        _cmp(ref, got, f"BS={BS} K={K} E={E} F={F} mode={mode}")
