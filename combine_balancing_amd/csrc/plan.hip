@@ -151,6 +151,10 @@ __global__ __launch_bounds__(kHistThreads) void plan_hist(PlanDims d, const int*
 // across the wave's ranges with shuffles and across the 16 waves through
 // LDS. Measured on MI355X (warm): 8 experts per group beat 4, 16 and 32,
 // and the whole plan went from 63 to 56 us on a 1024-chunk plan.
+// PER (1, 2, 4 or 8) is the range length rounded up to a power of two. The
+// loads are unconditional, at indices clamped into the table, and masked
+// where they are used: loads under lane conditions made the compiler wait
+// for the earlier ones before each of the later ones.
 constexpr int kScanExperts = 8;
 constexpr int kScanSubs = kWave / kScanExperts;                   // ranges per wave
 constexpr int kScanThreads = 1024;
@@ -158,6 +162,7 @@ constexpr int kScanRanges = (kScanThreads / kWave) * kScanSubs;  // 128
 constexpr int kScanItems = kMaxChunks / kScanRanges;             // 8
 static_assert(kScanItems * kScanRanges == kMaxChunks, "chunk ranges must cover kMaxChunks");
 
+template <int PER>
 __global__ __launch_bounds__(kScanThreads) void plan_scan(PlanDims d, int* __restrict__ chunk,
                                                           int* __restrict__ cnt) {
     __shared__ int s_wave[kScanThreads / kWave][kScanExperts];
@@ -166,14 +171,16 @@ __global__ __launch_bounds__(kScanThreads) void plan_scan(PlanDims d, int* __res
     const int el = lane % kScanExperts, sub = lane / kScanExperts;
     const int e = blockIdx.x * kScanExperts + el;
     const bool live = e < d.E;
-    const int per = (d.nchunks + kScanRanges - 1) / kScanRanges;  // <= kScanItems
+    const int per = (d.nchunks + kScanRanges - 1) / kScanRanges;  // <= PER
     const int c0 = (wave * kScanSubs + sub) * per;
-    int v[kScanItems];
+    const int ec = min(e, d.E - 1);
+    int v[PER];
+#pragma unroll
+    for (int i = 0; i < PER; ++i) v[i] = chunk[min(c0 + i, d.nchunks - 1) * d.E + ec];
     int sum = 0;
 #pragma unroll
-    for (int i = 0; i < kScanItems; ++i) {
-        const int c = c0 + i;
-        v[i] = live && i < per && c < d.nchunks ? chunk[c * d.E + e] : 0;
+    for (int i = 0; i < PER; ++i) {
+        if (!(live && i < per && c0 + i < d.nchunks)) v[i] = 0;
         sum += v[i];
     }
     // inclusive sum over this wave's ranges of the same expert (lanes el + 8k)
@@ -189,7 +196,7 @@ __global__ __launch_bounds__(kScanThreads) void plan_scan(PlanDims d, int* __res
     for (int w = 0; w < wave; ++w) before += s_wave[w][el];
     int ex = before + incl - sum;
 #pragma unroll
-    for (int i = 0; i < kScanItems; ++i) {
+    for (int i = 0; i < PER; ++i) {
         const int c = c0 + i;
         if (live && i < per && c < d.nchunks) chunk[c * d.E + e] = ex;
         ex += v[i];
@@ -1284,8 +1291,14 @@ int plan_launch(const PlanDims& d, char* ws, const int32_t* topk_ids, const Plan
     hipLaunchKernelGGL(plan_hist, dim3(d.nchunks), dim3(kHistThreads), d.E * sizeof(int), s, d,
                        (const int*)topk_ids, w.chunk);
     MEP_LAUNCH_CHECK();
-    hipLaunchKernelGGL(plan_scan, dim3((d.E + kScanExperts - 1) / kScanExperts),
-                       dim3(kScanThreads), 0, s, d, w.chunk, w.cnt);
+    {
+        const int per = (d.nchunks + kScanRanges - 1) / kScanRanges;
+        const dim3 sg((d.E + kScanExperts - 1) / kScanExperts), sb(kScanThreads);
+        if (per <= 1) hipLaunchKernelGGL(plan_scan<1>, sg, sb, 0, s, d, w.chunk, w.cnt);
+        else if (per <= 2) hipLaunchKernelGGL(plan_scan<2>, sg, sb, 0, s, d, w.chunk, w.cnt);
+        else if (per <= 4) hipLaunchKernelGGL(plan_scan<4>, sg, sb, 0, s, d, w.chunk, w.cnt);
+        else hipLaunchKernelGGL(plan_scan<kScanItems>, sg, sb, 0, s, d, w.chunk, w.cnt);
+    }
     MEP_LAUNCH_CHECK();
     // expert ids below 256 need 8 ballots in the multi-split, not 10
     const dim3 rg(d.nchunks), rb(kRouteThreads), fb(fnt);
