@@ -96,19 +96,7 @@ __global__ __launch_bounds__(kMaxTpr) void group_rows(const u32x4* __restrict__ 
         // grouping (probe on the real map).
         if (tid < nvec) __builtin_nontemporal_store(__builtin_nontemporal_load(src + tid), dst + tid);
     } else {
-        for (int v0 = 0; v0 < nvec; v0 += tpr * VPT) {
-            u32x4 q[VPT];
-#pragma unroll
-            for (int i = 0; i < VPT; ++i) {
-                const int v = v0 + i * tpr + tid;
-                if (v < nvec) q[i] = __builtin_nontemporal_load(src + v);
-            }
-#pragma unroll
-            for (int i = 0; i < VPT; ++i) {
-                const int v = v0 + i * tpr + tid;
-                if (v < nvec) __builtin_nontemporal_store(q[i], dst + v);
-            }
-        }
+        rows::copy_row<VPT>(src, dst, nvec, tid, tpr);
     }
 }
 

@@ -135,19 +135,7 @@ __global__ __launch_bounds__(kMaxTpr) void ungroup_rows(const u32x4* __restrict_
         // one vector per thread covers the row (as in group_rows)
         if (tid < nvec) __builtin_nontemporal_store(__builtin_nontemporal_load(src + tid), dst + tid);
     } else {
-        for (int v0 = 0; v0 < nvec; v0 += tpr * VPT) {
-            u32x4 q[VPT];
-#pragma unroll
-            for (int i = 0; i < VPT; ++i) {
-                const int v = v0 + i * tpr + tid;
-                if (v < nvec) q[i] = __builtin_nontemporal_load(src + v);
-            }
-#pragma unroll
-            for (int i = 0; i < VPT; ++i) {
-                const int v = v0 + i * tpr + tid;
-                if (v < nvec) __builtin_nontemporal_store(q[i], dst + v);
-            }
-        }
+        rows::copy_row<VPT>(src, dst, nvec, tid, tpr);
     }
 }
 

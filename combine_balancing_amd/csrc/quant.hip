@@ -212,19 +212,7 @@ __global__ __launch_bounds__(kMaxTpr) void quant_group_rows(
         // one unit per thread covers the row: no loop (as in group_rows)
         if (tid < nunits) __builtin_nontemporal_store(__builtin_nontemporal_load(src + tid), dst + tid);
     } else {
-        for (int v0 = 0; v0 < nunits; v0 += tpr * VPT) {
-            U q[VPT];
-#pragma unroll
-            for (int i = 0; i < VPT; ++i) {
-                const int v = v0 + i * tpr + tid;
-                if (v < nunits) q[i] = __builtin_nontemporal_load(src + v);
-            }
-#pragma unroll
-            for (int i = 0; i < VPT; ++i) {
-                const int v = v0 + i * tpr + tid;
-                if (v < nunits) __builtin_nontemporal_store(q[i], dst + v);
-            }
-        }
+        rows::copy_row<VPT>(src, dst, nunits, tid, tpr);
     }
     if (tid == 0) scales[t] = *(const float*)(m + hq);
 }

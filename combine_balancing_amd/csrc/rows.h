@@ -101,6 +101,28 @@ __device__ __forceinline__ int row_in_group(int tpr, int rpb) {
     return __builtin_amdgcn_readfirstlane((int)threadIdx.x) >> __builtin_ctz((unsigned)tpr);
 }
 
+// dst[v] = src[v] for v in [0, n) (n >= 1), the row's nthr threads taking
+// VPT vectors each per pass, all of a pass's loads issued before its
+// stores. The loads are unconditional, at indices clamped into the row (a
+// lane past its end reloads the last vector and stores nothing): with each
+// load under its lane condition the compiler waited for the previous load
+// before issuing the next, one round trip per vector.
+template <int VPT, typename T>
+__device__ __forceinline__ void copy_row(const T* __restrict__ src, T* __restrict__ dst, int n,
+                                         int tid, int nthr) {
+    for (int v0 = 0; v0 < n; v0 += nthr * VPT) {
+        T q[VPT];
+#pragma unroll
+        for (int i = 0; i < VPT; ++i)
+            q[i] = __builtin_nontemporal_load(src + min(v0 + i * nthr + tid, n - 1));
+#pragma unroll
+        for (int i = 0; i < VPT; ++i) {
+            const int v = v0 + i * nthr + tid;
+            if (v < n) __builtin_nontemporal_store(q[i], dst + v);
+        }
+    }
+}
+
 inline RowShape row_shape(int nvec, int vpt, int max_tpr) {
     int tpr = (nvec + vpt - 1) / vpt;
     tpr = (tpr + kWave - 1) / kWave * kWave;
