@@ -116,29 +116,43 @@ __device__ __forceinline__ int efirst_of(int r, int R, int E) {
 }
 
 // ---------------------------------------------------------------- plan_hist
+// The kernel's arguments are requested as one batch of scalar loads, and the
+// first batch of ids is loaded before the histogram is cleared: the compiler
+// had issued the arguments' loads next to their first uses (three cold
+// scalar round trips before the first id load, the block size among them),
+// and the ids only after the clearing barrier.
 __global__ __launch_bounds__(kHistThreads) void plan_hist(PlanDims d, const int* __restrict__ ids,
                                                           int* __restrict__ chunk) {
+    asm volatile("" ::"s"(ids), "s"(chunk), "s"(d.E), "s"(d.C), "s"(d.T), "s"(d.cps));
     extern __shared__ int s_hist[];
+    constexpr int U = 8;  // ids in flight per thread
     const int c = blockIdx.x;
     const int src = c / d.cps, sub = c - src * d.cps;
     const int f0 = src * d.C + sub * d.T;
     const int f1 = min(f0 + d.T, (src + 1) * d.C);
-    for (int e = threadIdx.x; e < d.E; e += blockDim.x) s_hist[e] = 0;
-    lds_barrier();
-    constexpr int U = 8;  // ids in flight per thread
-    for (int base = f0; base < f1; base += kHistThreads * U) {
-        int e[U];
+    int e[U];
+    auto load = [&](int base) {
 #pragma unroll
         for (int u = 0; u < U; ++u) {
             const int f = base + u * kHistThreads + (int)threadIdx.x;
             e[u] = f < f1 ? ids[f] : -1;
         }
+    };
+    auto count = [&]() {
 #pragma unroll
         for (int u = 0; u < U; ++u)
             if ((unsigned)e[u] < (unsigned)d.E) atomicAdd(&s_hist[e[u]], 1);
+    };
+    load(f0);
+    for (int i = threadIdx.x; i < d.E; i += kHistThreads) s_hist[i] = 0;
+    lds_barrier();
+    count();
+    for (int base = f0 + kHistThreads * U; base < f1; base += kHistThreads * U) {
+        load(base);
+        count();
     }
     lds_barrier();
-    for (int e = threadIdx.x; e < d.E; e += blockDim.x) chunk[c * d.E + e] = s_hist[e];
+    for (int i = threadIdx.x; i < d.E; i += kHistThreads) chunk[c * d.E + i] = s_hist[i];
 }
 
 // ---------------------------------------------------------------- plan_scan
@@ -732,6 +746,8 @@ __device__ __forceinline__ PhaseScalars global_phases(const PlanDims& d, const P
 
 // One element per thread in the per-expert and per-rank phases (E, R <= NT).
 __global__ __launch_bounds__(kGlobalThreads) void plan_global(PlanDims d, PlanWs w, PlanOut o) {
+    // the first loads' arguments as one batch of scalar loads (as in plan_hist)
+    asm volatile("" ::"s"(w.cnt), "s"(w.chunk), "s"(d.E), "s"(d.R), "s"(d.m), "s"(d.cps));
     extern __shared__ int lds[];
     const int E = d.E, R = d.R, m = d.m;
     const int tid = threadIdx.x;
@@ -1036,9 +1052,11 @@ static_assert(kRouteThreads <= kGlobalThreads, "the global phases' scan scratch 
 // registers, which leaves room for 7 waves per SIMD, i.e. one work-group.
 template <bool STAGED, int KEY_BITS, int NT>
 __global__ __launch_bounds__(NT) __attribute__((amdgpu_waves_per_eu(8)))
-void plan_fused(PlanDims d, PlanWs w,
-                                                            const int* __restrict__ ids,
-                                                            PlanOut o) {
+void plan_fused(PlanDims d, PlanWs w, const int* __restrict__ ids, PlanOut o) {
+    // the prologue loads' arguments as one batch of scalar loads (as in
+    // plan_hist): the workspace pointers had come one round trip later
+    asm volatile("" ::"s"(w.cnt), "s"(w.chunk), "s"(ids), "s"(d.E), "s"(d.R), "s"(d.C),
+                 "s"(d.m), "s"(d.T), "s"(d.cps));
     extern __shared__ int4 lds4[];  // 16-byte aligned base
     const int E = d.E, R = d.R, C = d.C, m = d.m;
     const int tid = threadIdx.x;
