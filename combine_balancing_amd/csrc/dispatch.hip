@@ -37,10 +37,14 @@ using namespace rows;
 // previous one): fewer outstanding stores measured faster on MI355X (dsv3
 // shape: 8 back-to-back stores 113 us, one at a time 104 us). Neither
 // scalar position loads nor prefetching a next item per thread gained
-// anything. Capping residency at two work-groups per CU gained 4 us more
-// at full K but lost 10 us when a third of the positions are skipped (dedup
-// maps) and 40 us in the peer-write variant, so the launch keeps full
-// residency.
+// anything. Capping residency at two work-groups per CU gains 4 us when
+// every position is written but lost 10 us when a third of them are skipped
+// (dedup maps) and 40 us in the peer-write variant, so only launches that
+// write every position are capped (kPackReserveLds).
+// LDS reserved, and not used, by a pack launch that writes every position:
+// of gfx950's 160 KiB per CU, 56 KiB leaves room for two work-groups.
+constexpr size_t kPackReserveLds = 56 * 1024;
+
 template <int KT>
 __global__ __launch_bounds__(kFlatThreads) void pack_flat(const u32x4* __restrict__ x,
                                                           const int* __restrict__ send_pos,
@@ -212,14 +216,22 @@ extern "C" int mep_dispatch(int T, int K, int H, const uint16_t* x, const int32_
         const u32x4* xv = (const u32x4*)x;
         const int* sp = (const int*)send_pos;
         u32x4* buf = (u32x4*)send_buf;
+        // When every position is written (n_send = T*K: the plain send
+        // map), the launch reserves LDS the kernel does not use, so that
+        // only two work-groups share a CU: fewer rows are then being written
+        // at once. On the dsv3 map pack went from 104 to 100 us; three or
+        // four work-groups per CU measured 107-109 us. Maps that skip
+        // positions (dedup, pruning) keep full residency: there the cap
+        // cost 10 us (fewer stores per thread leave too few in flight).
+        const size_t plds = (long long)n_send == (long long)T * K ? kPackReserveLds : 0;
         switch (K) {
-            case 1: hipLaunchKernelGGL(pack_flat<1>, g, b, 0, s, xv, sp, buf, total, K, n_send, dv); break;
-            case 2: hipLaunchKernelGGL(pack_flat<2>, g, b, 0, s, xv, sp, buf, total, K, n_send, dv); break;
-            case 4: hipLaunchKernelGGL(pack_flat<4>, g, b, 0, s, xv, sp, buf, total, K, n_send, dv); break;
-            case 6: hipLaunchKernelGGL(pack_flat<6>, g, b, 0, s, xv, sp, buf, total, K, n_send, dv); break;
-            case 8: hipLaunchKernelGGL(pack_flat<8>, g, b, 0, s, xv, sp, buf, total, K, n_send, dv); break;
-            case 16: hipLaunchKernelGGL(pack_flat<16>, g, b, 0, s, xv, sp, buf, total, K, n_send, dv); break;
-            default: hipLaunchKernelGGL(pack_flat<0>, g, b, 0, s, xv, sp, buf, total, K, n_send, dv); break;
+            case 1: hipLaunchKernelGGL(pack_flat<1>, g, b, plds, s, xv, sp, buf, total, K, n_send, dv); break;
+            case 2: hipLaunchKernelGGL(pack_flat<2>, g, b, plds, s, xv, sp, buf, total, K, n_send, dv); break;
+            case 4: hipLaunchKernelGGL(pack_flat<4>, g, b, plds, s, xv, sp, buf, total, K, n_send, dv); break;
+            case 6: hipLaunchKernelGGL(pack_flat<6>, g, b, plds, s, xv, sp, buf, total, K, n_send, dv); break;
+            case 8: hipLaunchKernelGGL(pack_flat<8>, g, b, plds, s, xv, sp, buf, total, K, n_send, dv); break;
+            case 16: hipLaunchKernelGGL(pack_flat<16>, g, b, plds, s, xv, sp, buf, total, K, n_send, dv); break;
+            default: hipLaunchKernelGGL(pack_flat<0>, g, b, plds, s, xv, sp, buf, total, K, n_send, dv); break;
         }
         MEP_LAUNCH_CHECK();
     }
