@@ -37,13 +37,16 @@ using namespace rows;
 // previous one): fewer outstanding stores measured faster on MI355X (dsv3
 // shape: 8 back-to-back stores 113 us, one at a time 104 us). Neither
 // scalar position loads nor prefetching a next item per thread gained
-// anything. Capping residency at two work-groups per CU gains 4 us when
-// every position is written but lost 10 us when a third of them are skipped
-// (dedup maps) and 40 us in the peer-write variant, so only launches that
-// write every position are capped (kPackReserveLds).
-// LDS reserved, and not used, by a pack launch that writes every position:
-// of gfx950's 160 KiB per CU, 56 KiB leaves room for two work-groups.
+// anything. Residency is capped through the launch's LDS reservation
+// (kPackReserveLds, kPackSkipReserveLds).
+// LDS reserved, and not used, by a pack launch, which caps the work-groups
+// sharing a CU (gfx950 has 160 KiB of LDS per CU). A map that writes every
+// position: 56 KiB, two work-groups. A map that skips positions (dedup,
+// pruning): 40 KiB, four work-groups, which took the dsv3 dedup pack from
+// 70.4-72.1 to 67.6-68.3 us (five per CU: 68.8-69.8 us, three 70.9-71.7,
+// two 10 us slower than none).
 constexpr size_t kPackReserveLds = 56 * 1024;
+constexpr size_t kPackSkipReserveLds = 40 * 1024;
 
 template <int KT>
 __global__ __launch_bounds__(kFlatThreads) void pack_flat(const u32x4* __restrict__ x,
@@ -216,14 +219,15 @@ extern "C" int mep_dispatch(int T, int K, int H, const uint16_t* x, const int32_
         const u32x4* xv = (const u32x4*)x;
         const int* sp = (const int*)send_pos;
         u32x4* buf = (u32x4*)send_buf;
+        // The launch reserves LDS the kernel does not use, so that fewer
+        // work-groups share a CU and fewer rows are being written at once.
         // When every position is written (n_send = T*K: the plain send
-        // map), the launch reserves LDS the kernel does not use, so that
-        // only two work-groups share a CU: fewer rows are then being written
-        // at once. On the dsv3 map pack went from 104 to 100 us; three or
-        // four work-groups per CU measured 107-109 us. Maps that skip
-        // positions (dedup, pruning) keep full residency: there the cap
-        // cost 10 us (fewer stores per thread leave too few in flight).
-        const size_t plds = (long long)n_send == (long long)T * K ? kPackReserveLds : 0;
+        // map), two per CU: on the dsv3 map pack went from 104 to 100 us,
+        // and three or four per CU measured 107-109 us. Maps that skip
+        // positions (dedup, pruning) leave each thread fewer stores in
+        // flight and do best with four.
+        const size_t plds =
+            (long long)n_send == (long long)T * K ? kPackReserveLds : kPackSkipReserveLds;
         switch (K) {
             case 1: hipLaunchKernelGGL(pack_flat<1>, g, b, plds, s, xv, sp, buf, total, K, n_send, dv); break;
             case 2: hipLaunchKernelGGL(pack_flat<2>, g, b, plds, s, xv, sp, buf, total, K, n_send, dv); break;
