@@ -665,6 +665,14 @@ def main():
                      "peak": HBM_PEAK_GBS, "unit": "GB/s",
                      "frac": round(group_gbs / HBM_PEAK_GBS, 4),
                      "traffic": _traffic("group_rows")},
+        # the same figures for each row mover of the step (per-kernel event
+        # intervals, algorithmic bytes, HBM peak)
+        "kernel_rooflines": {
+            kern: {"achieved": round(b[n] / (us[n] * 1e-6) / 1e9, 2),
+                   "frac": round(b[n] / (us[n] * 1e-6) / 1e9 / HBM_PEAK_GBS, 4),
+                   "algorithmic_bytes": b[n], "us": round(us[n], 2), "traffic": _traffic(kern)}
+            for n, kern in (("pack", "pack_flat"), ("group", "group_rows"),
+                            ("combine", "combine_flat"))},
     }
     legs = set() if args.legs == "none" else set(args.legs.split(","))
     unknown = legs - set(LEGS)
