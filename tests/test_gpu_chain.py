@@ -203,3 +203,43 @@ def test_zero_copy_and_ungroup_edges(orc, T, K, H, R, C):
     ya = cba.ungroup(dev(rows), dev(rp))
     torch.cuda.synchronize()
     assert np.array_equal(host(ya), orc.ungroup(rows, rp))
+
+
+def test_zero_copy_random_shapes(orc):
+    """Sixteen seeded shapes for the zero-copy push and pull: T up to 200,
+    K up to 16, up to 256 ranks, ragged rows, routes outside the buffers and
+    repeated (dest, slot) pairs dropped; whole buffers compared."""
+    torch = require_gpu()
+    import combine_balancing_amd as cba
+    shapes = np.random.default_rng(20261210)
+    for case in range(16):
+        T = int(shapes.integers(1, 201))
+        K = int(shapes.integers(1, 17))
+        R = int(shapes.integers(1, 257))
+        C = int(shapes.integers(1, max(2, 2 * T * K // R + 2)))
+        H = 8 * int(shapes.integers(1, max(2, min(1025, 2_000_000 // (8 * R * C)))))
+        rng = np.random.default_rng(case)
+        x = synth.bf16_normal(rng, (T, H))
+        rd = rng.integers(0, R + 1, T * K).astype(np.int32)  # R: no such rank
+        rs = rng.integers(0, C, T * K).astype(np.int32)
+        seen = set()
+        for f in range(T * K):
+            if (rd[f], rs[f]) in seen:
+                rd[f] = -1
+            seen.add((rd[f], rs[f]))
+        note(f"zero-copy random case {case}: T={T} K={K} H={H} R={R} C={C}")
+        grouped = torch.zeros(R, C, H, dtype=torch.bfloat16, device="cuda")
+        cba.dispatch_to_peers(K, dev(x), dev(rd), dev(rs), cba.peer_table(grouped), C)
+        torch.cuda.synchronize()
+        assert np.array_equal(host(grouped), orc.push(x, rd, rs, K, R, C)), f"case {case}"
+        del grouped
+        y = synth.bf16_normal(rng, (R, C, H))
+        sc = rng.standard_normal((T, K)).astype(np.float32)
+        yd = dev(y).view(torch.bfloat16)  # the peer table holds raw addresses: keep yd alive
+        ob, of = cba.combine_from_peers(cba.peer_table(yd), C, H, dev(rd), dev(rs), dev(sc),
+                                        out_bf16=True, out_f32=True)
+        torch.cuda.synchronize()
+        rb, rf = orc.pull_combine(y, rd, rs, sc)
+        assert np.array_equal(host(ob), rb), f"case {case}"
+        assert np.array_equal(host(of).view(np.uint32), rf.view(np.uint32)), f"case {case}"
+        del yd

@@ -110,3 +110,29 @@ def test_dedup_chain(orc, name):
                                                            device="cuda"))
         torch.cuda.synchronize()
         assert np.array_equal(host(grouped), ref[r]["recv_grouped"])
+
+
+def test_dedup_random_shapes(orc):
+    """Twenty seeded shapes (R up to 64, E up to 512, K up to 24, ragged
+    1024-token chunks, skewed and flat routing), each at a random rank."""
+    torch = require_gpu()
+    import combine_balancing_amd as cba
+    shapes = np.random.default_rng(20261209)
+    for case in range(20):
+        R = int(shapes.integers(1, 65))
+        E = int(shapes.integers(1, 513))
+        K = int(shapes.integers(1, min(E, 24) + 1))
+        S = int(shapes.integers(1, max(2, min(3000, 60000 // (R * K)))))
+        skew = float(shapes.choice([0.0, 1.5]))
+        m = int(shapes.integers(0, R))
+        rng = np.random.default_rng(case)
+        g = rng.gumbel(size=(R * S, E)) - skew * np.log(np.arange(E) + 1.0)
+        ids = np.argsort(-g, axis=1, kind="stable")[:, :K].astype(np.int32)
+        note(f"dedup random case {case}: R={R} E={E} S={S} K={K} m={m}")
+        p = cba.plan(dev(ids.reshape(-1)), R, E, S, K, my_rank=m)
+        ref_plan = orc.plan(ids, R, E, S, K, m=m)
+        got = cba.plan_dedup(p, R, S, K, m)
+        torch.cuda.synchronize()
+        ref = orc.plan_dedup(ref_plan, R, S, K, m)
+        for k in KEYS:
+            assert np.array_equal(host(got[k]), ref[k]), (case, k)

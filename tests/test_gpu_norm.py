@@ -122,3 +122,22 @@ def test_fused_norm_headline_shape(orc):
     g = synth.bf16_normal(rng, (d["H"],))
     _check(orc, d["y_ret"], p["send_pos"], d["scores"][0], res, g, 1e-6)
     del torch
+
+
+def test_fused_norm_random_shapes(orc):
+    """Twenty seeded shapes (T up to 300, K up to 16, H up to 16384, few or
+    no expert rows, pruned routes, residuals over a range of magnitudes,
+    three eps values), every token checked."""
+    require_gpu()
+    shapes = np.random.default_rng(20261208)
+    for case in range(20):
+        T = int(shapes.integers(1, 301))
+        K = int(shapes.integers(1, 17))
+        H = 8 * int(shapes.integers(1, 2049))
+        n_y = int(shapes.integers(0, 3 * T * K + 1)) if shapes.random() < 0.9 else 0
+        eps = float(shapes.choice([0.0, 1e-6, 1e-2]))
+        scale = float(2.0 ** shapes.integers(-6, 7))
+        prune = float(shapes.choice([0.0, 0.15, 0.6]))
+        note(f"combine_add_rmsnorm random case {case}: T={T} K={K} H={H} n_y={n_y} eps={eps}")
+        y, sp, sc, res, g = _inputs(T, K, H, n_y, 1000 + case, prune=prune, scale=scale)
+        _check(orc, y, sp, sc, res, g, eps)

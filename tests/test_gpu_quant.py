@@ -143,3 +143,44 @@ def test_int8_path_headline(orc):
     gx, gs = orc.group_quant(ref_m, p["recv_pos"], H)
     assert np.array_equal(host(xq).view(np.uint8), gx)
     assert np.array_equal(host(sc), gs)
+
+
+def test_quant_random_shapes(orc):
+    """Twenty-four seeded shapes (T up to 300, K up to 16, H up to 16384,
+    rows scaled over a wide range of magnitudes), half of them smoothed with
+    some routes naming no expert; then the receive split of the messages."""
+    torch = require_gpu()
+    import combine_balancing_amd as cba
+    shapes = np.random.default_rng(20261207)
+    for case in range(24):
+        T = int(shapes.integers(1, 301))
+        K = int(shapes.integers(1, 17))
+        H = 8 * int(shapes.integers(1, 2049))
+        smooth = bool(shapes.random() < 0.5)
+        rng = np.random.default_rng(case)
+        x = synth.bf16_normal(rng, (T, H))
+        mag = np.float32(2.0) ** rng.integers(-20, 21, T).astype(np.float32)
+        xf = (x.astype(np.uint32) << 16).view(np.float32)
+        x = synth.bf16_from_f32_trunc(xf * mag[:, None])
+        sp = rng.permutation(T * K).astype(np.int32)
+        sp[rng.random(T * K) < 0.1] = -1
+        sm = ex = None
+        if smooth:
+            E = int(rng.integers(1, 13))
+            sm = (rng.random((E, H), dtype=np.float32) * 2.0 + 0.05).astype(np.float32)
+            ex = rng.integers(0, E + 1, T * K).astype(np.int32)  # E: no such expert
+        note(f"dispatch_quant random case {case}: T={T} K={K} H={H} smooth={smooth}")
+        msgs = _run(orc, x, sp, K, smooth=sm, ex=ex)
+        n = int(rng.integers(1, min(2 * T * K, 2000) + 1))
+        rp = rng.integers(-1, T * K, n).astype(np.int32)
+        xq = torch.full((n, H), 7, dtype=torch.int8, device="cuda")
+        sc = torch.full((n,), 3.0, dtype=torch.float32, device="cuda")
+        cba.group_quant(dev(msgs), dev(rp), H, x_q=xq, scales=sc)
+        torch.cuda.synchronize()
+        rxq = np.full((n, H), 7, np.uint8)
+        rsc = np.full(n, 3.0, np.float32)
+        gx, gs = orc.group_quant(msgs, rp, H)
+        ok = rp >= 0
+        rxq[ok], rsc[ok] = gx[ok], gs[ok]
+        assert np.array_equal(host(xq).view(np.uint8), rxq), f"case {case}"
+        assert np.array_equal(host(sc), rsc), f"case {case}"
