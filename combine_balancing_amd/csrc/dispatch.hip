@@ -30,15 +30,6 @@ namespace {
 using namespace rows;
 
 // ------------------------------------------------------------------- pack
-// send_buf[send_pos[t*K+k]] = x[t] for each k with 0 <= send_pos < nrows (the
-// send buffer's row count).
-// One thread per (token, vector): the token's row is read once and stored to
-// each of its K send rows, one store in flight at a time (each waits for the
-// previous one): fewer outstanding stores measured faster on MI355X (dsv3
-// shape: 8 back-to-back stores 113 us, one at a time 104 us). Neither
-// scalar position loads nor prefetching a next item per thread gained
-// anything. Residency is capped through the launch's LDS reservation
-// (kPackReserveLds, kPackSkipReserveLds).
 // LDS reserved, and not used, by a pack launch, which caps the work-groups
 // sharing a CU (gfx950 has 160 KiB of LDS per CU). A map that writes every
 // position: 56 KiB, two work-groups. A map that skips positions (dedup,
@@ -48,6 +39,15 @@ using namespace rows;
 constexpr size_t kPackReserveLds = 56 * 1024;
 constexpr size_t kPackSkipReserveLds = 40 * 1024;
 
+// send_buf[send_pos[t*K+k]] = x[t] for each k with 0 <= send_pos < nrows (the
+// send buffer's row count).
+// One thread per (token, vector): the token's row is read once and stored to
+// each of its K send rows, one store in flight at a time (each waits for the
+// previous one): fewer outstanding stores measured faster on MI355X (dsv3
+// shape: 8 back-to-back stores 113 us, one at a time 104 us). Neither
+// scalar position loads nor prefetching a next item per thread gained
+// anything. Residency is capped through the launch's LDS reservation
+// (kPackReserveLds, kPackSkipReserveLds).
 template <int KT>
 __global__ __launch_bounds__(kFlatThreads) void pack_flat(const u32x4* __restrict__ x,
                                                           const int* __restrict__ send_pos,
