@@ -83,6 +83,9 @@ CASES = [
     (8, 64, 1149, 4, 1.5),
     # more chunks than CUs, short ones: the fused form in 512-thread groups
     (300, 128, 125, 8, 1.0), (300, 300, 125, 8, 1.0),
+    # more than 512 ranks: one chunk per source rank, at 524,288 and 240,000
+    # routes
+    (1024, 512, 64, 8, 1.0), (600, 256, 100, 4, 2.0),
 ]
 
 
