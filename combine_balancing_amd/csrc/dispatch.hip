@@ -36,8 +36,13 @@ using namespace rows;
 // pruning): 40 KiB, four work-groups, which took the dsv3 dedup pack from
 // 70.4-72.1 to 67.6-68.3 us (five per CU: 68.8-69.8 us, three 70.9-71.7,
 // two 10 us slower than none).
+// Only a launch of at least kPackCapVectors vectors (8192 work-groups) is
+// capped: on smaller ones the cap leaves the GPU partly idle (random maps:
+// T=512, H=7168 took 16.9 us capped against 14.5 uncapped; T=1024, H=2048
+// 8.7 against 7.4; T=2048, H=7168 even; T=4096 and 8192 1.5-2.5 us faster).
 constexpr size_t kPackReserveLds = 56 * 1024;
 constexpr size_t kPackSkipReserveLds = 40 * 1024;
+constexpr uint32_t kPackCapVectors = 2u << 20;
 
 // send_buf[send_pos[t*K+k]] = x[t] for each k with 0 <= send_pos < nrows (the
 // send buffer's row count).
@@ -227,7 +232,8 @@ extern "C" int mep_dispatch(int T, int K, int H, const uint16_t* x, const int32_
         // positions (dedup, pruning) leave each thread fewer stores in
         // flight and do best with four.
         const size_t plds =
-            (long long)n_send == (long long)T * K ? kPackReserveLds : kPackSkipReserveLds;
+            total < kPackCapVectors ? 0
+            : (long long)n_send == (long long)T * K ? kPackReserveLds : kPackSkipReserveLds;
         switch (K) {
             case 1: hipLaunchKernelGGL(pack_flat<1>, g, b, plds, s, xv, sp, buf, total, K, n_send, dv); break;
             case 2: hipLaunchKernelGGL(pack_flat<2>, g, b, plds, s, xv, sp, buf, total, K, n_send, dv); break;

@@ -37,8 +37,11 @@ constexpr int kStagePeers = 1024;
 // CU, 40 KiB leaves room for four work-groups. Fewer rows are then being
 // written at once: the dsv3 push went from 105.9-106.9 to 101.6-101.8 us.
 // Five work-groups per CU measured 102.6-104.5 us, three 113 us, and two
-// (the pack's cap) 40 us slower.
+// (the pack's cap) 40 us slower. As for the pack, launches of fewer than
+// kPushCapVectors vectors (8192 work-groups) are not capped: on small grids
+// the cap leaves the GPU partly idle.
 constexpr size_t kPushReserveLds = 40 * 1024;
+constexpr uint32_t kPushCapVectors = 2u << 20;
 
 // peers[route_dest[t*K+k]][route_slot[t*K+k]] = x[t] for every valid route.
 // One thread per (token, vector), as the pack: the row is read once and
@@ -178,14 +181,15 @@ extern "C" int mep_dispatch_to_peers(int T, int K, int H, int R, int C, const ui
     const int* rd = (const int*)route_dest;
     const int* rs = (const int*)route_slot;
     u32x4* const* p = (u32x4* const*)peer_bufs;
+    const size_t plds = total < kPushCapVectors ? 0 : kPushReserveLds;
     switch (K) {
-        case 1: hipLaunchKernelGGL(push_flat<1>, g, b, kPushReserveLds, s, xv, rd, rs, p, total, K, R, C, dv); break;
-        case 2: hipLaunchKernelGGL(push_flat<2>, g, b, kPushReserveLds, s, xv, rd, rs, p, total, K, R, C, dv); break;
-        case 4: hipLaunchKernelGGL(push_flat<4>, g, b, kPushReserveLds, s, xv, rd, rs, p, total, K, R, C, dv); break;
-        case 6: hipLaunchKernelGGL(push_flat<6>, g, b, kPushReserveLds, s, xv, rd, rs, p, total, K, R, C, dv); break;
-        case 8: hipLaunchKernelGGL(push_flat<8>, g, b, kPushReserveLds, s, xv, rd, rs, p, total, K, R, C, dv); break;
-        case 16: hipLaunchKernelGGL(push_flat<16>, g, b, kPushReserveLds, s, xv, rd, rs, p, total, K, R, C, dv); break;
-        default: hipLaunchKernelGGL(push_flat<0>, g, b, kPushReserveLds, s, xv, rd, rs, p, total, K, R, C, dv); break;
+        case 1: hipLaunchKernelGGL(push_flat<1>, g, b, plds, s, xv, rd, rs, p, total, K, R, C, dv); break;
+        case 2: hipLaunchKernelGGL(push_flat<2>, g, b, plds, s, xv, rd, rs, p, total, K, R, C, dv); break;
+        case 4: hipLaunchKernelGGL(push_flat<4>, g, b, plds, s, xv, rd, rs, p, total, K, R, C, dv); break;
+        case 6: hipLaunchKernelGGL(push_flat<6>, g, b, plds, s, xv, rd, rs, p, total, K, R, C, dv); break;
+        case 8: hipLaunchKernelGGL(push_flat<8>, g, b, plds, s, xv, rd, rs, p, total, K, R, C, dv); break;
+        case 16: hipLaunchKernelGGL(push_flat<16>, g, b, plds, s, xv, rd, rs, p, total, K, R, C, dv); break;
+        default: hipLaunchKernelGGL(push_flat<0>, g, b, plds, s, xv, rd, rs, p, total, K, R, C, dv); break;
     }
     MEP_LAUNCH_CHECK();
     return MEP_OK;
