@@ -16,7 +16,7 @@
 //   drecv_pos[slot]  = Q[g][m] for the route of g occupying slot on m
 //   drecv_count[src] = Q[(src+1)*S][m] - Q[src*S][m].
 //
-// Three launches (latency-bound, like the plan):
+// Two or three launches (latency-bound, like the plan):
 //   dedup_count  one 1024-thread work-group per chunk of 1024 tokens (chunks
 //                never straddle a source): each token's destination bit
 //                mask, then per-destination counts by wave ballots
@@ -28,6 +28,11 @@
 //                and slots together), Q of every token for its destinations
 //                from the chunk base, the wave bases and the token's rank in
 //                its wave's ballot (kept in LDS); writes the three maps
+// When the chunk counts are small (nchunks * R <= kDedupFusedInts, 1 KiB at
+// R = 8, S = 4096), dedup_scan is left out: every dedup_maps work-group
+// copies the whole count table to LDS and sums the columns it needs itself
+// (its chunk's base, and Q at rank m's first and last chunk), and work-group
+// 0 writes the two count outputs.
 // R <= 64 (a token's destinations fit one 64-bit mask).
 #include "mep_device.h"
 
@@ -38,6 +43,7 @@ constexpr int kDedupThreads = 1024;
 constexpr int kDedupChunk = kDedupThreads;  // tokens per chunk
 constexpr int kDedupWaves = kDedupThreads / kWave;
 constexpr int kDedupMaxR = 64;
+constexpr int kDedupFusedInts = 8192;  // count table held in LDS by dedup_maps
 
 struct DedupDims {
     int R, S, K, m, cps, nchunks;
@@ -177,11 +183,28 @@ __global__ __launch_bounds__(kDedupThreads) void dedup_scan(DedupDims dd, DedupW
     }
 }
 
+// Sum over chunks [lo, hi) of the count table's column d, held in LDS
+// ([nchunks][R]), by the 16 lanes of one destination group (lane part of 16
+// takes every 16th chunk); every lane of the group returns the total.
+__device__ __forceinline__ int group16_sum(const int* s_all, int R, int d, int part, int lo,
+                                           int hi) {
+    int sum = 0;
+    for (int ch = lo + part; ch < hi; ch += 16) sum += s_all[ch * R + d];
+#pragma unroll
+    for (int o = 8; o > 0; o >>= 1) sum += __shfl_xor(sum, o, 16);
+    return sum;
+}
+
+template <bool FUSED>
 __global__ __launch_bounds__(kDedupThreads) void dedup_maps(DedupDims dd, DedupWs w,
                                                             const int* __restrict__ route_dest,
                                                             const int* __restrict__ route_slot,
                                                             int* __restrict__ dpack_pos,
-                                                            int* __restrict__ drecv_pos) {
+                                                            int* __restrict__ drecv_pos,
+                                                            int* __restrict__ dsend_count,
+                                                            int* __restrict__ drecv_count) {
+    __shared__ int s_all[FUSED ? kDedupFusedInts : 1];  // fused: the count table [nchunks][R]
+    __shared__ int s_q0[kDedupMaxR], s_q1[kDedupMaxR];
     __shared__ uint64_t s_bal[kDedupWaves][kDedupMaxR];
     __shared__ int s_wbase[kDedupWaves][kDedupMaxR];
     __shared__ int s_cbase[kDedupMaxR];
@@ -191,6 +214,15 @@ __global__ __launch_bounds__(kDedupThreads) void dedup_maps(DedupDims dd, DedupW
     const int t = sub * kDedupChunk + threadIdx.x;
     const bool valid = t < dd.S;
     const size_t g = (size_t)src * dd.S + (valid ? t : 0);
+    const int wave = threadIdx.x / kWave;
+    const int lane = lane_id();
+    if constexpr (FUSED) {
+        // the count table straight into LDS (gfx950's global_load_lds: each
+        // wave instruction fills 64 consecutive ints), issued first
+        const int n_all = dd.nchunks * dd.R;
+        for (int b = wave * kWave; b < n_all; b += kDedupThreads)
+            if (b + lane < n_all) __builtin_amdgcn_global_load_lds(w.cnt + b + lane, s_all + b, 4, 0, 0);
+    }
     // the token's first kRegRoutes destinations are loaded up front and
     // reused for every map
     constexpr int kRegRoutes = 16;
@@ -203,12 +235,48 @@ __global__ __launch_bounds__(kDedupThreads) void dedup_maps(DedupDims dd, DedupW
             if (k < kRegRoutes) rd[k] = d;
             if ((unsigned)d < (unsigned)dd.R) mk |= 1ull << d;
         });
-    const int wave = threadIdx.x / kWave;
     for (int d = 0; d < dd.R; ++d) {
         const uint64_t b = ballot64((mk >> d) & 1ull);
-        if (lane_id() == 0) s_bal[wave][d] = b;
+        if (lane == 0) s_bal[wave][d] = b;
     }
-    if (threadIdx.x < dd.R) {
+    if constexpr (FUSED) {
+        // the table's LDS writes count on vmcnt: done in every wave before
+        // the barrier
+        asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
+        lds_barrier();
+        // per destination (16 lanes each): Q below this chunk and at rank
+        // m's first chunk and one past its last
+        const int d = threadIdx.x >> 4, part = threadIdx.x & 15;
+        const int cm0 = dd.m * dd.cps, cm1 = cm0 + dd.cps;
+        if (d < dd.R) {
+            const int below = group16_sum(s_all, dd.R, d, part, 0, c);
+            const int q0 = group16_sum(s_all, dd.R, d, part, 0, cm0);
+            const int q1 = q0 + group16_sum(s_all, dd.R, d, part, cm0, cm1);
+            if (part == 0) {
+                s_cbase[d] = below;
+                s_q0[d] = q0;
+                s_q1[d] = q1;
+            }
+        }
+        lds_barrier();
+        // rank m's send segments: exclusive scan of its counts over the
+        // destinations (R <= 64: the first wave)
+        if (threadIdx.x < kWave) {
+            const int n = threadIdx.x < dd.R ? s_q1[threadIdx.x] - s_q0[threadIdx.x] : 0;
+            const int seg = wave_inclusive_sum(n) - n;
+            if (threadIdx.x < dd.R) {
+                s_seg[threadIdx.x] = seg - s_q0[threadIdx.x];
+                if (c == 0) dsend_count[threadIdx.x] = n;
+            }
+        }
+        // the tokens of each source reaching m
+        if (c == 0)
+            for (int s2 = threadIdx.x; s2 < dd.R; s2 += kDedupThreads) {
+                int n = 0;
+                for (int ch = s2 * dd.cps; ch < (s2 + 1) * dd.cps; ++ch) n += s_all[ch * dd.R + dd.m];
+                drecv_count[s2] = n;
+            }
+    } else if (threadIdx.x < dd.R) {
         s_cbase[threadIdx.x] = w.base[(size_t)c * dd.R + threadIdx.x];
         s_seg[threadIdx.x] = w.segbase[threadIdx.x] - w.q0[threadIdx.x];
     }
@@ -222,7 +290,7 @@ __global__ __launch_bounds__(kDedupThreads) void dedup_maps(DedupDims dd, DedupW
     }
     lds_barrier();
     if (!valid) return;
-    const uint64_t below = (1ull << lane_id()) - 1ull;
+    const uint64_t below = (1ull << lane) - 1ull;
     auto q_of = [&](int d) {
         return s_cbase[d] + s_wbase[wave][d] + __popcll(s_bal[wave][d] & below);
     };
@@ -332,11 +400,18 @@ extern "C" int mep_plan_dedup(int R, int S, int K, int my_rank, const int32_t* r
     const int* rd = (const int*)route_dest;
     hipLaunchKernelGGL(dedup_count, dim3(d.nchunks), dim3(kDedupThreads), 0, s, d, w, rd);
     MEP_LAUNCH_CHECK();
-    hipLaunchKernelGGL(dedup_scan, dim3(1), dim3(kDedupThreads), 0, s, d, w, (int*)dsend_count,
-                       (int*)drecv_count);
-    MEP_LAUNCH_CHECK();
-    hipLaunchKernelGGL(dedup_maps, dim3(d.nchunks), dim3(kDedupThreads), 0, s, d, w, rd,
-                       (const int*)route_slot, (int*)dpack_pos, (int*)drecv_pos);
+    if ((long long)d.nchunks * d.R <= kDedupFusedInts) {
+        hipLaunchKernelGGL(dedup_maps<true>, dim3(d.nchunks), dim3(kDedupThreads), 0, s, d, w, rd,
+                           (const int*)route_slot, (int*)dpack_pos, (int*)drecv_pos,
+                           (int*)dsend_count, (int*)drecv_count);
+    } else {
+        hipLaunchKernelGGL(dedup_scan, dim3(1), dim3(kDedupThreads), 0, s, d, w,
+                           (int*)dsend_count, (int*)drecv_count);
+        MEP_LAUNCH_CHECK();
+        hipLaunchKernelGGL(dedup_maps<false>, dim3(d.nchunks), dim3(kDedupThreads), 0, s, d, w, rd,
+                           (const int*)route_slot, (int*)dpack_pos, (int*)drecv_pos, nullptr,
+                           nullptr);
+    }
     MEP_LAUNCH_CHECK();
     return MEP_OK;
 }
