@@ -33,7 +33,9 @@
  * force, equivalence with already pinned functions). Parity unpinned, where
  * the pages print no formula or example and the pins fix the reading taken
  * rather than the pages: remap with instance counts above one beyond the
- * hand-derived examples; the precision and order of the prune threshold sum
+ * hand-derived examples (structural pins fix the reading: mode 0's columns
+ * split the ranks into groups of ceil(ws/count), mode 1's cycle over tokens);
+ * the precision and order of the prune threshold sum
  * (the pins fix the stated reading, fp32 in k order with each product
  * rounded, by tokens whose mask flips under fp64, a reversed order or a
  * fused multiply-add; the pages say nothing of it); the combine + add +

@@ -207,3 +207,53 @@ def test_prune_products_rounded_before_the_add(orc):
     out = orc.remap_prune(ids, table, 3, 1, 0, 0, expert_scales=sc, scale_dtype="fp32",
                           pruning_threshold=thr)
     assert out["balanced_mask"].tolist() == [[0, 0, 1]]
+
+
+def test_mode0_groups_partition_the_ranks(orc):
+    # Reading R-d as a structure, not a formula: over ranks 0..ws-1 the mode-0
+    # column of a count-c row starts at 1, never decreases, rises by one
+    # between groups, and every group of equal columns but the last holds
+    # ceil(ws/c) ranks (the last holds the rest). Checked for every
+    # world size up to 40 and every count up to 12 that fits it.
+    for ws in range(1, 41):
+        counts = [c for c in range(1, 13) if c <= ws]
+        F = max(counts) + 1
+        table = np.zeros((len(counts), F), np.int32)
+        for i, c in enumerate(counts):
+            table[i, 0] = c
+            table[i, 1:] = 1000 + np.arange(F - 1)
+        ids = np.arange(len(counts), dtype=np.int32).reshape(-1, 1)
+        cols = np.stack([orc.remap_prune(ids, table, ws, 2000, r, 0, want_send=False)
+                         ["balanced_ids"][:, 0] - 999 for r in range(ws)])   # [rank, row]
+        for i, c in enumerate(counts):
+            seq = cols[:, i]
+            assert seq[0] == 1 and np.all(np.diff(seq) >= 0) and np.all(np.diff(seq) <= 1)
+            assert seq.max() <= c
+            if c == 1:
+                assert np.all(seq == 1)
+                continue
+            size = -(-ws // c)
+            runs = np.diff(np.flatnonzero(np.diff(np.r_[0, seq, seq[-1] + 1])))
+            assert np.all(runs[:-1] == size) and 1 <= runs[-1] <= size, (ws, c, seq)
+
+
+def test_mode1_cycles_over_tokens(orc):
+    # Reading R-b/R-c as a structure: in mode 1, over consecutive tokens the
+    # column of a count-c row starts at 1 and advances by one, wrapping from
+    # c back to 1. Every token routes to every row (K = E = 8, counts 1 to 8),
+    # in a different order per token.
+    counts = list(range(1, 9))
+    F = 9
+    table = np.zeros((len(counts), F), np.int32)
+    for i, c in enumerate(counts):
+        table[i, 0] = c
+        table[i, 1:] = 1000 + np.arange(F - 1)
+    BS, K = 50, len(counts)
+    rng = np.random.default_rng(3)
+    ids = np.stack([rng.permutation(K) for _ in range(BS)]).astype(np.int32)
+    out = orc.remap_prune(ids, table, 64, 8, 0, 1, want_send=False)
+    col = out["balanced_ids"] - 999
+    for e, c in enumerate(counts):
+        seq = col[ids == e]            # one per token, in token order
+        assert len(seq) == BS and seq[0] == 1
+        assert np.all(seq[1:] == np.where(seq[:-1] == c, 1, seq[:-1] + 1)), (c, seq)
