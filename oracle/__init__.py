@@ -17,7 +17,10 @@ import os
 import numpy as np
 
 _HERE = os.path.dirname(os.path.abspath(__file__))
-LIB_PATH = os.path.join(_HERE, "liboracle.so")
+# MEP_ORACLE_LIB names another build of oracle.c to load (the mutation
+# check in tests/oracle_mutations.py loads oracle builds with planted
+# mistakes this way, leaving the in-tree library alone)
+LIB_PATH = os.environ.get("MEP_ORACLE_LIB") or os.path.join(_HERE, "liboracle.so")
 
 _lib = None
 

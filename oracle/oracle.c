@@ -30,19 +30,23 @@
  *
  * Pins. Every function is checked by the test suite against something other
  * than itself (the op doc's worked example, closed forms, invariants, brute
- * force, equivalence with already pinned functions). Parity unpinned, where
- * the pages print no formula or example and the pins fix the reading taken
- * rather than the pages: remap with instance counts above one beyond the
- * hand-derived examples (structural pins fix the reading: mode 0's columns
- * split the ranks into groups of ceil(ws/count), mode 1's cycle over tokens);
- * the precision and order of the prune threshold sum
- * (the pins fix the stated reading, fp32 in k order with each product
- * rounded, by tokens whose mask flips under fp64, a reversed order or a
- * fused multiply-add; the pages say nothing of it); the combine + add +
- * RMSNorm formula
- * (oracle_combine_add_rmsnorm); the int8 quantization formula
- * (oracle_dispatch_quant); the prefetch-slot order (oracle_weight_rows);
- * the dedup orders (oracle_plan_dedup).
+ * force, textbook special cases, equivalence with already pinned functions),
+ * and each pin fails for a planted mistake in the function it covers; no
+ * function here is without a pin. Where the pages leave a point open, the
+ * function follows a stated reading (listed with the design notes of this
+ * repository) and its pins fix that reading: the remap columns for instance
+ * counts above one (the printed formula is garbled; structural pins for
+ * every count up to 12: mode 0's columns split the ranks into groups of
+ * ceil(ws/count), mode 1's cycle over tokens); the precision and order of
+ * the prune threshold sum (fp32 in k order with each product rounded,
+ * pinned by tokens whose mask flips under fp64, a reversed order or a fused
+ * multiply-add); the combine + add + RMSNorm formula
+ * (oracle_combine_add_rmsnorm: the textbook RMSNorm, pinned by a hand
+ * example and closed forms); the int8 quantization formula
+ * (oracle_dispatch_quant: symmetric per-row scaling to +-127, pinned by its
+ * defining properties); the prefetch-slot order (oracle_weight_rows) and
+ * the dedup orders (oracle_plan_dedup), pinned by layout properties and by
+ * equivalence with the plain dispatch chain.
  *
  * Build: gcc -O2 -ffp-contract=off -fPIC -shared (no FMA contraction, so
  * every fp32 multiply and add is rounded on its own).

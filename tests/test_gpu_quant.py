@@ -76,6 +76,19 @@ def test_quant_rounding_edges(orc):
     assert np.all(got[1, :8] == 0)
 
 
+def test_quant_quotient_next_to_half_step(orc):
+    # rows whose v / s lands next to 63.5, where the IEEE division (63, then
+    # 64 for a quotient that rounds onto the tie) differs from a product
+    # with a rounded reciprocal and from an fp64 quotient; the values
+    # expected are those of the oracle's pin, from exact rationals
+    note("dispatch_quant quotient next to a half step")
+    rows = np.array([[1.3671875, 0.68359375] + [0.0] * 6, [1.1875, 0.59375] + [0.0] * 6,
+                     [-1.3671875, -0.68359375] + [0.0] * 6], np.float32)
+    x = (rows.view(np.uint32) >> 16).astype(np.uint16)
+    got = _run(orc, x, np.array([0, 1, 2], np.int32), 1)
+    assert list(got[:, 1].view(np.int8)) == [63, 64, -63]
+
+
 def test_quant_headline_shape_and_grouping(orc):
     # S=4096 K=8 H=7168 on rank 0's planned send map: every message byte;
     # then the receive grouping of message rows (a byte copy) vs the oracle's

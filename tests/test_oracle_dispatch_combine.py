@@ -47,6 +47,24 @@ def test_rne_against_distance_rule(orc):
     assert np.array_equal(got, _bf16_nearest_even(x[fin]))
 
 
+def test_rne_specials(orc):
+    # IEEE conversion: a NaN stays a NaN of the same sign, even when its
+    # payload lies only in the 16 bits that are cut off (truncating those
+    # would turn it into an infinity); infinities and signed zeros are kept;
+    # values past the largest bf16 by half an ulp or more round to infinity.
+    nan_bits = np.array([0x7F800001, 0xFF800001, 0x7F80FFFF, 0x7FC00000, 0xFFFFFFFF,
+                         0x7FBFFFFF], np.uint32)
+    got = orc.bf16_from_float(nan_bits.view(np.float32)).astype(np.uint32)
+    assert np.all((got & 0x7F80) == 0x7F80) and np.all((got & 0x007F) != 0)
+    assert np.array_equal(got >> 15, nan_bits >> 31)
+    big = np.array([np.inf, -np.inf, 0.0, -0.0], np.float32)
+    assert list(orc.bf16_from_float(big)) == [0x7F80, 0xFF80, 0x0000, 0x8000]
+    # largest bf16 is 0x7F7F; 0x7F7F8000 is the tie above it (odd mantissa:
+    # rounds up, to infinity), 0x7F7F7FFF stays below
+    edge = np.array([0x7F7F8000, 0x7F7F7FFF, 0xFF7F8000], np.uint32).view(np.float32)
+    assert list(orc.bf16_from_float(edge)) == [0x7F80, 0x7F7F, 0xFF80]
+
+
 @pytest.mark.parametrize("T,K,H", [(1, 1, 8), (7, 3, 16), (33, 4, 64)])
 def test_pack_is_row_scatter(orc, T, K, H):
     rng = np.random.default_rng(T * K)
@@ -254,3 +272,32 @@ def test_combine_pins_separate_product_rounding(orc):
     ob, of = orc.combine(y, np.array([0, 1], np.int32), sc)
     assert np.all(of == np.float32(2.0 + 2.0 ** -7))
     assert np.all(ob == 0x4000)
+
+
+def test_zero_copy_skips_out_of_range_routes(orc):
+    # a route whose destination or slot lies outside the R x C grouped
+    # buffers is not written by the push and adds nothing to the pull: the
+    # result equals the one with that route dropped (pack's -1)
+    rng = np.random.default_rng(19)
+    T, K, H, R, C = 6, 3, 16, 3, 8
+    x = rng.integers(0, 65536, (T, H)).astype(np.uint16)
+    rd = rng.integers(0, R, T * K).astype(np.int32)
+    rs = rng.integers(0, C, T * K).astype(np.int32)
+    bad = np.array([1, 5, 9, 16])
+    rd_bad, rs_bad = rd.copy(), rs.copy()
+    rd_bad[bad[:2]] = [R, -1]
+    rs_bad[bad[2:]] = [C, -1]
+    keep = np.ones(T * K, bool)
+    keep[bad] = False
+    ref = np.zeros((R, C, H), np.uint16)
+    for f in np.nonzero(keep)[0]:
+        ref[rd[f], rs[f]] = x[f // K]
+    assert np.array_equal(orc.push(x, rd_bad, rs_bad, K, R, C), ref)
+    # the pull equals the pinned combine over the flattened buffers with the
+    # out-of-range routes given position -1
+    y = rng.integers(0, 65536, (R, C, H)).astype(np.uint16)
+    sc = synth.make_scores(rng, T, K)
+    sp = np.where(keep, rd * C + rs, -1).astype(np.int32)
+    ob, of = orc.pull_combine(y, rd_bad, rs_bad, sc)
+    rb, rf = orc.combine(y.reshape(R * C, H), sp, sc)
+    assert np.array_equal(ob, rb) and np.array_equal(of.view(np.uint32), rf.view(np.uint32))

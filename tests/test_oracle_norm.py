@@ -73,6 +73,26 @@ def test_zero_residual_equals_combine(orc):
     assert np.array_equal(o["x_out"], ob)
 
 
+def test_rows_past_n_y_are_skipped(orc):
+    # a route whose row lies at or past the n_y returned rows adds nothing,
+    # as a route with position -1 does
+    rng = np.random.default_rng(6)
+    T, K, H, n_y = 9, 4, 32, 20
+    y = synth.bf16_normal(rng, (n_y, H))
+    sp = rng.integers(0, n_y, T * K).astype(np.int32)
+    sc = synth.make_scores(rng, T, K)
+    res = synth.bf16_normal(rng, (T, H))
+    g = _bf16(np.ones(H))
+    far = sp.copy()
+    far[::3] = n_y + np.arange(far[::3].size)
+    drop = sp.copy()
+    drop[::3] = -1
+    a = orc.combine_add_rmsnorm(y, far, sc, res, g, 1e-6, n_y=n_y)
+    b = orc.combine_add_rmsnorm(y, drop, sc, res, g, 1e-6, n_y=n_y)
+    for key in ("x_out", "x_f32", "rstd", "y"):
+        assert np.array_equal(a[key], b[key]), key
+
+
 def test_unit_rms_when_eps_zero(orc):
     # eps = 0: sum_h (y/gamma)^2 / H = 1 for every row
     rng = np.random.default_rng(5)

@@ -117,6 +117,78 @@ def test_smoothing(orc):
         assert s[r] == (spl[r] * np.float32(2.0) if ex[f] == 2 else spl[r])
 
 
+def test_smoothing_per_column_and_expert(orc):
+    # each route reads its own expert's smoothing row, column by column: with
+    # power-of-two factors the product is exact, so a smoothed route's
+    # message equals the unsmoothed message of its row pre-multiplied
+    rng = np.random.default_rng(5)
+    T, K, H, E = 10, 3, 48, 4
+    x = synth.bf16_normal(rng, (T, H))
+    sp = rng.permutation(T * K).astype(np.int32)
+    ex = rng.integers(0, E, T * K).astype(np.int32)
+    h, e = np.meshgrid(np.arange(H), np.arange(E))
+    sm = np.exp2(((h * 3 + e * 2) % 7 - 3).astype(np.float32)).astype(np.float32)
+    got = orc.dispatch_quant(x, sp, K, smooth=sm, route_expert=ex)
+    for f in range(T * K):
+        t, r = f // K, sp[f]
+        row = _bf16(_f32(x[t]) * sm[ex[f]])
+        ref = orc.dispatch_quant(row[None, :], np.array([0], np.int32), 1)
+        assert np.array_equal(got[r], ref[0]), f
+
+
+def test_smoothing_skips_routes_without_an_expert(orc):
+    # with smoothing, a route whose expert id is outside [0, E) has no
+    # smoothing row: it is skipped and its message row left untouched
+    rng = np.random.default_rng(7)
+    T, K, H, E = 5, 2, 32, 3
+    x = synth.bf16_normal(rng, (T, H))
+    sp = np.arange(T * K, dtype=np.int32)
+    ex = rng.integers(0, E, T * K).astype(np.int32)
+    ex[[1, 6]] = [E, -1]
+    sm = np.full((E, H), 2.0, np.float32)
+    msgs = np.full((T * K, orc.quant_msg_bytes(H)), 0x5A, np.uint8)
+    got = orc.dispatch_quant(x, sp, K, smooth=sm, route_expert=ex, msgs=msgs)
+    assert np.all(got[[1, 6]] == 0x5A)
+    ok = np.setdiff1d(np.arange(T * K), [1, 6])
+    assert not np.any(np.all(got[ok] == 0x5A, axis=1))
+
+
+def _rn32(q):
+    """IEEE round-to-nearest-even of a positive rational to fp32 (normal
+    range), from the definition: scale into [2^23, 2^24), round the
+    integer part half to even."""
+    from fractions import Fraction
+    e = q.numerator.bit_length() - q.denominator.bit_length()
+    while Fraction(2) ** e > q:
+        e -= 1
+    while Fraction(2) ** (e + 1) <= q:
+        e += 1
+    return Fraction(round(q / Fraction(2) ** (e - 23))) * Fraction(2) ** (e - 23)
+
+
+def test_quotient_is_the_correctly_rounded_division(orc):
+    # q = rint(fl(v / s)) with fl the IEEE division. The rows below put v / s
+    # next to 63.5, where the reading's division and two plausible
+    # alternatives disagree. Expected values come from exact rationals.
+    from fractions import Fraction
+    rows = [[1.3671875, 0.68359375], [1.1875, 0.59375]]
+    x = _bf16(np.array([r + [0.0] * 6 for r in rows], np.float32))
+    m = orc.dispatch_quant(x, np.array([0, 1], np.int32), 1)
+    q, s = _q(m, 8), _s(m, 8)
+    for i, (amax, v) in enumerate(rows):
+        S = _rn32(Fraction(amax) / 127)
+        Q = _rn32(Fraction(v) / S)
+        assert s[i] == float(S)
+        assert list(q[i][:2]) == [127, round(Q)]
+        # the case tells the division apart from a product with a rounded
+        # reciprocal and from an unrounded (fp64) quotient
+        recip = round(_rn32(Fraction(v) * _rn32(1 / S)))
+        exact = round(Fraction(v) / S)
+        assert round(Q) != recip
+        assert i == 0 or round(Q) != exact
+    assert list(q[:, 1]) == [63, 64]
+
+
 def test_token_copies_identical_and_skips(orc):
     rng = np.random.default_rng(5)
     T, K, H = 10, 4, 48
