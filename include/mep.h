@@ -26,8 +26,9 @@
  *
  * Conventions for every call:
  *   - Pointers are DEVICE pointers unless marked (host). The caller owns
- *     every buffer; the library keeps no state between calls and never
- *     allocates device memory.
+ *     every buffer; the library never allocates device memory and keeps
+ *     no state between calls, except mep_plan_noalloc's static device
+ *     array (see there), which holds its workspace.
  *   - bf16 data is passed as raw 16-bit patterns (uint16_t); ids, tables
  *     and maps are int32_t; masks are uint8_t holding 0 or 1.
  *   - `stream` is a hipStream_t (NULL = the legacy default stream). Calls
@@ -44,7 +45,8 @@
  *     out_f32) must be 16-byte aligned and H a multiple of 8.
  *   - Every output is a pure function of the inputs (no order-dependent
  *     atomics), as [UpdExp] "约束说明" asks (deterministic by default).
- *   - Calls are reentrant; concurrent calls must not share output buffers.
+ *   - Calls are reentrant; concurrent calls must not share output buffers
+ *     (nor, for mep_plan_noalloc, overlap on one GPU).
  */
 #ifndef MEP_H
 #define MEP_H
