@@ -1,8 +1,10 @@
 /*
- * A C consumer of libmep.so: no Python, no PyTorch. Runs the plan, the pack,
- * the receive grouping and the combine through the C ABI (include/mep.h) on
- * device buffers from the HIP runtime, and checks every output bit for bit
- * against the C oracle (oracle/oracle.c, test infrastructure) on the host.
+ * A C consumer of libmep.so: no Python, no PyTorch. Runs the plan (with a
+ * workspace and allocation-free), the EPLB remap/prune with its send map,
+ * the pack, the receive grouping and the combine through the C ABI
+ * (include/mep.h) on device buffers from the HIP runtime, and checks every
+ * output bit for bit against the C oracle (oracle/oracle.c, test
+ * infrastructure) on the host.
  * Also checks a few argument errors. Prints one line; exit status 0 on
  * success.
  */
@@ -26,6 +28,11 @@ int oracle_group(int n_recv, int H, const int32_t* recv_pos, const uint16_t* rec
                  uint16_t* recv_grouped);
 int oracle_combine(int T, int K, int H, const uint16_t* y_ret, const int32_t* send_pos,
                    const float* scores, uint16_t* out_bf16, float* out_f32);
+int oracle_remap_prune(int BS, int K, int E, int F, int world_size, int place_per_rank,
+                       int local_rank_id, int balance_mode, const int32_t* expert_ids,
+                       const int32_t* eplb_table, const void* scales, int scale_dtype,
+                       const float* thr, const uint8_t* active, int32_t* balanced_ids,
+                       uint8_t* balanced_mask, int32_t* send_pos, int32_t* send_count);
 
 #define CHECK_HIP(x)                                                          \
     do {                                                                      \
@@ -67,6 +74,85 @@ static int same(const char* what, const void* d, const void* h, size_t n) {
     const int ok = memcmp(t, h, n) == 0;
     if (!ok) printf("c abi: %s differs from the oracle\n", what);
     free(t);
+    return ok;
+}
+
+/* A small EPLB workload: a table of instance counts in [1,8] and distinct
+ * instance ids, K distinct experts per token, bf16 scales sorted
+ * descending, fp32 thresholds, an active mask with a tail of inactive
+ * tokens. Both modes at one rank, every output compared with the oracle. */
+static int check_remap(void) {
+    const int E = 96, F = 9, ws = 40, ppr = 2, BS = 200, K = 8, rank = 13;
+    const int n_inst = ws * ppr, n = BS * K;
+    int32_t* table = malloc(4 * (size_t)E * F);
+    for (int e = 0; e < E; e++) {
+        const int cnt = 1 + (int)(next_u32() % 8);
+        table[e * F] = cnt;
+        for (int c = 1; c < F; c++) {
+            int id, dup;
+            do {
+                id = (int)(next_u32() % n_inst);
+                dup = 0;
+                for (int j = 1; j < c; j++) dup |= table[e * F + j] == id;
+            } while (dup);
+            table[e * F + c] = id;
+        }
+    }
+    int32_t* ids = malloc(4 * (size_t)n);
+    uint16_t* sc = malloc(2 * (size_t)n);
+    for (int t = 0; t < BS; t++) {
+        float prev = 1.0f;
+        for (int k = 0; k < K; k++) {
+            int e, dup;
+            do {
+                e = (int)(next_u32() % E);
+                dup = 0;
+                for (int j = 0; j < k; j++) dup |= ids[t * K + j] == e;
+            } while (dup);
+            ids[t * K + k] = e;
+            prev = prev * (0.3f + 0.7f * next_unit());
+            sc[t * K + k] = bf16_trunc(prev);
+        }
+    }
+    float thr[8];
+    for (int k = 0; k < K; k++) thr[k] = 0.2f * next_unit();
+    uint8_t* act = malloc((size_t)BS);
+    for (int t = 0; t < BS; t++) act[t] = t < BS - 25;
+    int32_t *bid = malloc(4 * (size_t)n), *spos = malloc(4 * (size_t)n), *scnt = malloc(4 * ws);
+    uint8_t* bmask = malloc((size_t)n);
+    int32_t* d_tab = dev_copy(table, 4 * (size_t)E * F);
+    int32_t* d_ids = dev_copy(ids, 4 * (size_t)n);
+    uint16_t* d_sc = dev_copy(sc, 2 * (size_t)n);
+    float* d_thr = dev_copy(thr, 4 * K);
+    uint8_t* d_act = dev_copy(act, (size_t)BS);
+    int32_t *d_bid = dev_alloc(4 * (size_t)n), *d_spos = dev_alloc(4 * (size_t)n),
+            *d_scnt = dev_alloc(4 * ws);
+    uint8_t* d_bmask = dev_alloc((size_t)n);
+    int ok = 1;
+    for (int mode = 0; mode < 2; mode++) {
+        if (oracle_remap_prune(BS, K, E, F, ws, ppr, rank, mode, ids, table, sc, MEP_SCALE_BF16, thr,
+                               act, bid, bmask, spos, scnt) != 0) {
+            printf("c abi: oracle_remap_prune failed\n");
+            return 0;
+        }
+        const int st = mep_remap_prune(BS, K, E, F, ws, ppr, rank, mode, d_ids, d_tab, d_sc,
+                                       MEP_SCALE_BF16, d_thr, d_act, d_bid, d_bmask, d_spos,
+                                       d_scnt, NULL);
+        if (st != MEP_OK) {
+            printf("c abi: mep_remap_prune returned %d (%s)\n", st, mep_status_str(st));
+            return 0;
+        }
+        CHECK_HIP(hipDeviceSynchronize());
+        ok &= same(mode ? "remap mode 1 ids" : "remap mode 0 ids", d_bid, bid, 4 * (size_t)n);
+        ok &= same(mode ? "remap mode 1 mask" : "remap mode 0 mask", d_bmask, bmask, (size_t)n);
+        ok &= same(mode ? "remap mode 1 send_pos" : "remap mode 0 send_pos", d_spos, spos,
+                   4 * (size_t)n);
+        ok &= same(mode ? "remap mode 1 send_count" : "remap mode 0 send_count", d_scnt, scnt,
+                   4 * (size_t)ws);
+    }
+    /* unpaired optional arguments are refused */
+    ok &= mep_remap_prune(BS, K, E, F, ws, ppr, rank, 0, d_ids, d_tab, d_sc, MEP_SCALE_BF16, NULL,
+                          NULL, d_bid, d_bmask, NULL, NULL, NULL) == MEP_ERR_PARAM;
     return ok;
 }
 
@@ -134,6 +220,25 @@ int main(void) {
     ok &= same("recv_pos", d_rp, rp, 4 * C);
     ok &= same("recv_count", d_rc, rc, 4 * R);
 
+    /* the allocation-free plan: same outputs, no workspace argument */
+    CHECK_HIP(hipMemset(d_rd, 0xFF, 4 * (size_t)N));
+    CHECK_HIP(hipMemset(d_sp, 0xFF, 4 * C));
+    st = mep_plan_noalloc(R, E, S, K, m, d_ids, d_ec, d_rl, d_rd, d_rs, d_ic, d_ie, d_icu, d_igb,
+                          d_sp, d_sc, d_rp, d_rc, NULL);
+    if (st != MEP_OK) {
+        printf("c abi: mep_plan_noalloc returned %d (%s)\n", st, mep_status_str(st));
+        return 1;
+    }
+    CHECK_HIP(hipDeviceSynchronize());
+    ok &= same("noalloc route_dest", d_rd, rd, 4 * (size_t)N);
+    ok &= same("noalloc route_slot", d_rs, rs, 4 * (size_t)N);
+    ok &= same("noalloc inst_cu", d_icu, icu, 4 * R * (E + 1));
+    ok &= same("noalloc send_pos", d_sp, sp, 4 * C);
+    ok &= same("noalloc recv_pos", d_rp, rp, 4 * C);
+
+    /* EPLB remap + prune with its send map, both balance modes, bf16 scales */
+    ok &= check_remap();
+
     /* pack, group, combine */
     uint16_t *send = calloc((size_t)C * H, 2), *grouped = calloc((size_t)C * H, 2);
     uint16_t* ob = malloc(2 * (size_t)S * H);
@@ -167,7 +272,8 @@ int main(void) {
     ok &= mep_combine(S, K, H, NULL, C, d_sp, d_scores, d_ob, NULL, NULL) == MEP_ERR_NULLPTR;
     ok &= mep_version() > 0 && strlen(mep_status_str(MEP_ERR_SHAPE)) > 0;
 
-    printf(ok ? "c abi ok: plan, pack, group, combine bit-exact against the oracle\n"
+    printf(ok ? "c abi ok: plan, allocation-free plan, remap/prune, pack, group, combine "
+                "bit-exact against the oracle\n"
               : "c abi: FAILED\n");
     return ok ? 0 : 1;
 }

@@ -1,7 +1,9 @@
 """The C ABI used from C: a plain C program (tests/c_abi/abi_check.c, built
 by __graft_entry__.build() with gcc against the HIP runtime only) runs the
-plan, the pack, the grouping and the combine through include/mep.h and
-checks them bit for bit against the C oracle. It runs as a child process."""
+plan (with a workspace and allocation-free), the EPLB remap/prune with its
+send map in both balance modes, the pack, the grouping and the combine
+through include/mep.h and checks them bit for bit against the C oracle. It
+runs as a child process."""
 import os
 import subprocess
 
