@@ -14,7 +14,8 @@ kernel gives the per-kernel breakdown and the roofline's kernel time; an
 event between two kernels adds a few us of launch gap, so those intervals
 run slightly long.
 
-Prints one JSON line. --gpus above 1 is refused: this build runs on one GPU.
+Prints one JSON line. --gpus above 1 is refused: the path runs on one GPU (R is a
+logical world size).
 """
 from __future__ import annotations
 
