@@ -57,6 +57,10 @@ class _Numpy(types.ModuleType):
 
 
 def main(argv):
+    import torch
+    if not torch.cuda.is_available():
+        print("no GPU visible: the sweep runs the GPU parity tests")
+        return 2
     offs = [int(a) for a in argv[0].split(",")] if argv else [1, 2, 3]
     budget = float(argv[1]) if len(argv) > 1 else 600.0
     t0 = time.time()
