@@ -89,6 +89,24 @@ def test_quant_quotient_next_to_half_step(orc):
     assert list(got[:, 1].view(np.int8)) == [63, 64, -63]
 
 
+def test_quant_subnormal_rows(orc):
+    # bf16 subnormal rows: quantized like any other (s stays a nonzero
+    # subnormal), and, smoothed down to a few smallest fp32 subnormals, a
+    # scale that rounds to zero giving all-zero codes
+    note("dispatch_quant subnormal rows")
+    x = np.zeros((3, 16), np.uint16)
+    x[0, :4] = [0x0001, 0x8002, 0x0004, 0x007F]
+    x[1, :3] = [0x0001, 0x8001, 0x0003]
+    x[2, :5] = [0x0080, 0x8100, 0x0001, 0x0040, 0x80FF]  # normals and subnormals mixed
+    got = _run(orc, x, np.array([0, 1, 2], np.int32), 1)
+    assert list(got[0, :4].view(np.int8)) == [1, -2, 4, 127]
+    sm = np.ones((2, 16), np.float32)
+    sm[1] = 2.0 ** -12
+    ex = np.array([0, 1, 0], np.int32)
+    got = _run(orc, x, np.array([0, 1, 2], np.int32), 1, smooth=sm, ex=ex)
+    assert np.all(got[1, :16] == 0)
+
+
 def test_quant_headline_shape_and_grouping(orc):
     # S=4096 K=8 H=7168 on rank 0's planned send map: every message byte;
     # then the receive grouping of message rows (a byte copy) vs the oracle's

@@ -153,6 +153,34 @@ def test_smoothing_skips_routes_without_an_expert(orc):
     assert not np.any(np.all(got[ok] == 0x5A, axis=1))
 
 
+def test_scale_that_underflows_gives_zero_codes(orc):
+    # s = fl(amax / 127) is zero for a nonzero row when amax is a few
+    # smallest subnormals (here bf16 2^-133 smoothed by 2^-12: v = 2^-145,
+    # and 2^-145 / 127 rounds to +0); with s = 0 every code is 0, as for a
+    # zero row, and the scale written is +0
+    x = np.zeros((1, 8), np.uint16)
+    x[0, :3] = [0x0001, 0x8001, 0x0003]  # 2^-133, -2^-133, 3 * 2^-133
+    sm = np.full((1, 8), 2.0 ** -12, np.float32)
+    m = orc.dispatch_quant(x, np.array([0], np.int32), 1, smooth=sm,
+                           route_expert=np.zeros(1, np.int32))
+    assert np.all(_q(m, 8) == 0)
+    assert _s(m, 8)[0] == 0.0 and not np.signbit(_s(m, 8)[0])
+
+
+def test_subnormal_rows(orc):
+    # a row of bf16 subnormals quantizes like any other: its largest
+    # magnitude maps to +-127 (s = fl(amax / 127) stays a nonzero subnormal)
+    x = np.zeros((1, 8), np.uint16)
+    x[0, :4] = [0x0001, 0x8002, 0x0004, 0x007F]  # k * 2^-133
+    m = orc.dispatch_quant(x, np.array([0], np.int32), 1)
+    s = _s(m, 8)[0]
+    assert s > 0.0 and s < np.finfo(np.float32).tiny
+    q = _q(m, 8)[0]
+    assert q[3] == 127
+    assert s == np.float32(2.0 ** -133)  # 127 * 2^-133 / 127, exact
+    assert list(q[:3]) == [1, -2, 4]
+
+
 def _rn32(q):
     """IEEE round-to-nearest-even of a positive rational to fp32 (normal
     range), from the definition: scale into [2^23, 2^24), round the
