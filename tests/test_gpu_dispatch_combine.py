@@ -48,6 +48,20 @@ def _check_combine(orc, y, sp, sc, ctx):
     return gb, gf, rb, rf
 
 
+def test_combine_subnormal_rows(orc):
+    # expert rows of bf16 subnormals and tiny scores: products and partial
+    # sums in the fp32 subnormal range, taken exactly as the oracle takes them
+    require_gpu()
+    rng = np.random.default_rng(23)
+    T, K, H = 24, 4, 64
+    y = (rng.integers(0, 0x80, (T * K, H)) | (rng.integers(0, 2, (T * K, H)) << 15)).astype(np.uint16)
+    y[::5] = synth.bf16_normal(rng, (len(y[::5]), H))  # some normal rows beside them
+    sp = rng.permutation(T * K).astype(np.int32)
+    sc = synth.make_scores(rng, T, K)
+    sc[::3, 1] = np.float32(2.0 ** -20)
+    _check_combine(orc, y, sp, sc, "subnormal rows")
+
+
 @pytest.fixture(scope="module")
 def dsv3(orc):
     require_gpu()

@@ -151,6 +151,25 @@ def test_prune_order_vectors(orc):
     assert got["balanced_mask"].tolist() == [[0, 0, 1], [0, 0, 1]]
 
 
+def test_prune_subnormal_scales(orc):
+    # bf16 scales down in the fp32 subnormal range: products and sums that
+    # are subnormal decide masks (a kernel that flushed them to zero would
+    # keep token 0's first route: its scale would then equal the sum)
+    require_gpu()
+    table = np.array([[1, 0], [1, 1], [1, 2]], np.int32)
+    ids = np.array([[0, 1, 2]] * 4, np.int32)
+    sc = np.array([[0x0080, 0x0040, 0x0001],    # 2^-126, 2^-127, 2^-133
+                   [0x0040, 0x0020, 0x0010],
+                   [0x0100, 0x0003, 0x8001],
+                   [0x3F80, 0x0001, 0x0001]], np.uint16)
+    thr = np.array([1.0, 1.0, 0.75], np.float32)
+    note("prune with subnormal bf16 scales")
+    got = _gpu(ids, table, 3, 1, 0, 0, scales=sc, thr=thr)
+    ref = orc.remap_prune(ids, table, 3, 1, 0, 0, expert_scales=sc, pruning_threshold=thr)
+    _cmp(ref, got, "subnormal scales")
+    assert got["balanced_mask"][0].tolist() == [0, 0, 0]
+
+
 def test_random_shapes(orc):
     """Thirty seeded shapes: BS, K, E, F, world size and instances per card
     drawn over their limits, both modes, all three scale types, with and
