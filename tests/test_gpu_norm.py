@@ -9,7 +9,10 @@ All terms are non-negative, so the sum's relative error is at most
 reciprocal add a few ulps, so rstd is within 1e-5 relative (a bound with
 room). y in fp32 adds two more roundings, and the final bf16 rounding adds
 at most half a bf16 ulp (2^-8 of |y|), so |y - y_exact| <= |y_exact| *
-(2^-8 + 1e-5) + 1e-30.
+(2^-8 + 1e-5) + 1e-30. The bound holds while the squares stay normal fp32
+numbers: a row whose |x| all lie below about 1.1e-19 (squares underflow)
+or reach about 1.8e19 (squares overflow) leaves fp32's range, and the
+tests keep to rows inside it.
 """
 import numpy as np
 import pytest
