@@ -7,7 +7,10 @@
 // add + RMSNorm of the unrounded fp32 sum:
 //   a       = combine accumulator: +0, then a = a + score_k * y_k in k order
 //   x       = a + residual                                (fp32)
-//   rstd    = 1 / sqrt(sum(x^2) / H + eps)                 (fp32)
+//   rstd    = 1 / sqrt(sum(x^2) / H + eps)   squares and sum in fp64, then
+//             rounded to fp32 (the square of an fp32 value is exact in fp64
+//             and never leaves its range, so the sum keeps full precision
+//             for rows of any magnitude)
 //   y       = (x * rstd) * gamma, rounded to bf16; x_out = bf16(x)
 //
 // One work-group per token (several tokens per group for short rows), up to
@@ -31,7 +34,7 @@ using namespace rows;
 constexpr int kNormThreads = 1024;
 constexpr int kNormMaxNv = 2;  // H <= 2 * 1024 * 8 = 16384
 
-__device__ __forceinline__ float wave_sum(float v) {
+__device__ __forceinline__ double wave_sum(double v) {
 #pragma unroll
     for (int m = 32; m >= 1; m >>= 1) v += __shfl_xor(v, m, kWave);
     return v;
@@ -61,7 +64,7 @@ __global__ __launch_bounds__(kNormThreads) void combine_norm_rows(
     const u32x4* __restrict__ gamma, float eps, u32x4* __restrict__ x_out,
     u32x4* __restrict__ y_out, float* __restrict__ rstd_out, int T, int K, int nvec, int tpr,
     int rpb) {
-    __shared__ float s_red[kNormThreads / kWave];
+    __shared__ double s_red[kNormThreads / kWave];
     const int r = row_in_group(tpr, rpb);
     const int tid = threadIdx.x - r * tpr;
     const int t_raw = blockIdx.x * rpb + r;
@@ -132,13 +135,13 @@ __global__ __launch_bounds__(kNormThreads) void combine_norm_rows(
     }
 
     // x = a + residual; sum of squares over this thread's real vectors
-    float ss = 0.0f;
+    double ss = 0.0;
 #pragma unroll
     for (int i = 0; i < NV; ++i) {
         load_add(x[i], rv[i]);
         if (i * tpr + tid < nvec) {
 #pragma unroll
-            for (int j = 0; j < 8; ++j) ss = ss + x[i][j] * x[i][j];
+            for (int j = 0; j < 8; ++j) ss = ss + (double)x[i][j] * (double)x[i][j];
         }
     }
 
@@ -147,9 +150,9 @@ __global__ __launch_bounds__(kNormThreads) void combine_norm_rows(
     const int w = threadIdx.x / kWave;
     if (lane_id() == 0) s_red[w] = ss;
     lds_barrier();
-    float tot = 0.0f;
+    double tot = 0.0;
     for (int q = 0; q < wpr; ++q) tot = tot + s_red[r * wpr + q];
-    const float rstd = 1.0f / sqrtf(tot / (float)(nvec * 8) + eps);
+    const float rstd = (float)(1.0 / sqrt(tot / (double)(nvec * 8) + (double)eps));
 
     if (!live) return;
     if (tid == 0 && rstd_out) rstd_out[t] = rstd;

@@ -2,17 +2,13 @@
 
 x_out is compared bit for bit (the same fp32 operations in the same order as
 the oracle). rstd and y depend on the sum of squares, which the kernel
-reduces in fp32 as a tree (at most 16 sequential terms per thread, then 6
-wave levels and at most 15 cross-wave adds), while the oracle sums in fp64.
-All terms are non-negative, so the sum's relative error is at most
-(16 + 6 + 15) * 2^-24 < 2.3e-6. The division by H, the eps add, sqrt and the
-reciprocal add a few ulps, so rstd is within 1e-5 relative (a bound with
-room). y in fp32 adds two more roundings, and the final bf16 rounding adds
-at most half a bf16 ulp (2^-8 of |y|), so |y - y_exact| <= |y_exact| *
-(2^-8 + 1e-5) + 1e-30. The bound holds while the squares stay normal fp32
-numbers: a row whose |x| all lie below about 1.1e-19 (squares underflow)
-or reach about 1.8e19 (squares overflow) leaves fp32's range, and the
-tests keep to rows inside it.
+forms in fp64 as the oracle does: each square of an fp32 value is exact in
+fp64 and the sum's relative error is of order 1e-15, whatever the row's
+magnitude. rstd is then rounded to fp32 (2^-24 relative), after an eps
+that the kernel takes as fp32 (at most 2^-25 relative in rstd), so rstd is
+within 2^-23 relative. y = (x * rstd) * gamma takes two more fp32 roundings
+and the bf16 rounding (at most 2^-8 of |y|), so |y - y_exact| <=
+|y_exact| * (2^-8 + 2^-21) + 1e-30.
 """
 import numpy as np
 import pytest
@@ -22,8 +18,8 @@ from gpu_util import dev, host, note, require_gpu
 
 pytestmark = pytest.mark.gpu
 
-RSTD_TOL = 1e-5
-Y_TOL = 2.0 ** -8 + 1e-5
+RSTD_TOL = 2.0 ** -23
+Y_TOL = 2.0 ** -8 + 2.0 ** -21
 
 
 def _f32(bits):
@@ -64,6 +60,23 @@ def _check(orc, y, sp, sc, res, g, eps, rows=None, n_y=None):
     err = np.abs(yg - ref["y"])
     bound = np.abs(ref["y"]) * Y_TOL + 1e-30
     assert np.all(err <= bound), (err / np.maximum(np.abs(ref["y"]), 1e-30)).max()
+
+
+def _scaled(bits, f):
+    """bf16 patterns times a power of two (exact while in range)."""
+    return ((_f32(bits) * np.float32(f)).view(np.uint32) >> 16).astype(np.uint16)
+
+
+@pytest.mark.parametrize("f", [2.0 ** -70, 2.0 ** 70])
+@pytest.mark.parametrize("eps", [0.0, 1e-6])
+def test_fused_norm_tiny_and_huge_rows(orc, f, eps):
+    # rows whose squares fall below fp32's normal range (2^-70: x^2 near
+    # 2^-146) or above it (2^70: x^2 near 2^140) are normalised as any
+    # other, the squares being summed in fp64
+    note(f"fused norm rows scaled by 2^{int(np.log2(f))} eps={eps}")
+    T, K, H = 24, 8, 1024
+    y, sp, sc, res, g = _inputs(T, K, H, 120, 4242)
+    _check(orc, _scaled(y, f), sp, sc, _scaled(res, f), g, eps)
 
 
 CASES = [
